@@ -1,0 +1,222 @@
+/*
+ * tern.h -- C ABI of the ternary packed-bit GEMV / small-M GEMM library for
+ * AMD MI355X (gfx950).
+ *
+ * The operation.  Every transformer linear holds weights in three states,
+ * minus, zero and plus (article "Neutrino-1: quantization is a training
+ * decision, not a deployment one", intro and "What's actually ternary").
+ * The weights stay bit-packed at rest and are decoded inside the matrix
+ * kernels, with nothing in the decode path stored as fp16 or fp32 weight
+ * material (Neutrino-1 8B model card, "Overview"; wpnews item "Neutrino-1 8B:
+ * 763 tok/s ...", "Not Quantization -- Trained Ternary").  A weight is a
+ * state times a higher-precision scale, and signed accumulation replaces
+ * multiplies (article, "What's actually ternary" and "The take").  Per-row
+ * metadata holds the row's scale and row sum (model card, "Where the bytes
+ * live").  With activations given per token as int8 q, an fp32 scale s_act
+ * and an int32 zero point z (x_j = s_act * (q_j - z)), every entry point
+ * computes, for token m and output row i,
+ *
+ *     acc[m][i] = sum_j w_ij * q[m][j]  -  z[m] * rowsum[i]      (int32, exact)
+ *     y[m][i]   = (s_row[i] * (float)acc[m][i]) * s_act[m]       (fp32, RNE, in
+ *                                                                  this order)
+ *
+ * which is sum_j (s_row[i] w_ij) * (s_act[m] (q[m][j] - z[m])) up to the two
+ * fp32 roundings.  The stored row sum turns the zero point into one
+ * multiply-subtract per output.
+ *
+ * Packed layout (the pages call their own format proprietary and
+ * unpublished -- wiki entry "Neutrino-1", "What is actually new here" -- so
+ * this one is the library's own):
+ *   - code(w) = w + 1: -1 -> 00, 0 -> 01, +1 -> 10; 11 is invalid;
+ *   - row i starts at packed + i * tern_row_bytes(K); a row is
+ *     16 * ceil(K / 64) bytes, so every row is 16-byte aligned;
+ *   - weight j sits in the little-endian 32-bit word j / 16 of its row, at
+ *     bit 8 * (j % 4) + 2 * ((j % 16) / 4); hence (word >> 2k) & 0x03030303
+ *     holds the codes of weights 4k .. 4k+3 of that word in byte order;
+ *   - columns K <= j < 4 * row_bytes are padding with code 01 (weight 0).
+ *   - metadata are separate arrays: float s_row[N], int32 rowsum[N].
+ *
+ * Conventions common to every call:
+ *   - Pointers marked "device" are device memory of the current HIP device;
+ *     the caller allocates and owns every buffer (including the stack
+ *     workspace).  The library allocates no device memory and keeps no global
+ *     state; calls are reentrant.
+ *   - Every call enqueues on `stream` and returns without synchronising
+ *     (tern_linear_stack_prepare is the one exception, see there).  Argument
+ *     errors are returned before anything is enqueued.  A failed launch
+ *     returns TERN_ERR_HIP (the HIP code is kept per thread, see
+ *     tern_last_hip_error); faults during execution surface at the caller's
+ *     next synchronisation.
+ *   - Sizes are int64.  N == 0 or M == 0 is an empty problem: nothing is
+ *     enqueued and TERN_OK is returned.  K must be >= 1.
+ *   - Alignment: `packed`, `q` and each q row (ldq) must be 16-byte aligned;
+ *     y and acc 4-byte aligned; otherwise TERN_ERR_ALIGNMENT.
+ *   - Outputs must not overlap inputs.
+ *   - Range: |z| <= 255 is a precondition (z is not read on the host).  Then
+ *     |acc| <= K * 383, and K > TERN_MAX_K is rejected with TERN_ERR_RANGE so
+ *     that no int32 intermediate can wrap.  The fp32 conversion of acc is
+ *     exact while |acc| < 2^24 (always so for K <= 43,804).
+ *   - Packed input holding the invalid code 11 gives unspecified outputs
+ *     (no fault); tern_validate finds such data.
+ */
+#ifndef TERN_H
+#define TERN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TERN_OK = 0,
+  TERN_ERR_INVALID_ARG = 1, /* null pointer, K < 1, negative size, bad stride */
+  TERN_ERR_ALIGNMENT = 2,   /* see "Alignment" above */
+  TERN_ERR_RANGE = 3,       /* K > TERN_MAX_K, or a size beyond int32 rows */
+  TERN_ERR_UNSUPPORTED = 4, /* a path hint the shape cannot take */
+  TERN_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned */
+  TERN_ERR_HIP = 6          /* a HIP runtime call failed */
+} tern_status;
+
+/* Path hints for tern_gemm_smallM and tern_linear_stack_prepare. */
+enum {
+  TERN_PATH_AUTO = 0, /* M == 1: VALU GEMV; M >= 2: MFMA int8 */
+  TERN_PATH_VALU = 1, /* VALU dot4 path (M <= TERN_VALU_MAX_M) */
+  TERN_PATH_MFMA = 2  /* MFMA int8 path (any M) */
+};
+
+#define TERN_MAX_K 5600000
+#define TERN_VALU_MAX_M 8
+
+/* Bytes of one packed row: 16 * ceil(K / 64); 0 for K < 1. */
+int64_t tern_row_bytes(int64_t K);
+
+/*
+ * tern_pack -- load-time packing of an int8 ternary matrix (the weights are
+ * packed once and stay packed at rest; no decode pass at load: Fermion
+ * Research models page, "Neutrino-1 0.6B").
+ *   w         device, N x K int8, row stride ldw >= K elements, values in
+ *             {-1, 0, +1};
+ *   packed    device, N * tern_row_bytes(K) bytes, 16-byte aligned (written);
+ *   rowsum    device, N int32 (written): sum_j w_ij;
+ *   bad_count device, one int32 or NULL; when given it is set to the number
+ *             of entries outside {-1, 0, +1} (each is stored as weight 0 and
+ *             left out of the row sum).
+ */
+int tern_pack(const int8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed,
+              int32_t* rowsum, int32_t* bad_count, hipStream_t stream);
+
+/*
+ * tern_unpack -- packed rows back to int8 weights (a test aid).
+ *   w  device, N x K int8 with row stride ldw >= K (written); a field with the
+ *      invalid code 11 is written as 0.
+ */
+int tern_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* w, int64_t ldw,
+                hipStream_t stream);
+
+/*
+ * tern_validate -- checks packed rows.
+ *   counts  device, two int32 (written): counts[0] = fields with code 11 among
+ *           the real columns, counts[1] = padding fields that are not 01.
+ */
+int tern_validate(const uint8_t* packed, int64_t N, int64_t K, int32_t* counts,
+                  hipStream_t stream);
+
+/*
+ * tern_gemv -- one token (M = 1).
+ *   packed, s_row, rowsum  device: the packed N x K matrix and its metadata;
+ *   q                      device, K int8 (16-byte aligned);
+ *   s_act, z               device, one float / one int32;
+ *   y                      device, N floats (written);
+ *   acc                    device, N int32 (written) or NULL.
+ */
+int tern_gemv(const uint8_t* packed, const float* s_row, const int32_t* rowsum, int64_t N,
+              int64_t K, const int8_t* q, const float* s_act, const int32_t* z, float* y,
+              int32_t* acc, hipStream_t stream);
+
+/*
+ * tern_gemm_smallM -- M tokens against the same packed weights (the batched
+ * verify pass of drafted decoding and prefill-sized batches: wiki entry
+ * "Neutrino-1", "What is actually new here"; models page "Neutrino-1 0.6B").
+ *   q      device, M x K int8, row stride ldq >= K (multiple of 16 when M > 1);
+ *   s_act  device, M floats;  z  device, M int32;
+ *   y      device, M x N floats, row stride ldy >= N (written);
+ *   acc    device, M x N int32 with the same stride ldy (written) or NULL;
+ *   path   TERN_PATH_AUTO, _VALU (M <= TERN_VALU_MAX_M) or _MFMA;
+ *          TERN_ERR_UNSUPPORTED for a hint the shape cannot take.
+ */
+int tern_gemm_smallM(const uint8_t* packed, const float* s_row, const int32_t* rowsum,
+                     int64_t N, int64_t K, int64_t M, const int8_t* q, int64_t ldq,
+                     const float* s_act, const int32_t* z, float* y, int64_t ldy,
+                     int32_t* acc, int path, hipStream_t stream);
+
+/*
+ * A stack of L independent linears evaluated by one persistent launch (the
+ * 8B carries 252 such linears, seven per decoder layer, and the 0.6B 196:
+ * article "What's actually ternary"; models page "The family").  Every linear
+ * sees the same token count M; each has its own shapes and buffers (all
+ * pointers device, same meaning and rules as in tern_gemm_smallM).
+ */
+typedef struct {
+  const uint8_t* packed;
+  const float* s_row;
+  const int32_t* rowsum;
+  int64_t N, K;
+  const int8_t* q;
+  int64_t ldq;
+  const float* s_act;
+  const int32_t* z;
+  float* y;
+  int64_t ldy;
+  int32_t* acc; /* may be NULL */
+} tern_linear_desc;
+
+/* Host-side handle filled by tern_linear_stack_prepare (plain data; copy it
+ * freely; it stays valid while the workspace and the buffers live). */
+typedef struct {
+  void* workspace;
+  int64_t workspace_bytes;
+  int32_t L, M;
+  int32_t path;      /* the path chosen */
+  int32_t grid;      /* workgroups launched */
+  int32_t block;     /* threads per workgroup */
+  int32_t workers;   /* waves with a schedule entry */
+  int32_t segments;  /* schedule entries */
+  int32_t kernel;    /* internal kernel selector */
+  int64_t bytes;     /* algorithmic bytes one launch moves (see below) */
+} tern_stack_plan;
+
+/* Upper bound of the workspace tern_linear_stack_prepare needs for L linears
+ * at M tokens on the current device; 0 on bad arguments. */
+int64_t tern_linear_stack_workspace_bytes(int64_t L, int64_t M);
+
+/*
+ * tern_linear_stack_prepare -- validates every descriptor, builds the static
+ * schedule (contiguous row ranges balanced by packed bytes over all waves of
+ * the launch) and copies descriptors and schedule into `workspace`
+ * (device, >= tern_linear_stack_workspace_bytes(L, M) bytes, 256-byte
+ * aligned).  Enqueues the copy on `stream` and synchronises that stream
+ * before returning (a one-time set-up step).  Fills *plan.
+ * plan->bytes = sum over linears of N*row_bytes(K) + 8*N + M*K + 8*M + 4*M*N.
+ */
+int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
+                              void* workspace, int64_t workspace_bytes,
+                              tern_stack_plan* plan, hipStream_t stream);
+
+/* tern_linear_stack -- one persistent launch over the prepared stack. */
+int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* tern_status_string(int status);
+
+/* The hipError_t of the last TERN_ERR_HIP returned on this thread. */
+int tern_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TERN_H */

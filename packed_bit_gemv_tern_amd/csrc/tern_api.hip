@@ -1,0 +1,338 @@
+// tern_api.hip -- the C ABI declared in include/tern.h: argument checks,
+// path dispatch and the static schedule of the persistent stack launch.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "tern.h"
+#include "tern_internal.h"
+
+using namespace tern;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return TERN_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kI32Max = 2147483647;
+
+int64_t row_bytes(int64_t K) { return K < 1 ? 0 : 16 * ((K + 63) / 64); }
+
+// Shape and pointer checks shared by every compute entry point.
+int check_linear(const uint8_t* packed, const float* s_row, const int32_t* rowsum, int64_t N,
+                 int64_t K, int64_t M, const int8_t* q, int64_t ldq, const float* s_act,
+                 const int32_t* z, const float* y, int64_t ldy, const int32_t* acc) {
+  if (N < 0 || M < 0 || K < 1) return TERN_ERR_INVALID_ARG;
+  if (K > TERN_MAX_K) return TERN_ERR_RANGE;
+  if (N > kI32Max || M > kI32Max) return TERN_ERR_RANGE;
+  if (N == 0 || M == 0) return TERN_OK;
+  if (!packed || !s_row || !rowsum || !q || !s_act || !z || !y) return TERN_ERR_INVALID_ARG;
+  if (M > 1 && ldq < K) return TERN_ERR_INVALID_ARG;
+  if (M > 1 && ldy < N) return TERN_ERR_INVALID_ARG;
+  if (ldq > kI32Max || ldy > kI32Max) return TERN_ERR_RANGE;
+  if (!aligned(packed, 16) || !aligned(q, 16)) return TERN_ERR_ALIGNMENT;
+  if (M > 1 && (ldq % 16) != 0) return TERN_ERR_ALIGNMENT;
+  if (!aligned(y, 4) || !aligned(s_row, 4) || !aligned(rowsum, 4) || !aligned(s_act, 4) ||
+      !aligned(z, 4) || (acc && !aligned(acc, 4)))
+    return TERN_ERR_ALIGNMENT;
+  return TERN_OK;
+}
+
+LinearArgs make_args(const uint8_t* packed, const float* s_row, const int32_t* rowsum, int64_t N,
+                     int64_t K, int64_t M, const int8_t* q, int64_t ldq, const float* s_act,
+                     const int32_t* z, float* y, int64_t ldy, int32_t* acc) {
+  LinearArgs a;
+  memset(&a, 0, sizeof(a));
+  a.packed = packed;
+  a.s_row = s_row;
+  a.rowsum = rowsum;
+  a.q = q;
+  a.s_act = s_act;
+  a.z = z;
+  a.y = y;
+  a.acc = acc;
+  a.N = (int32_t)N;
+  a.K = (int32_t)K;
+  a.ld = (int32_t)row_bytes(K);
+  a.nch = a.ld / 16;
+  a.ldq = (int32_t)(M > 1 ? ldq : 0);
+  a.ldy = (int32_t)(M > 1 ? ldy : 0);
+  a.M = (int32_t)M;
+  a.variant = valu_variant_for(K);
+  return a;
+}
+
+// Path the call takes, or -1 when the hint cannot be honoured.
+int resolve_path(int path, int64_t M) {
+  switch (path) {
+    case TERN_PATH_AUTO: return M == 1 ? TERN_PATH_VALU : TERN_PATH_MFMA;
+    case TERN_PATH_VALU: return M <= TERN_VALU_MAX_M ? TERN_PATH_VALU : -1;
+    case TERN_PATH_MFMA: return TERN_PATH_MFMA;
+    default: return -1;
+  }
+}
+
+int32_t valu_stack_kernel_for(int64_t M) {
+  if (M == 1) return SK_VALU_M1;
+  if (M == 2) return SK_VALU_M2;
+  if (M <= 4) return SK_VALU_M4;
+  return SK_VALU_M8;
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cus;
+}
+
+constexpr int kStackBlock = 256;
+constexpr int kWavesPerBlock = kStackBlock / 64;
+constexpr int kMaxWavesPerCu = 32;  // 8 waves per SIMD x 4 SIMDs
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+  int64_t off_lin, off_seg_start, off_seg, total;
+};
+
+Layout layout_for(int64_t L, int64_t workers, int64_t nseg) {
+  Layout l;
+  l.off_lin = (int64_t)sizeof(StackHeader);
+  l.off_seg_start = align_up(l.off_lin + L * (int64_t)sizeof(LinearArgs), 16);
+  l.off_seg = align_up(l.off_seg_start + (workers + 1) * 4, 16);
+  l.total = l.off_seg + nseg * (int64_t)sizeof(Segment);
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t tern_row_bytes(int64_t K) { return row_bytes(K); }
+
+const char* tern_status_string(int status) {
+  switch (status) {
+    case TERN_OK: return "ok";
+    case TERN_ERR_INVALID_ARG: return "invalid argument";
+    case TERN_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case TERN_ERR_RANGE: return "size out of range";
+    case TERN_ERR_UNSUPPORTED: return "unsupported path for this shape";
+    case TERN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case TERN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int tern_last_hip_error(void) { return g_last_hip; }
+
+int tern_pack(const int8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed,
+              int32_t* rowsum, int32_t* bad_count, hipStream_t stream) {
+  if (N < 0 || K < 1 || ldw < K) return TERN_ERR_INVALID_ARG;
+  if (K > TERN_MAX_K || N > kI32Max) return TERN_ERR_RANGE;
+  if (bad_count && !aligned(bad_count, 4)) return TERN_ERR_ALIGNMENT;
+  if (bad_count) {
+    hipError_t e = launch_zero_i32(bad_count, 1, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (N == 0) return TERN_OK;
+  if (!w || !packed || !rowsum) return TERN_ERR_INVALID_ARG;
+  if (!aligned(packed, 16) || !aligned(rowsum, 4)) return TERN_ERR_ALIGNMENT;
+  hipError_t e = launch_pack(w, N, K, ldw, packed, rowsum, bad_count, stream);
+  return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
+int tern_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* w, int64_t ldw,
+                hipStream_t stream) {
+  if (N < 0 || K < 1 || ldw < K) return TERN_ERR_INVALID_ARG;
+  if (K > TERN_MAX_K || N > kI32Max) return TERN_ERR_RANGE;
+  if (N == 0) return TERN_OK;
+  if (!packed || !w) return TERN_ERR_INVALID_ARG;
+  if (!aligned(packed, 16)) return TERN_ERR_ALIGNMENT;
+  hipError_t e = launch_unpack(packed, N, K, w, ldw, stream);
+  return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
+int tern_validate(const uint8_t* packed, int64_t N, int64_t K, int32_t* counts,
+                  hipStream_t stream) {
+  if (N < 0 || K < 1 || !counts) return TERN_ERR_INVALID_ARG;
+  if (K > TERN_MAX_K || N > kI32Max) return TERN_ERR_RANGE;
+  if (!aligned(counts, 4)) return TERN_ERR_ALIGNMENT;
+  if (N > 0 && !packed) return TERN_ERR_INVALID_ARG;
+  if (N > 0 && !aligned(packed, 16)) return TERN_ERR_ALIGNMENT;
+  hipError_t e = launch_zero_i32(counts, 2, stream);
+  if (e != hipSuccess) return hip_fail(e);
+  if (N == 0) return TERN_OK;
+  e = launch_validate(packed, N, K, counts, stream);
+  return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
+int tern_gemm_smallM(const uint8_t* packed, const float* s_row, const int32_t* rowsum, int64_t N,
+                     int64_t K, int64_t M, const int8_t* q, int64_t ldq, const float* s_act,
+                     const int32_t* z, float* y, int64_t ldy, int32_t* acc, int path,
+                     hipStream_t stream) {
+  int st = check_linear(packed, s_row, rowsum, N, K, M, q, ldq, s_act, z, y, ldy, acc);
+  if (st != TERN_OK) return st;
+  const int p = resolve_path(path, M < 1 ? 1 : M);
+  if (p < 0) return TERN_ERR_UNSUPPORTED;
+  if (N == 0 || M == 0) return TERN_OK;
+  const LinearArgs a = make_args(packed, s_row, rowsum, N, K, M, q, ldq, s_act, z, y, ldy, acc);
+  const hipError_t e = p == TERN_PATH_VALU ? launch_valu_linear(a, stream)
+                                           : launch_mfma_linear(a, stream);
+  return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
+int tern_gemv(const uint8_t* packed, const float* s_row, const int32_t* rowsum, int64_t N,
+              int64_t K, const int8_t* q, const float* s_act, const int32_t* z, float* y,
+              int32_t* acc, hipStream_t stream) {
+  return tern_gemm_smallM(packed, s_row, rowsum, N, K, 1, q, K, s_act, z, y, N, acc,
+                          TERN_PATH_AUTO, stream);
+}
+
+int64_t tern_linear_stack_workspace_bytes(int64_t L, int64_t M) {
+  if (L < 0 || M < 0 || L > kI32Max) return 0;
+  int cus = device_cus();
+  if (cus <= 0) cus = 256;
+  const int64_t workers = (int64_t)cus * kMaxWavesPerCu;
+  return layout_for(L, workers, workers + L).total;
+}
+
+int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
+                              void* workspace, int64_t workspace_bytes, tern_stack_plan* plan,
+                              hipStream_t stream) {
+  if (!plan || L < 0 || M < 0) return TERN_ERR_INVALID_ARG;
+  if (L > kI32Max || M > kI32Max) return TERN_ERR_RANGE;
+  if (L > 0 && !descs) return TERN_ERR_INVALID_ARG;
+  const int p = resolve_path(path, M < 1 ? 1 : M);
+  if (p < 0) return TERN_ERR_UNSUPPORTED;
+  // every descriptor is checked before anything is written
+  int64_t bytes = 0;
+  for (int64_t i = 0; i < L; ++i) {
+    const tern_linear_desc& d = descs[i];
+    const int st = check_linear(d.packed, d.s_row, d.rowsum, d.N, d.K, M, d.q, d.ldq, d.s_act,
+                                d.z, d.y, d.ldy, d.acc);
+    if (st != TERN_OK) return st;
+    if (d.N > 0 && M > 0)
+      bytes += d.N * row_bytes(d.K) + 8 * d.N + M * d.K + 8 * M + 4 * M * d.N;
+  }
+  memset(plan, 0, sizeof(*plan));
+  plan->workspace = workspace;
+  plan->workspace_bytes = workspace_bytes;
+  plan->L = (int32_t)L;
+  plan->M = (int32_t)M;
+  plan->path = p;
+  plan->bytes = bytes;
+  plan->block = kStackBlock;
+  if (L == 0 || M == 0) return TERN_OK;  // empty stack: launches nothing
+  if (!workspace) return TERN_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return TERN_ERR_WORKSPACE;
+
+  const int32_t kernel = p == TERN_PATH_VALU ? valu_stack_kernel_for(M) : (int32_t)SK_MFMA;
+  const int cus = device_cus();
+  if (cus <= 0) return hip_fail(hipErrorNoDevice);
+  int per_cu = p == TERN_PATH_VALU ? valu_stack_blocks_per_cu(kernel) : mfma_stack_blocks_per_cu((int32_t)M);
+  per_cu = std::min(per_cu, kMaxWavesPerCu / kWavesPerBlock);
+  int grid = cus * per_cu;
+  grid = std::max(8, grid / 8 * 8);  // a multiple of 8 for the XCD-aware numbering
+  const int64_t workers = (int64_t)grid * kWavesPerBlock;
+
+  // Granules: units of each linear's rows, cost = packed bytes + a fixed
+  // per-unit overhead; contiguous granule runs balanced over the workers.
+  std::vector<LinearArgs> lin((size_t)L);
+  struct Gran {
+    int32_t lin, r0, r1;
+    double cost;
+  };
+  std::vector<Gran> gran;
+  double total = 0.0;
+  for (int64_t i = 0; i < L; ++i) {
+    const tern_linear_desc& d = descs[i];
+    lin[(size_t)i] = make_args(d.packed, d.s_row, d.rowsum, d.N, d.K, M, d.q, d.ldq, d.s_act, d.z,
+                               d.y, d.ldy, d.acc);
+    if (d.N == 0) continue;
+    const int unit = p == TERN_PATH_VALU ? valu_unit_rows(lin[(size_t)i].variant, (int32_t)M)
+                                         : mfma_unit_rows((int32_t)M);
+    const double ld = (double)row_bytes(d.K);
+    for (int64_t r0 = 0; r0 < d.N; r0 += unit) {
+      const int64_t r1 = std::min<int64_t>(d.N, r0 + unit);
+      const double c = (double)(r1 - r0) * ld + 256.0;
+      gran.push_back({(int32_t)i, (int32_t)r0, (int32_t)r1, c});
+      total += c;
+    }
+  }
+  std::vector<int32_t> seg_start((size_t)workers + 1, 0);
+  std::vector<Segment> segs;
+  segs.reserve(gran.size() / 4 + (size_t)workers + (size_t)L);
+  double cum = 0.0;
+  int64_t cur_w = -1;
+  for (const Gran& g : gran) {
+    int64_t w = (int64_t)((cum + 0.5 * g.cost) / total * (double)workers);
+    if (w >= workers) w = workers - 1;
+    cum += g.cost;
+    if (!segs.empty() && w == cur_w && segs.back().lin == g.lin && segs.back().row_end == g.r0) {
+      segs.back().row_end = g.r1;
+      continue;
+    }
+    while (cur_w < w) seg_start[(size_t)(++cur_w)] = (int32_t)segs.size();
+    segs.push_back({g.lin, g.r0, g.r1, 0});
+  }
+  while (cur_w < workers) seg_start[(size_t)(++cur_w)] = (int32_t)segs.size();
+  // the loop above sets seg_start[w] for w <= cur_w as "first segment of w";
+  // worker w owns [seg_start[w], seg_start[w + 1]); the final entry is nseg
+  seg_start[(size_t)workers] = (int32_t)segs.size();
+
+  const Layout lay = layout_for(L, workers, (int64_t)segs.size());
+  if (workspace_bytes < lay.total) return TERN_ERR_WORKSPACE;
+  std::vector<char> host((size_t)lay.total, 0);
+  StackHeader h;
+  memset(&h, 0, sizeof(h));
+  h.magic = kStackMagic;
+  h.L = (int32_t)L;
+  h.M = (int32_t)M;
+  h.workers = (int32_t)workers;
+  h.nseg = (int32_t)segs.size();
+  h.kernel = kernel;
+  h.off_lin = lay.off_lin;
+  h.off_seg_start = lay.off_seg_start;
+  h.off_seg = lay.off_seg;
+  memcpy(host.data(), &h, sizeof(h));
+  memcpy(host.data() + lay.off_lin, lin.data(), lin.size() * sizeof(LinearArgs));
+  memcpy(host.data() + lay.off_seg_start, seg_start.data(), seg_start.size() * 4);
+  if (!segs.empty()) memcpy(host.data() + lay.off_seg, segs.data(), segs.size() * sizeof(Segment));
+  hipError_t e = hipMemcpyAsync(workspace, host.data(), (size_t)lay.total, hipMemcpyHostToDevice,
+                                stream);
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e);
+
+  plan->grid = grid;
+  plan->workers = (int32_t)workers;
+  plan->segments = (int32_t)segs.size();
+  plan->kernel = kernel;
+  return TERN_OK;
+}
+
+int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream) {
+  if (!plan) return TERN_ERR_INVALID_ARG;
+  if (plan->L == 0 || plan->M == 0 || plan->workers == 0) return TERN_OK;
+  if (!plan->workspace || !aligned(plan->workspace, 256)) return TERN_ERR_WORKSPACE;
+  LaunchShape shp;
+  shp.grid = plan->grid;
+  shp.block = plan->block;
+  shp.waves_per_block = plan->block / 64;
+  if (shp.grid <= 0 || shp.block != kStackBlock) return TERN_ERR_INVALID_ARG;
+  const hipError_t e = plan->kernel == SK_MFMA
+                           ? launch_mfma_stack(plan->M, plan->workspace, shp, stream)
+                           : launch_valu_stack(plan->kernel, plan->workspace, shp, stream);
+  return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
+}  // extern "C"

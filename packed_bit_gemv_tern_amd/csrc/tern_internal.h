@@ -1,0 +1,97 @@
+// tern_internal.h -- shared between the host API (tern_api.cpp) and the HIP
+// kernels: the device-side descriptor of one linear, the stack workspace
+// layout and the kernel launchers.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tern {
+
+// Kernel variants of the VALU path.  LPR = lanes per row (a row is split
+// over LPR lanes, 64 / LPR rows per wave-wide load), CPL = 16-byte chunks of
+// a row per lane (one chunk = 64 weights), so a row holds up to LPR*CPL
+// chunks.  The generic variant streams q from memory and takes any K.
+enum ValuVariant : int32_t {
+  V8x1 = 0,   // K <= 512
+  V16x1 = 1,  // K <= 1024
+  V32x1 = 2,  // K <= 2048
+  V16x3 = 3,  // K <= 3072
+  V64x1 = 4,  // K <= 4096
+  V64x2 = 5,  // K <= 8192
+  V64x3 = 6,  // K <= 12288
+  V64x4 = 7,  // K <= 16384
+  VGEN = 8,   // any K
+  kNumValuVariants = 9
+};
+
+// Device-side view of one linear layer; 96 bytes, read by the kernels from
+// kernel arguments (single-linear calls) or from the stack workspace.
+struct alignas(16) LinearArgs {
+  const uint8_t* packed;  // N rows of ld bytes
+  const float* s_row;     // N
+  const int32_t* rowsum;  // N
+  const int8_t* q;        // M rows of ldq bytes
+  const float* s_act;     // M
+  const int32_t* z;       // M
+  float* y;               // M rows of ldy floats
+  int32_t* acc;           // M rows of ldy int32, or null
+  int32_t N, K, ld, nch;  // rows, columns, row bytes, 16-byte chunks per row
+  int32_t ldq, ldy, M, variant;
+};
+static_assert(sizeof(LinearArgs) == 96, "LinearArgs layout");
+
+// One schedule entry: rows [row_begin, row_end) of linear `lin`.
+struct Segment {
+  int32_t lin, row_begin, row_end, pad;
+};
+
+// Stack workspace layout (device memory, 256-byte aligned):
+//   StackHeader | LinearArgs[L] | int32 seg_start[workers + 1] | Segment[nseg]
+struct alignas(256) StackHeader {
+  int32_t magic, L, M, workers, nseg, kernel, pad0, pad1;
+  int64_t off_lin, off_seg_start, off_seg;
+};
+constexpr int32_t kStackMagic = 0x7e54a11;
+
+// Kernel selectors of a prepared stack.
+enum StackKernel : int32_t {
+  SK_VALU_M1 = 0,
+  SK_VALU_M2 = 1,
+  SK_VALU_M4 = 2,
+  SK_VALU_M8 = 3,
+  SK_MFMA = 4
+};
+
+// Launch parameters chosen by the launchers below.
+struct LaunchShape {
+  int grid, block, waves_per_block;
+};
+
+// ---- launchers (defined in the .hip files) ----
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
+hipError_t launch_pack(const int8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed,
+                       int32_t* rowsum, int32_t* bad, hipStream_t s);
+hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* w, int64_t ldw,
+                         hipStream_t s);
+hipError_t launch_validate(const uint8_t* packed, int64_t N, int64_t K, int32_t* counts,
+                           hipStream_t s);
+
+// VALU path for one linear, M in {1, 2, 4} token registers (M <= 4).
+hipError_t launch_valu_linear(const LinearArgs& a, hipStream_t s);
+// MFMA path for one linear, any M.
+hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s);
+
+// Rows handled per work unit (schedule granularity) of each path.
+int valu_unit_rows(int32_t variant, int32_t M);
+int mfma_unit_rows(int32_t M);
+int32_t valu_variant_for(int64_t K);
+
+// Persistent stack launches over a prepared workspace.
+hipError_t launch_valu_stack(int32_t kernel, const void* ws, const LaunchShape& shp,
+                             hipStream_t s);
+int valu_stack_blocks_per_cu(int32_t kernel);
+hipError_t launch_mfma_stack(int32_t M, const void* ws, const LaunchShape& shp, hipStream_t s);
+int mfma_stack_blocks_per_cu(int32_t M);
+
+}  // namespace tern

@@ -1,0 +1,461 @@
+// tern_valu.hip -- VALU path of the ternary linear: in-register 2-bit decode
+// with add / subtract / skip accumulation through v_dot4_u32_u8.
+//
+// The article "Neutrino-1: quantization is a training decision, not a
+// deployment one" ("The take") says signed accumulation replaces multiplies;
+// the model card ("Overview") says packed weights are decoded inside the
+// matrix kernels.  Single-stream decode reads every weight once per token and
+// is bound by bytes moved (article, "Serving it: the Neutrino Engine"), so
+// this path is built around one coalesced 16-byte non-temporal load per lane
+// per 64 weights and as few VALU operations per weight as possible:
+//
+//  * activations are biased to unsigned once, qb = q + 128 (q ^ 0x80), and
+//    zero past K;
+//  * a packed 32-bit word w holds 16 weights; (w & 0x03030303 << 2k) keeps
+//    the codes c = w+1 of weights 4k..4k+3 scaled by 4^k, one per byte, so
+//    four ANDs and four unsigned dot4s against the matching qb bytes give
+//    4^k-scaled partial sums of c * qb -- 0.5 VALU operations per weight;
+//  * with S = sum_j c_j qb_j and QB = sum_{j<K} qb_j (padding has qb = 0):
+//      sum_j w_j q_j - z * rowsum = S - QB - (z + 128) * rowsum,
+//    all in wrapping 32-bit arithmetic, exact whenever the result fits in
+//    int32 (guaranteed by the host's K bound and |z| <= 255).
+//
+// A row is split over LPR lanes; each wave reduces U rows at once with a
+// transposed butterfly (v_permlane32/16_swap and DPP), so the cross-lane cost
+// is about two operations per row instead of six.
+#include "tern_device.h"
+
+namespace tern {
+
+namespace {
+
+constexpr uint32_t kPlane0 = 0x03030303u, kPlane1 = 0x0C0C0C0Cu, kPlane2 = 0x30303030u,
+                   kPlane3 = 0xC0C0C0C0u;
+constexpr uint32_t kBias = 0x80808080u, kOnes = 0x01010101u;
+
+__device__ __forceinline__ uint32_t udot4(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_udot4(a, b, c, false);
+}
+
+// 64 biased activations of one token, [64*ch, 64*ch + 64), zero past K.
+// Without RAGGED the caller guarantees 64*ch + 64 <= K.
+template <bool RAGGED>
+__device__ __forceinline__ void load_q_chunk(const int8_t* q, int K, int ch, uint32_t (&out)[16]) {
+  const int j0 = ch * 64;
+  if (!RAGGED || j0 + 64 <= K) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 t = load16(q + j0 + 16 * i);
+      out[4 * i + 0] = t.x ^ kBias;
+      out[4 * i + 1] = t.y ^ kBias;
+      out[4 * i + 2] = t.z ^ kBias;
+      out[4 * i + 3] = t.w ^ kBias;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int j = j0 + 4 * i + b;
+        if (j < K) v |= (uint32_t)((uint8_t)load_g(q + j) ^ 0x80u) << (8 * b);
+      }
+      out[i] = v;
+    }
+  }
+}
+
+// Accumulate the four 4^k-scaled planes of one 16-byte weight chunk against
+// the matching 64 biased activations.
+__device__ __forceinline__ void dot_chunk(const u32x4 w, const uint32_t (&qc)[16], uint32_t (&p)[4]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t x = w[d];
+    p[0] = udot4(x & kPlane0, qc[4 * d + 0], p[0]);
+    p[1] = udot4(x & kPlane1, qc[4 * d + 1], p[1]);
+    p[2] = udot4(x & kPlane2, qc[4 * d + 2], p[2]);
+    p[3] = udot4(x & kPlane3, qc[4 * d + 3], p[3]);
+  }
+}
+
+// 64 * sum(c * qb) from the four plane sums (plane k is 4^k-scaled).
+__device__ __forceinline__ uint32_t combine_scaled(const uint32_t (&p)[4]) {
+  return ((((p[0] << 2) + p[1]) << 2) + p[2]) * 4u + p[3];
+}
+
+// sum(c * qb) exactly, without the 64x headroom (any K).
+__device__ __forceinline__ uint32_t combine_exact(const uint32_t (&p)[4]) {
+  return p[0] + (p[1] >> 2) + (p[2] >> 4) + (p[3] >> 6);
+}
+
+template <int N>
+__device__ __forceinline__ uint32_t pick(const uint32_t (&v)[N], int i) {
+  uint32_t r = v[0];
+#pragma unroll
+  for (int k = 1; k < N; ++k) r = (i == k) ? v[k] : r;
+  return r;
+}
+
+__device__ __forceinline__ void store_out(const LinearArgs& a, int m, int row, uint32_t s,
+                                          uint32_t qb_sum, int32_t zb, int32_t rs, float sr,
+                                          float sa) {
+  const int32_t acc = (int32_t)(s - qb_sum - (uint32_t)zb * (uint32_t)rs);
+  const int64_t o = (int64_t)m * a.ldy + row;
+  store_g(a.y + o, epilogue(sr, acc, sa));
+  if (a.acc) store_g(a.acc + o, acc);
+}
+
+// ---------------------------------------------------------------------------
+// One token, activations held in registers: lane (sub, r) of the wave owns
+// chunks r, r + LPR, ..., r + LPR*(CPL-1) of rows  base + u*RPW + sub.
+// Units of U*RPW rows are taken as unit0, unit0 + ustride, ... inside
+// [row_lo, row_hi).
+template <int LPR, int CPL, int U, bool RAGGED>
+__device__ __forceinline__ void valu_range_reg(const LinearArgs& a, int row_lo, int row_hi,
+                                               int unit0, int ustride, int lane) {
+  constexpr int RPW = 64 / LPR;
+  constexpr int UNIT = U * RPW;
+  static_assert(U <= LPR, "U");
+  static_assert(64.0 * 510.0 * 64.0 * LPR * CPL < 2147483648.0, "scaled sum headroom");
+  const int sub = lane / LPR, r = lane % LPR;
+  const int nch = a.nch;
+
+  uint32_t qc[CPL][16];
+  uint32_t qsum = 0;
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) {
+    const int ch = r + LPR * t;
+    if (ch < nch) {
+      load_q_chunk<RAGGED>(a.q, a.K, ch, qc[t]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qc[t][i] = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qsum = udot4(qc[t][i], kOnes, qsum);
+  }
+  const uint32_t qb_sum = group_sum<LPR>(qsum);
+
+  const int my_u = split_index<LPR, U>(lane);
+  const bool writer = (r % (LPR / U)) == 0;
+  const float sa = load_g(a.s_act);
+  const int32_t zb = load_g(a.z) + 128;
+
+#pragma unroll 1
+  for (int unit = unit0;; unit += ustride) {
+    const int base = row_lo + unit * UNIT;
+    if (base >= row_hi) break;
+    u32x4 w[U][CPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = base + u * RPW + sub;
+#pragma unroll
+      for (int t = 0; t < CPL; ++t) {
+        const int ch = r + LPR * t;
+        if (row < row_hi && ch < nch)
+          w[u][t] = load_weights16(a.packed + (int64_t)row * a.ld + 16 * ch);
+        else
+          w[u][t] = u32x4{0, 0, 0, 0};
+      }
+    }
+    const int my_row = base + my_u * RPW + sub;
+    const bool do_store = writer && my_row < row_hi;
+    int32_t rs = 0;
+    float sr = 0.f;
+    if (do_store) {
+      rs = load_g(a.rowsum + my_row);
+      sr = load_g(a.s_row + my_row);
+    }
+    uint32_t part[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t p[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < CPL; ++t) dot_chunk(w[u][t], qc[t], p);
+      part[u] = combine_scaled(p);
+    }
+    const uint32_t tot = reduce_split<LPR, U>(part, lane);
+    if (do_store) store_out(a, 0, my_row, tot >> 6, qb_sum, zb, rs, sr, sa);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Any K, MT tokens (rows of q streamed through registers one 64-weight chunk
+// at a time).  One row per 64 lanes, U rows per unit.
+template <int U, int MT>
+__device__ __forceinline__ void valu_range_stream(const LinearArgs& a, int row_lo, int row_hi,
+                                                  int unit0, int ustride, int lane) {
+  constexpr int NV = U * MT;
+  static_assert(NV <= 64, "NV");
+  const int nch = a.nch;
+  const int M = a.M;
+
+  // biased activation sums per token
+  uint32_t qb_sums[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    uint32_t s = 0;
+    if (m < M) {
+      for (int ch = lane; ch < nch; ch += 64) {
+        uint32_t qc[16];
+        load_q_chunk<true>(a.q + (int64_t)m * a.ldq, a.K, ch, qc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s = udot4(qc[i], kOnes, s);
+      }
+    }
+    qb_sums[m] = group_sum<64>(s);
+  }
+
+  const int vidx = split_index<64, NV>(lane);
+  const int my_u = vidx / MT, my_m = vidx % MT;
+  const bool writer = (lane % (64 / NV)) == 0;
+  const uint32_t my_qb = pick<MT>(qb_sums, my_m);
+  const bool tok_ok = my_m < M;
+  const float sa = tok_ok ? load_g(a.s_act + my_m) : 0.f;
+  const int32_t zb = tok_ok ? load_g(a.z + my_m) + 128 : 0;
+
+#pragma unroll 1
+  for (int unit = unit0;; unit += ustride) {
+    const int base = row_lo + unit * U;
+    if (base >= row_hi) break;
+    uint32_t part[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) part[v] = 0;
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+      const int ch = c0 + lane;
+      u32x4 w[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int row = base + u;
+        w[u] = (row < row_hi && ch < nch) ? load_weights16(a.packed + (int64_t)row * a.ld + 16 * ch)
+                                          : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        uint32_t qc[16];
+        if (m < M && ch < nch) {
+          load_q_chunk<true>(a.q + (int64_t)m * a.ldq, a.K, ch, qc);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) qc[i] = 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          uint32_t p[4] = {0, 0, 0, 0};
+          dot_chunk(w[u], qc, p);
+          part[u * MT + m] += combine_exact(p);
+        }
+      }
+    }
+    const int my_row = base + my_u;
+    const bool do_store = writer && tok_ok && my_row < row_hi;
+    const uint32_t tot = reduce_split<64, NV>(part, lane);
+    if (do_store) {
+      store_out(a, my_m, my_row, tot, my_qb, zb, load_g(a.rowsum + my_row),
+                load_g(a.s_row + my_row), sa);
+    }
+  }
+}
+
+// Rows per unit and dispatch of the register variants.
+template <int V>
+struct ValuCfg;
+template <> struct ValuCfg<V8x1>  { static constexpr int LPR = 8,  CPL = 1, U = 8; };
+template <> struct ValuCfg<V16x1> { static constexpr int LPR = 16, CPL = 1, U = 8; };
+template <> struct ValuCfg<V32x1> { static constexpr int LPR = 32, CPL = 1, U = 8; };
+template <> struct ValuCfg<V16x3> { static constexpr int LPR = 16, CPL = 3, U = 4; };
+template <> struct ValuCfg<V64x1> { static constexpr int LPR = 64, CPL = 1, U = 8; };
+template <> struct ValuCfg<V64x2> { static constexpr int LPR = 64, CPL = 2, U = 4; };
+template <> struct ValuCfg<V64x3> { static constexpr int LPR = 64, CPL = 3, U = 4; };
+template <> struct ValuCfg<V64x4> { static constexpr int LPR = 64, CPL = 4, U = 2; };
+constexpr int kStreamU = 8;
+
+template <int V, bool RAGGED>
+__device__ __forceinline__ void run_reg(const LinearArgs& a, int lo, int hi, int u0, int us, int lane) {
+  using C = ValuCfg<V>;
+  valu_range_reg<C::LPR, C::CPL, C::U, RAGGED>(a, lo, hi, u0, us, lane);
+}
+
+// M = 1, one segment of a prepared stack: the register variants for K a
+// multiple of 64, the streaming variant for everything else.
+__device__ __forceinline__ void valu_m1_segment(const LinearArgs& a, int lo, int hi, int lane) {
+  if ((a.K & 63) != 0) {
+    valu_range_stream<kStreamU, 1>(a, lo, hi, 0, 1, lane);
+    return;
+  }
+  switch (a.variant) {
+    case V8x1: run_reg<V8x1, false>(a, lo, hi, 0, 1, lane); break;
+    case V16x1: run_reg<V16x1, false>(a, lo, hi, 0, 1, lane); break;
+    case V32x1: run_reg<V32x1, false>(a, lo, hi, 0, 1, lane); break;
+    case V16x3: run_reg<V16x3, false>(a, lo, hi, 0, 1, lane); break;
+    case V64x1: run_reg<V64x1, false>(a, lo, hi, 0, 1, lane); break;
+    case V64x2: run_reg<V64x2, false>(a, lo, hi, 0, 1, lane); break;
+    case V64x3: run_reg<V64x3, false>(a, lo, hi, 0, 1, lane); break;
+    case V64x4: run_reg<V64x4, false>(a, lo, hi, 0, 1, lane); break;
+    default: valu_range_stream<kStreamU, 1>(a, lo, hi, 0, 1, lane); break;
+  }
+}
+
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / 64;
+
+__device__ __forceinline__ int wave_id_uniform() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
+// that consecutive schedule ranges land on the same XCD (and its L2).
+__device__ __forceinline__ int xcd_logical_block() {
+  const int n = gridDim.x, b = blockIdx.x;
+  return (n % 8 == 0) ? (b % 8) * (n / 8) + b / 8 : b;
+}
+
+}  // namespace
+
+template <int V, bool RAGGED>
+__global__ __launch_bounds__(kBlock) void valu_linear_kernel(LinearArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * kWavesPerBlock + wave_id_uniform();
+  const int nw = gridDim.x * kWavesPerBlock;
+  run_reg<V, RAGGED>(a, 0, a.N, wave, nw, lane);
+}
+
+template <int MT>
+__global__ __launch_bounds__(kBlock) void valu_stream_kernel(LinearArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * kWavesPerBlock + wave_id_uniform();
+  const int nw = gridDim.x * kWavesPerBlock;
+  valu_range_stream<(MT >= 8 ? 4 : kStreamU), MT>(a, 0, a.N, wave, nw, lane);
+}
+
+template <int MT>
+__global__ __launch_bounds__(kBlock) void valu_stack_kernel(const StackHeader* __restrict__ h) {
+  const int lane = threadIdx.x & 63;
+  const int worker = xcd_logical_block() * kWavesPerBlock + wave_id_uniform();
+  if (worker >= h->workers) return;
+  const LinearArgs* lin = reinterpret_cast<const LinearArgs*>(
+      reinterpret_cast<const char*>(h) + h->off_lin);
+  const int32_t* seg_start = reinterpret_cast<const int32_t*>(
+      reinterpret_cast<const char*>(h) + h->off_seg_start);
+  const Segment* seg = reinterpret_cast<const Segment*>(
+      reinterpret_cast<const char*>(h) + h->off_seg);
+  const int s1 = seg_start[worker + 1];
+  for (int s = seg_start[worker]; s < s1; ++s) {
+    const Segment sg = seg[s];
+    const LinearArgs a = lin[sg.lin];
+    if constexpr (MT == 1)
+      valu_m1_segment(a, sg.row_begin, sg.row_end, lane);
+    else
+      valu_range_stream<(MT >= 8 ? 4 : kStreamU), MT>(a, sg.row_begin, sg.row_end, 0, 1, lane);
+  }
+}
+
+// ------------------------------------------------------------- launchers --
+
+int32_t valu_variant_for(int64_t K) {
+  if (K <= 512) return V8x1;
+  if (K <= 1024) return V16x1;
+  if (K <= 2048) return V32x1;
+  if (K <= 3072) return V16x3;
+  if (K <= 4096) return V64x1;
+  if (K <= 8192) return V64x2;
+  if (K <= 12288) return V64x3;
+  if (K <= 16384) return V64x4;
+  return VGEN;
+}
+
+static int stream_u(int32_t M) { return M > 4 ? 4 : kStreamU; }
+
+int valu_unit_rows(int32_t variant, int32_t M) {
+  if (M > 1) return stream_u(M);
+  switch (variant) {
+    case V8x1: return ValuCfg<V8x1>::U * 64 / ValuCfg<V8x1>::LPR;
+    case V16x1: return ValuCfg<V16x1>::U * 64 / ValuCfg<V16x1>::LPR;
+    case V32x1: return ValuCfg<V32x1>::U * 64 / ValuCfg<V32x1>::LPR;
+    case V16x3: return ValuCfg<V16x3>::U * 64 / ValuCfg<V16x3>::LPR;
+    case V64x1: return ValuCfg<V64x1>::U;
+    case V64x2: return ValuCfg<V64x2>::U;
+    case V64x3: return ValuCfg<V64x3>::U;
+    case V64x4: return ValuCfg<V64x4>::U;
+    default: return kStreamU;
+  }
+}
+
+static int blocks_for_units(int64_t units) {
+  // enough waves to cover the units, capped at 64 workgroups per CU-sized
+  // slice; each wave loops over its units
+  int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  return (int)blocks;
+}
+
+hipError_t launch_valu_linear(const LinearArgs& a, hipStream_t s) {
+  const int64_t units = (a.N + valu_unit_rows(a.variant, a.M) - 1) / valu_unit_rows(a.variant, a.M);
+  const dim3 grid(blocks_for_units(units)), block(kBlock);
+  if (a.M == 1) {
+    const bool ragged = (a.K & 63) != 0;
+#define TERN_REG_CASE(V)                                                              \
+  case V:                                                                             \
+    if (ragged)                                                                       \
+      hipLaunchKernelGGL((valu_linear_kernel<V, true>), grid, block, 0, s, a);        \
+    else                                                                              \
+      hipLaunchKernelGGL((valu_linear_kernel<V, false>), grid, block, 0, s, a);       \
+    break;
+    switch (a.variant) {
+      TERN_REG_CASE(V8x1)
+      TERN_REG_CASE(V16x1)
+      TERN_REG_CASE(V32x1)
+      TERN_REG_CASE(V16x3)
+      TERN_REG_CASE(V64x1)
+      TERN_REG_CASE(V64x2)
+      TERN_REG_CASE(V64x3)
+      TERN_REG_CASE(V64x4)
+      default: hipLaunchKernelGGL(valu_stream_kernel<1>, grid, block, 0, s, a); break;
+    }
+#undef TERN_REG_CASE
+  } else if (a.M == 2) {
+    hipLaunchKernelGGL(valu_stream_kernel<2>, grid, block, 0, s, a);
+  } else if (a.M <= 4) {
+    hipLaunchKernelGGL(valu_stream_kernel<4>, grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL(valu_stream_kernel<8>, grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_valu_stack(int32_t kernel, const void* ws, const LaunchShape& shp, hipStream_t s) {
+  const StackHeader* h = static_cast<const StackHeader*>(ws);
+  const dim3 grid(shp.grid), block(shp.block);
+  switch (kernel) {
+    case SK_VALU_M1: hipLaunchKernelGGL(valu_stack_kernel<1>, grid, block, 0, s, h); break;
+    case SK_VALU_M2: hipLaunchKernelGGL(valu_stack_kernel<2>, grid, block, 0, s, h); break;
+    case SK_VALU_M4: hipLaunchKernelGGL(valu_stack_kernel<4>, grid, block, 0, s, h); break;
+    case SK_VALU_M8: hipLaunchKernelGGL(valu_stack_kernel<8>, grid, block, 0, s, h); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int valu_stack_blocks_per_cu(int32_t kernel) {
+  int n = 0;
+  hipError_t e;
+  switch (kernel) {
+    case SK_VALU_M1:
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_stack_kernel<1>, kBlock, 0);
+      break;
+    case SK_VALU_M2:
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_stack_kernel<2>, kBlock, 0);
+      break;
+    case SK_VALU_M4:
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_stack_kernel<4>, kBlock, 0);
+      break;
+    default:
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_stack_kernel<8>, kBlock, 0);
+      break;
+  }
+  if (e != hipSuccess || n < 1) n = 1;
+  return n;
+}
+
+}  // namespace tern

@@ -21,16 +21,18 @@ Shapes and value distributions follow the Neutrino-1 pages:
     the article's 1-based "down 72.47 % at layer 3, gate 70.48 % at layer 4"
     and the wiki's "down 72.5 % at layer 2, gate 70.5 % at layer 3" agree.
 
-Recipe (numpy PCG64 ``default_rng``; draws in this order for every linear):
+Recipe (numpy PCG64 ``default_rng``).  Linear ``idx`` (0..6 in the order q,
+k, v, o, gate, up, down) of layer ``layer`` draws its weights from
+``default_rng([seed, layer, idx])``:
   1. W: one float32 uniform u per weight in row-major order; w = -1 if
      u < p_minus, 0 if u < p_minus + p_zero, else +1, with
      p_minus = p_plus = (1 - p_zero) / 2;
   2. s_row: ``uniform(0.01, 0.1, N)`` rounded to float32;
+and its M tokens of activations from ``default_rng([seed, layer, idx, M])``:
   3. q: ``integers(-128, 127, (M, K), int8, endpoint=True)``;
   4. per-token parameters: for M = 1, s_act = 0.02 and z = 3; for M > 1,
      s_act = ``uniform(0.01, 0.03, M)`` (float32) then z = ``integers(-8, 9, M)``.
-Linear ``idx`` (0..6 in the order q, k, v, o, gate, up, down) of layer
-``layer`` uses ``default_rng([seed, layer, idx])``.
+The same weights therefore serve every M.
 """
 from __future__ import annotations
 
@@ -128,13 +130,26 @@ class Linear:
         return self.q.shape[0]
 
 
-def make_linear(seed, layer: int, idx: int, N: int, K: int, p_zero: float, M: int,
-                name: str = "") -> Linear:
+def make_weights(seed, layer: int, idx: int, N: int, K: int, p_zero: float):
+    """(W int8 (N, K), s_row float32 (N,)) -- steps 1-2 of the recipe."""
     rng = np.random.default_rng([seed, layer, idx])
     w = ternary(rng, N, K, p_zero)
     s_row = rng.uniform(0.01, 0.1, N).astype(np.float32)
+    return w, s_row
+
+
+def make_activations(seed, layer: int, idx: int, K: int, M: int):
+    """(q int8 (M, K), s_act float32 (M,), z int32 (M,)) -- steps 3-4."""
+    rng = np.random.default_rng([seed, layer, idx, M])
     q = activations(rng, M, K)
     s_act, z = token_params(rng, M)
+    return q, s_act, z
+
+
+def make_linear(seed, layer: int, idx: int, N: int, K: int, p_zero: float, M: int,
+                name: str = "") -> Linear:
+    w, s_row = make_weights(seed, layer, idx, N, K, p_zero)
+    q, s_act, z = make_activations(seed, layer, idx, K, M)
     return Linear(name, w, s_row, q, s_act, z)
 
 

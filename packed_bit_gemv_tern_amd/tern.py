@@ -1,0 +1,191 @@
+"""ctypes binding of libtern.so (include/tern.h), with the same names.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels.  torch supplies device memory (``tensor.data_ptr()``) and the stream
+(``torch.cuda.current_stream().cuda_stream``).  Loading fails loudly when the
+shared library has not been built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtern.so")
+
+TERN_OK = 0
+TERN_ERR_INVALID_ARG = 1
+TERN_ERR_ALIGNMENT = 2
+TERN_ERR_RANGE = 3
+TERN_ERR_UNSUPPORTED = 4
+TERN_ERR_WORKSPACE = 5
+TERN_ERR_HIP = 6
+TERN_PATH_AUTO, TERN_PATH_VALU, TERN_PATH_MFMA = 0, 1, 2
+TERN_MAX_K = 5600000
+TERN_VALU_MAX_M = 8
+
+# Every function include/tern.h declares.
+EXPORTS = (
+    "tern_row_bytes", "tern_pack", "tern_unpack", "tern_validate", "tern_gemv",
+    "tern_gemm_smallM", "tern_linear_stack_workspace_bytes", "tern_linear_stack_prepare",
+    "tern_linear_stack", "tern_status_string", "tern_last_hip_error",
+)
+
+
+class TernError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = "%s: %s (status %d)" % (where, status_string(status), status)
+        if status == TERN_ERR_HIP:
+            msg += ", hipError %d" % _lib().tern_last_hip_error()
+        super().__init__(msg)
+
+
+class tern_linear_desc(ctypes.Structure):
+    _fields_ = [
+        ("packed", ctypes.c_void_p), ("s_row", ctypes.c_void_p), ("rowsum", ctypes.c_void_p),
+        ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("ldq", ctypes.c_int64),
+        ("s_act", ctypes.c_void_p), ("z", ctypes.c_void_p),
+        ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64), ("acc", ctypes.c_void_p),
+    ]
+
+
+class tern_stack_plan(ctypes.Structure):
+    _fields_ = [
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+        ("L", ctypes.c_int32), ("M", ctypes.c_int32), ("path", ctypes.c_int32),
+        ("grid", ctypes.c_int32), ("block", ctypes.c_int32), ("workers", ctypes.c_int32),
+        ("segments", ctypes.c_int32), ("kernel", ctypes.c_int32), ("bytes", ctypes.c_int64),
+    ]
+
+
+_lock = threading.Lock()
+_handle = None
+
+
+def _lib():
+    global _handle
+    if _handle is None:
+        with _lock:
+            if _handle is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        "libtern.so is not built (%s); run `python -m "
+                        "packed_bit_gemv_tern_amd.build` first" % LIB_PATH)
+                _handle = _declare(ctypes.CDLL(LIB_PATH))
+    return _handle
+
+
+def _declare(lib):
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    sig = {
+        "tern_row_bytes": (i64, [i64]),
+        "tern_pack": (i32, [vp, i64, i64, i64, vp, vp, vp, vp]),
+        "tern_unpack": (i32, [vp, i64, i64, vp, i64, vp]),
+        "tern_validate": (i32, [vp, i64, i64, vp, vp]),
+        "tern_gemv": (i32, [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp]),
+        "tern_gemm_smallM": (i32, [vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp,
+                                   i32, vp]),
+        "tern_linear_stack_workspace_bytes": (i64, [i64, i64]),
+        "tern_linear_stack_prepare": (i32, [ctypes.POINTER(tern_linear_desc), i64, i64, i32,
+                                            vp, i64, ctypes.POINTER(tern_stack_plan), vp]),
+        "tern_linear_stack": (i32, [ctypes.POINTER(tern_stack_plan), vp]),
+        "tern_status_string": (ctypes.c_char_p, [i32]),
+        "tern_last_hip_error": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _lib()
+
+
+def status_string(status: int) -> str:
+    return _lib().tern_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != TERN_OK:
+        raise TernError(status, where)
+
+
+def _ptr(t):
+    """Device address of a tensor (None -> NULL)."""
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
+
+
+# ------------------------------------------------------------ entry points --
+
+def tern_row_bytes(K: int) -> int:
+    return int(_lib().tern_row_bytes(int(K)))
+
+
+def tern_pack(w, N, K, ldw, packed, rowsum, bad_count=None, stream=None):
+    _check(_lib().tern_pack(_ptr(w), N, K, ldw, _ptr(packed), _ptr(rowsum), _ptr(bad_count),
+                            _stream(stream)), "tern_pack")
+
+
+def tern_unpack(packed, N, K, w, ldw, stream=None):
+    _check(_lib().tern_unpack(_ptr(packed), N, K, _ptr(w), ldw, _stream(stream)), "tern_unpack")
+
+
+def tern_validate(packed, N, K, counts, stream=None):
+    _check(_lib().tern_validate(_ptr(packed), N, K, _ptr(counts), _stream(stream)),
+           "tern_validate")
+
+
+def tern_gemv(packed, s_row, rowsum, N, K, q, s_act, z, y, acc=None, stream=None):
+    _check(_lib().tern_gemv(_ptr(packed), _ptr(s_row), _ptr(rowsum), N, K, _ptr(q), _ptr(s_act),
+                            _ptr(z), _ptr(y), _ptr(acc), _stream(stream)), "tern_gemv")
+
+
+def tern_gemm_smallM(packed, s_row, rowsum, N, K, M, q, ldq, s_act, z, y, ldy, acc=None,
+                     path=TERN_PATH_AUTO, stream=None):
+    _check(_lib().tern_gemm_smallM(_ptr(packed), _ptr(s_row), _ptr(rowsum), N, K, M, _ptr(q), ldq,
+                                   _ptr(s_act), _ptr(z), _ptr(y), ldy, _ptr(acc), int(path),
+                                   _stream(stream)), "tern_gemm_smallM")
+
+
+def tern_linear_stack_workspace_bytes(L: int, M: int) -> int:
+    return int(_lib().tern_linear_stack_workspace_bytes(int(L), int(M)))
+
+
+def make_desc(packed, s_row, rowsum, N, K, q, ldq, s_act, z, y, ldy, acc=None) -> tern_linear_desc:
+    d = tern_linear_desc()
+    d.packed, d.s_row, d.rowsum = packed.data_ptr(), s_row.data_ptr(), rowsum.data_ptr()
+    d.N, d.K = int(N), int(K)
+    d.q, d.ldq = q.data_ptr(), int(ldq)
+    d.s_act, d.z = s_act.data_ptr(), z.data_ptr()
+    d.y, d.ldy = y.data_ptr(), int(ldy)
+    d.acc = None if acc is None else acc.data_ptr()
+    return d
+
+
+def tern_linear_stack_prepare(descs, M, workspace, path=TERN_PATH_AUTO, stream=None):
+    """descs: a sequence of tern_linear_desc; workspace: a device tensor.
+    Returns the filled tern_stack_plan (keep it, and the buffers, alive)."""
+    arr = (tern_linear_desc * max(1, len(descs)))(*descs)
+    plan = tern_stack_plan()
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib().tern_linear_stack_prepare(arr, len(descs), int(M), int(path), _ptr(workspace),
+                                            nbytes, ctypes.byref(plan), _stream(stream)),
+           "tern_linear_stack_prepare")
+    return plan
+
+
+def tern_linear_stack(plan, stream=None):
+    _check(_lib().tern_linear_stack(ctypes.byref(plan), _stream(stream)), "tern_linear_stack")

@@ -1,0 +1,150 @@
+"""C ABI checks that need no GPU: the library loads, exports what the header
+declares, and argument errors come back as status codes before any launch
+(every call below fails validation, so nothing reaches the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from packed_bit_gemv_tern_amd import tern
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tern.h")
+
+
+def header_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tern_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tern.library()
+
+
+def test_header_lists_the_four_calls_and_helpers():
+    names = header_functions()
+    for n in ("tern_pack", "tern_gemv", "tern_gemm_smallM", "tern_linear_stack"):
+        assert n in names
+    assert set(names) == set(tern.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_row_bytes(lib):
+    for K, ld in [(0, 0), (-3, 0), (1, 16), (64, 16), (65, 32), (4096, 1024), (12288, 3072)]:
+        assert tern.tern_row_bytes(K) == ld
+
+
+def test_status_strings(lib):
+    for st in range(7):
+        assert tern.status_string(st)
+    assert tern.status_string(99) == "unknown status"
+    assert lib.tern_last_hip_error() == 0
+
+
+A16 = 0x10000        # a 16-byte-aligned fake device address (never dereferenced)
+ODD = 0x10008        # 8-byte aligned only
+S = None             # default stream
+
+
+def gemm(lib, packed=A16, s_row=A16, rowsum=A16, N=16, K=64, M=2, q=A16, ldq=64, s_act=A16,
+         z=A16, y=A16, ldy=16, acc=None, path=0):
+    return lib.tern_gemm_smallM(packed, s_row, rowsum, N, K, M, q, ldq, s_act, z, y, ldy, acc,
+                                path, S)
+
+
+def test_gemm_argument_errors(lib):
+    assert gemm(lib, K=0) == tern.TERN_ERR_INVALID_ARG
+    assert gemm(lib, K=-5) == tern.TERN_ERR_INVALID_ARG
+    assert gemm(lib, N=-1) == tern.TERN_ERR_INVALID_ARG
+    assert gemm(lib, M=-1) == tern.TERN_ERR_INVALID_ARG
+    assert gemm(lib, K=tern.TERN_MAX_K + 1) == tern.TERN_ERR_RANGE
+    assert gemm(lib, N=2 ** 31) == tern.TERN_ERR_RANGE
+    for field in ("packed", "s_row", "rowsum", "q", "s_act", "z", "y"):
+        assert gemm(lib, **{field: None}) == tern.TERN_ERR_INVALID_ARG, field
+    assert gemm(lib, ldq=63) == tern.TERN_ERR_INVALID_ARG
+    assert gemm(lib, ldy=15) == tern.TERN_ERR_INVALID_ARG
+    assert gemm(lib, packed=ODD) == tern.TERN_ERR_ALIGNMENT
+    assert gemm(lib, q=ODD) == tern.TERN_ERR_ALIGNMENT
+    assert gemm(lib, ldq=72) == tern.TERN_ERR_ALIGNMENT
+    assert gemm(lib, y=A16 + 2) == tern.TERN_ERR_ALIGNMENT
+    assert gemm(lib, acc=A16 + 1) == tern.TERN_ERR_ALIGNMENT
+    assert gemm(lib, path=tern.TERN_PATH_VALU, M=tern.TERN_VALU_MAX_M + 1) == tern.TERN_ERR_UNSUPPORTED
+    assert gemm(lib, path=7) == tern.TERN_ERR_UNSUPPORTED
+
+
+def test_empty_problems_enqueue_nothing(lib):
+    # N == 0 or M == 0 is valid and returns before any launch, even with
+    # null buffers
+    assert gemm(lib, N=0, packed=None, s_row=None, rowsum=None, y=None) == tern.TERN_OK
+    assert gemm(lib, M=0, q=None, s_act=None, z=None, y=None) == tern.TERN_OK
+    assert lib.tern_gemv(None, None, None, 0, 64, None, None, None, None, None, S) == tern.TERN_OK
+    assert lib.tern_pack(None, 0, 64, 64, None, None, None, S) == tern.TERN_OK
+    assert lib.tern_unpack(None, 0, 64, None, 64, S) == tern.TERN_OK
+
+
+def test_gemv_argument_errors(lib):
+    assert lib.tern_gemv(A16, A16, A16, 8, 0, A16, A16, A16, A16, None, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_gemv(ODD, A16, A16, 8, 64, A16, A16, A16, A16, None, S) == tern.TERN_ERR_ALIGNMENT
+    assert lib.tern_gemv(A16, A16, A16, 8, 64, None, A16, A16, A16, None, S) == tern.TERN_ERR_INVALID_ARG
+
+
+def test_pack_unpack_validate_errors(lib):
+    assert lib.tern_pack(A16, 4, 64, 63, A16, A16, None, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_pack(A16, 4, 0, 64, A16, A16, None, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_pack(A16, 4, 64, 64, ODD, A16, None, S) == tern.TERN_ERR_ALIGNMENT
+    assert lib.tern_pack(A16, 4, 64, 64, A16, A16 + 2, None, S) == tern.TERN_ERR_ALIGNMENT
+    assert lib.tern_pack(A16, 4, 64, 64, A16, A16, A16 + 1, S) == tern.TERN_ERR_ALIGNMENT
+    assert lib.tern_pack(None, 4, 64, 64, A16, A16, None, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_unpack(A16, 4, 64, A16, 10, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_unpack(ODD, 4, 64, A16, 64, S) == tern.TERN_ERR_ALIGNMENT
+    assert lib.tern_validate(A16, 4, 64, None, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_validate(A16, 4, 64, A16 + 2, S) == tern.TERN_ERR_ALIGNMENT
+    assert lib.tern_validate(ODD, 4, 64, A16, S) == tern.TERN_ERR_ALIGNMENT
+
+
+def _desc(**kw):
+    d = tern.tern_linear_desc()
+    d.packed = d.s_row = d.rowsum = d.q = d.s_act = d.z = d.y = A16
+    d.N, d.K, d.ldq, d.ldy = 16, 64, 64, 16
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_stack_prepare_errors(lib):
+    plan = tern.tern_stack_plan()
+    arr = (tern.tern_linear_desc * 2)(_desc(), _desc(K=0))
+    assert lib.tern_linear_stack_prepare(arr, 2, 1, 0, A16, 1 << 20, ctypes.byref(plan), S) \
+        == tern.TERN_ERR_INVALID_ARG
+    arr = (tern.tern_linear_desc * 2)(_desc(), _desc(packed=ODD))
+    assert lib.tern_linear_stack_prepare(arr, 2, 1, 0, A16, 1 << 20, ctypes.byref(plan), S) \
+        == tern.TERN_ERR_ALIGNMENT
+    arr = (tern.tern_linear_desc * 1)(_desc())
+    assert lib.tern_linear_stack_prepare(arr, 1, 1, 0, None, 1 << 20, ctypes.byref(plan), S) \
+        == tern.TERN_ERR_WORKSPACE
+    assert lib.tern_linear_stack_prepare(arr, 1, 1, 0, A16 + 16, 1 << 20, ctypes.byref(plan), S) \
+        == tern.TERN_ERR_WORKSPACE
+    assert lib.tern_linear_stack_prepare(arr, 1, 9, tern.TERN_PATH_VALU, A16, 1 << 20,
+                                         ctypes.byref(plan), S) == tern.TERN_ERR_UNSUPPORTED
+    assert lib.tern_linear_stack_prepare(arr, 1, 1, 0, A16, 1 << 20, None, S) \
+        == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_linear_stack(None, S) == tern.TERN_ERR_INVALID_ARG
+
+
+def test_stack_empty_plan(lib):
+    plan = tern.tern_stack_plan()
+    arr = (tern.tern_linear_desc * 1)(_desc())
+    assert lib.tern_linear_stack_prepare(arr, 0, 1, 0, None, 0, ctypes.byref(plan), S) == tern.TERN_OK
+    assert plan.L == 0 and plan.workers == 0 and plan.bytes == 0
+    assert lib.tern_linear_stack(ctypes.byref(plan), S) == tern.TERN_OK
+    assert lib.tern_linear_stack_prepare(arr, 1, 0, 0, None, 0, ctypes.byref(plan), S) == tern.TERN_OK
+    assert lib.tern_linear_stack(ctypes.byref(plan), S) == tern.TERN_OK

@@ -1,0 +1,49 @@
+"""Full-size parity: the whole 8B-shaped stack (252 linears, 6.95 G weights)
+in the launch configuration the benchmark times, at M = 1 and M = 8.  The
+oracle computes at least 256 sampled rows of every linear (first and last row
+included) from the same seeded weights and activations; the sampled packed
+bytes are compared too."""
+import numpy as np
+import pytest
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+from gpu_util import RTOL  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def stack():
+    from packed_bit_gemv_tern_amd.stack import DeviceStack
+    st = DeviceStack("8b", seed=0, threads=16, sample_rows=256)
+    yield st
+    del st
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("M", [1, 8])
+def test_full_8b_stack_sampled(stack, M):
+    b = stack.bind(M, with_acc=True)
+    assert b.plan.L == 252
+    b.run()
+    b.run()  # the benchmark launches the same plan back to back
+    torch.cuda.synchronize()
+    checked = 0
+    for i, pl in enumerate(stack.linears):
+        rows = pl.sample_rows
+        q, s_act, z = b.host_act[i]
+        rp, rr, bad = oracle.pack(pl.sample_w)
+        assert bad == 0
+        got_packed = pl.packed[torch.from_numpy(rows).to(pl.packed.device)].cpu().numpy()
+        assert np.array_equal(got_packed, rp), pl.name
+        assert np.array_equal(pl.rowsum.cpu().numpy()[rows], rr), pl.name
+        racc, ry32, ry64 = oracle.linear(rp, pl.sample_s_row, rr, pl.K, q, s_act, z)
+        acc = b.acc[i].cpu().numpy()[:, rows]
+        y = b.y[i].cpu().numpy()[:, rows]
+        assert np.array_equal(acc, racc), pl.name
+        assert np.all(np.abs(y.astype(np.float64) - ry64) <= RTOL * np.abs(ry64)), pl.name
+        assert np.array_equal(y.view(np.uint32), ry32.view(np.uint32)), pl.name
+        checked += rows.size
+    assert checked >= 252 * 256

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Integer results (packed bytes, row sums, int32 accumulators, counts) must be
+bit-exact; fp32 outputs must lie within 1e-6 relative of the oracle's fp64
+value and match its ordered fp32 evaluation bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from packed_bit_gemv_tern_amd import synth, tern
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from gpu_util import (DEV, Uploaded, assert_parity, gpu_pack, oracle_ref,  # noqa: E402
+                      to_dev)
+from test_oracle_pins import read_packed_rows  # noqa: E402
+
+
+def make(N, K, M, seed=0, p0=0.626):
+    return synth.make_linear(seed, N, K, N, K, p0, M, "t%dx%dx%d" % (N, K, M))
+
+
+# ------------------------------------------------------------------ pack --
+
+def test_pack_golden_rows():
+    for K, w, hx, rs in read_packed_rows():
+        packed, rowsum, bad = gpu_pack(w[None, :])
+        torch.cuda.synchronize()
+        assert packed.cpu().numpy().tobytes().hex() == hx, K
+        assert int(rowsum.item()) == rs and int(bad.item()) == 0
+
+
+@pytest.mark.parametrize("K", list(range(1, 131)) + [512, 1024, 2048, 3072, 4096, 12288])
+def test_pack_matches_oracle(K):
+    rng = np.random.default_rng(K)
+    N = 37
+    w = synth.ternary(rng, N, K, 0.626)
+    packed, rowsum, bad = gpu_pack(w)
+    rp, rr, rb = oracle.pack(w)
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), rp)
+    assert np.array_equal(rowsum.cpu().numpy(), rr)
+    assert int(bad.item()) == rb == 0
+
+
+def test_pack_strided_unaligned_rows_and_bad_values():
+    rng = np.random.default_rng(3)
+    N, K, ldw = 9, 77, 83  # rows neither 16-byte aligned nor a 16 multiple long
+    full = rng.integers(-1, 2, (N, ldw)).astype(np.int8)
+    full[2, 5] = 7
+    full[4, 76] = -128
+    full[6, 80] = 99  # past K: ignored
+    wd = to_dev(full)
+    packed = torch.empty((N, tern.tern_row_bytes(K)), dtype=torch.uint8, device=DEV)
+    rowsum = torch.empty(N, dtype=torch.int32, device=DEV)
+    bad = torch.empty(1, dtype=torch.int32, device=DEV)
+    tern.tern_pack(wd, N, K, ldw, packed, rowsum, bad)
+    rp, rr, rb = oracle.pack(full[:, :K])
+    torch.cuda.synchronize()
+    assert rb == 2 and int(bad.item()) == 2
+    assert np.array_equal(packed.cpu().numpy(), rp)
+    assert np.array_equal(rowsum.cpu().numpy(), rr)
+
+
+def test_unpack_roundtrip_and_validate():
+    rng = np.random.default_rng(4)
+    for K in (1, 15, 64, 100, 4096):
+        N = 21
+        w = synth.ternary(rng, N, K, 0.626)
+        packed, _, _ = gpu_pack(w)
+        back = torch.zeros((N, K + 3), dtype=torch.int8, device=DEV)
+        tern.tern_unpack(packed, N, K, back, K + 3)
+        counts = torch.full((2,), -1, dtype=torch.int32, device=DEV)
+        tern.tern_validate(packed, N, K, counts)
+        torch.cuda.synchronize()
+        assert np.array_equal(back.cpu().numpy()[:, :K], w)
+        assert counts.cpu().tolist() == [0, 0]
+        # corrupt: one 11 code in a real column, two non-01 padding fields
+        bad = packed.cpu().numpy().copy()
+        bad[3, 0] |= 0x03
+        extra_pad = 0
+        if K % 64:
+            j = K  # first padding column: byte 4*(j//16) + j%4, shift 2*((j%16)//4)
+            bad[5, 4 * (j // 16) + j % 4] &= ~(3 << (2 * ((j % 16) // 4))) & 0xFF
+            extra_pad = 1
+        badd = to_dev(bad)
+        tern.tern_validate(badd, N, K, counts)
+        torch.cuda.synchronize()
+        assert counts.cpu().tolist() == list(oracle.validate(bad, N, K)) == [1, extra_pad]
+        tern.tern_unpack(badd, N, K, back, K + 3)
+        ref, inv = oracle.unpack(bad, N, K)
+        torch.cuda.synchronize()
+        assert inv == 1 and np.array_equal(back.cpu().numpy()[:, :K], ref)
+
+
+# ------------------------------------------------------------------ gemv --
+
+def test_single_gemv_256x512_seed0():
+    lin = synth.single_gemv_case()
+    up = Uploaded(lin)
+    up.run()
+    y, acc = up.results()
+    assert_parity(y, acc, oracle_ref(lin), "256x512")
+
+
+GEMV_K = [1, 7, 63, 64, 65, 100, 500, 512, 1000, 1024, 1500, 2048, 2100, 3072, 3100, 4096,
+          4200, 8192, 12288, 16384, 16400, 20000]
+
+
+@pytest.mark.parametrize("K", GEMV_K)
+@pytest.mark.parametrize("N", [1, 5, 37, 300])
+def test_gemv_shapes(N, K):
+    lin = make(N, K, 1, seed=K * 7 + N)
+    up = Uploaded(lin)
+    up.run()
+    y, acc = up.results()
+    assert_parity(y, acc, oracle_ref(lin), "gemv N=%d K=%d" % (N, K))
+
+
+def test_gemv_extreme_values():
+    # worst-case magnitudes: q at -128 / 127, |z| = 255, all-nonzero rows
+    for qv, zv in [(-128, 255), (127, -255), (-128, -255)]:
+        N, K = 64, 12288
+        w = np.where(np.arange(K)[None, :] % 2 == 0, 1, -1).astype(np.int8).repeat(N, 0)
+        w[1] = 1
+        w[2] = -1
+        w[3] = 0
+        lin = synth.Linear("x", w, np.full(N, 0.1, np.float32), np.full((1, K), qv, np.int8),
+                           np.array([0.03], np.float32), np.array([zv], np.int32))
+        up = Uploaded(lin)
+        up.run()
+        y, acc = up.results()
+        assert_parity(y, acc, oracle_ref(lin), "extreme q=%d z=%d" % (qv, zv))
+
+
+def test_gemv_zero_weights_give_positive_zero():
+    N, K = 40, 4096
+    lin = synth.Linear("zero", np.zeros((N, K), np.int8), np.full(N, 0.05, np.float32),
+                       np.full((1, K), 9, np.int8), np.array([0.02], np.float32),
+                       np.array([3], np.int32))
+    up = Uploaded(lin)
+    up.run()
+    y, acc = up.results()
+    assert not acc.any()
+    assert np.all(y.view(np.uint32) == 0)
+
+
+def test_gemv_acc_optional_and_repeatable():
+    lin = make(300, 4096, 1, seed=11)
+    up = Uploaded(lin)
+    tern.tern_gemv(up.packed, up.s_row, up.rowsum, lin.N, lin.K, up.q, up.s_act, up.z, up.y, None)
+    torch.cuda.synchronize()
+    y1 = up.y.cpu().numpy().copy()
+    up.run()
+    y2, acc = up.results()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    assert_parity(y2, acc, oracle_ref(lin), "repeat")
+
+
+# --------------------------------------------------------------- small M --
+
+SMALLM_K = [64, 100, 1024, 3072, 4096, 12288]
+
+
+@pytest.mark.parametrize("M", list(range(1, 17)) + [17, 31, 64])
+@pytest.mark.parametrize("K", SMALLM_K)
+def test_gemm_mfma(M, K):
+    N = 70
+    lin = make(N, K, M, seed=M * 31 + K)
+    up = Uploaded(lin, ldy_extra=5)
+    up.run(tern.TERN_PATH_MFMA)
+    y, acc = up.results()
+    assert_parity(y, acc, oracle_ref(lin), "mfma M=%d K=%d" % (M, K))
+    # columns past N of each output row are untouched
+    torch.cuda.synchronize()
+    assert torch.isnan(up.y[:, N:]).all() and (up.acc[:, N:] == -7).all()
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("K", [64, 100, 4096, 12288, 20000])
+def test_gemm_valu(M, K):
+    N = 45
+    lin = make(N, K, M, seed=M * 13 + K)
+    up = Uploaded(lin, ldy_extra=3)
+    up.run(tern.TERN_PATH_VALU)
+    y, acc = up.results()
+    assert_parity(y, acc, oracle_ref(lin), "valu M=%d K=%d" % (M, K))
+
+
+@pytest.mark.parametrize("M", [64, 512])
+def test_gemm_prefill(M):
+    N, K = 200, 4096
+    lin = make(N, K, M, seed=M)
+    up = Uploaded(lin)
+    up.run()
+    y, acc = up.results()
+    assert_parity(y, acc, oracle_ref(lin), "prefill M=%d" % M)
+
+
+def test_gemm_empty_problems():
+    y = torch.full((4, 8), 5.0, device=DEV)
+    dummy8 = torch.zeros(64, dtype=torch.int8, device=DEV)
+    dummyf = torch.zeros(8, dtype=torch.float32, device=DEV)
+    dummyi = torch.zeros(8, dtype=torch.int32, device=DEV)
+    packed = torch.zeros(16 * 8, dtype=torch.uint8, device=DEV)
+    tern.tern_gemm_smallM(packed, dummyf, dummyi, 0, 64, 4, dummy8, 64, dummyf, dummyi, y, 8)
+    tern.tern_gemm_smallM(packed, dummyf, dummyi, 8, 64, 0, dummy8, 64, dummyf, dummyi, y, 8)
+    torch.cuda.synchronize()
+    assert (y == 5.0).all()
+
+
+# ----------------------------------------------------------------- stack --
+
+def _stack_case(model, layers, M, seed=0):
+    lins = synth.make_stack(seed, M, model=model, layers=layers, threads=8)
+    ups = [Uploaded(lin) for lin in lins]
+    return lins, ups
+
+
+@pytest.mark.parametrize("path", [tern.TERN_PATH_AUTO, tern.TERN_PATH_VALU, tern.TERN_PATH_MFMA])
+@pytest.mark.parametrize("M", [1, 8])
+def test_stack_06b_two_layers(M, path):
+    lins, ups = _stack_case("0.6b", 2, M)
+    L = len(ups)
+    ws = torch.empty(tern.tern_linear_stack_workspace_bytes(L, M), dtype=torch.uint8, device=DEV)
+    plan = tern.tern_linear_stack_prepare([u.desc() for u in ups], M, ws, path)
+    assert plan.L == L and plan.workers > 0
+    tern.tern_linear_stack(plan)
+    for lin, up in zip(lins, ups):
+        y, acc = up.results()
+        assert_parity(y, acc, oracle_ref(lin), "stack %s M=%d" % (lin.name, M))
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_stack_8b_one_layer(M):
+    lins, ups = _stack_case("8b", 1, M, seed=5)
+    ws = torch.empty(tern.tern_linear_stack_workspace_bytes(len(ups), M), dtype=torch.uint8,
+                     device=DEV)
+    plan = tern.tern_linear_stack_prepare([u.desc() for u in ups], M, ws)
+    tern.tern_linear_stack(plan)
+    tern.tern_linear_stack(plan)  # a second launch over the same plan
+    for lin, up in zip(lins, ups):
+        y, acc = up.results()
+        assert_parity(y, acc, oracle_ref(lin), "8b layer %s M=%d" % (lin.name, M))
+
+
+def test_stack_mixed_shapes_and_empty_linear():
+    specs = [(5, 1, 1), (300, 4096, 2), (0, 64, 3), (77, 100, 4), (40, 12288, 5), (129, 1000, 6)]
+    for M in (1, 3):
+        lins = [synth.make_linear(9, s, 0, N, K, 0.626, M, "m%d" % s) for (N, K, s) in specs]
+        ups = [Uploaded(lin) for lin in lins if lin.N > 0]
+        lins = [lin for lin in lins if lin.N > 0]
+        ws = torch.empty(tern.tern_linear_stack_workspace_bytes(len(ups) + 1, M),
+                         dtype=torch.uint8, device=DEV)
+        descs = [u.desc() for u in ups]
+        empty = tern.make_desc(ups[0].packed, ups[0].s_row, ups[0].rowsum, 0, 64, ups[0].q,
+                               ups[0].ldq, ups[0].s_act, ups[0].z, ups[0].y, ups[0].ldy)
+        plan = tern.tern_linear_stack_prepare(descs[:2] + [empty] + descs[2:], M, ws)
+        tern.tern_linear_stack(plan)
+        for lin, up in zip(lins, ups):
+            y, acc = up.results()
+            assert_parity(y, acc, oracle_ref(lin), "mixed %s M=%d" % (lin.name, M))
