@@ -55,6 +55,47 @@ def load_traffic(kernel: str):
     return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
+_VALU_SETS = {0: "80u", 1: "14u", 2: "255u", 3: "511u"}
+
+
+def kernel_name(plan) -> str:
+    """Name of the HIP kernel a prepared stack launches (as the profiler shows it)."""
+    k = plan.kernel
+    if k in _VALU_SETS:
+        return "valu_stack_kernel<1, %s>" % _VALU_SETS[k]
+    if k in (4, 5, 6):
+        return "valu_stack_kernel<%d, 0u>" % {4: 2, 5: 4, 6: 8}[k]
+    v = k - 8
+    return "mfma_stack_kernel<%d, %s>" % (4 if v & 1 else 1, "true" if v & 2 else "false")
+
+
+def read_probe(nbytes: int, reps: int = 5):
+    """Best plain-read rate over a few launch shapes (the achievable ceiling)."""
+    import torch
+    from packed_bit_gemv_tern_amd import tern
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    results = []
+    for bpc in (2, 4, 8):
+        for unroll in (8, 16):
+            for nt in (1, 0):
+                tern.tern_read_probe(buf, nbytes, sink, bpc, unroll, nt)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(reps):
+                    tern.tern_read_probe(buf, nbytes, sink, bpc, unroll, nt)
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                results.append({"blocks_per_cu": bpc, "unroll": unroll, "nontemporal": nt,
+                                "avg_us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1)})
+    del buf
+    best = max(results, key=lambda r: r["GBps"])
+    return {"bytes": nbytes, "best_GBps": best["GBps"], "best": best, "all": results}
+
+
 def cpu_baseline(seconds: float):
     """The oracle, as it stands, on a bounded sample of the same workload:
     layer 0's seven linears at M = 1 and at M = 8, repeated until `seconds`
@@ -99,8 +140,12 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="fewer layers (testing only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth probe")
     ap.add_argument("--only", choices=["m1", "m8"], default=None,
                     help="launch a single pass per step (for profiling)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times "
+                         "(reference for the HBM byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -116,14 +161,29 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
+    # Each pass gets its own copy of the stack (different seeds): the two
+    # passes never share weights, so neither can hit lines the other left in
+    # the caches (as in drafted decoding, where they are different models).
     t0 = time.time()
-    st = DeviceStack("8b", layers=args.layers, seed=0, threads=16)
-    log("packed %d linears, %d weights in %.1f s" % (len(st.linears), st.weights, time.time() - t0))
-    passes = []
-    if args.only != "m8":
-        passes.append(("m1", st.bind(1)))
-    if args.only != "m1":
-        passes.append(("m8", st.bind(8)))
+    passes, stacks = [], []
+    for name, M, seed in (("m1", 1, 0), ("m8", 8, 1)):
+        if args.only not in (None, name):
+            continue
+        st = DeviceStack("8b", layers=args.layers, seed=seed, threads=16)
+        stacks.append(st)
+        passes.append((name, st.bind(M)))
+    st = stacks[0]
+    log("packed %d x %d linears, %d weights each, in %.1f s"
+        % (len(stacks), len(st.linears), st.weights, time.time() - t0))
     stream = torch.cuda.current_stream()
 
     def step(events=None):
@@ -156,10 +216,7 @@ def main():
         ms = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]
         ms.sort()
         avg = sum(ms) / len(ms)
-        kname = "valu_stack_kernel<1>" if b.plan.kernel == 0 else (
-            "mfma_stack_kernel<1>" if b.M <= 16 else "mfma_stack_kernel<4>")
-        if b.plan.kernel in (1, 2, 3):
-            kname = "valu_stack_kernel<%d>" % {1: 2, 2: 4, 3: 8}[b.plan.kernel]
+        kname = kernel_name(b.plan)
         per_pass[name] = {
             "M": b.M, "kernel": kname, "bytes": b.bytes, "avg_us": round(avg * 1e3, 3),
             "p10_us": round(ms[len(ms) // 10] * 1e3, 3), "p90_us": round(ms[(9 * len(ms)) // 10] * 1e3, 3),
@@ -189,7 +246,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "8B-shaped ternary linear stack: %d linears (%d layers x 7, hidden 4096, "
-                        "FFN 12288), %d weights, one M=1 pass + one M=8 pass per step"
+                        "FFN 12288), %d weights; per step one M=1 pass and one M=8 pass, each "
+                        "over its own resident copy of the stack"
                         % (len(st.linears), len(st.linears) // 7, st.weights),
             "bytes_per_step": step_bytes,
             "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
@@ -197,6 +255,11 @@ def main():
         "passes": per_pass,
         "roofline": roofline,
     }
+    if not args.no_probe:
+        probe = read_probe(max(b.bytes for _, b in passes) // 16 * 16)
+        out["read_probe"] = probe
+        for name in per_pass:
+            per_pass[name]["frac_of_probe"] = round(per_pass[name]["GBps"] / probe["best_GBps"], 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -209,6 +209,20 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
 /* tern_linear_stack -- one persistent launch over the prepared stack. */
 int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream);
 
+/*
+ * tern_read_probe -- a measurement aid, not part of the method: reads `bytes`
+ * bytes of `buf` (device, 16-byte aligned, bytes a multiple of 16) with the
+ * same 16-byte loads and workgroup shape as the GEMV kernels and does nothing
+ * else, so its rate is the achievable read-bandwidth ceiling.
+ *   sink           device, one uint32; written only when the XOR of all data
+ *                  happens to equal a fixed constant (it keeps the loads live)
+ *   blocks_per_cu  1..8 workgroups of 256 threads per compute unit
+ *   unroll         4, 8 or 16 loads in flight per lane
+ *   nontemporal    nonzero: streaming (non-temporal) loads, as the kernels use
+ */
+int tern_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int blocks_per_cu, int unroll,
+                    int nontemporal, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* tern_status_string(int status);
 

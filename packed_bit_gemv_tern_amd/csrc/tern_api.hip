@@ -80,13 +80,6 @@ int resolve_path(int path, int64_t M) {
   }
 }
 
-int32_t valu_stack_kernel_for(int64_t M) {
-  if (M == 1) return SK_VALU_M1;
-  if (M == 2) return SK_VALU_M2;
-  if (M <= 4) return SK_VALU_M4;
-  return SK_VALU_M8;
-}
-
 int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -235,10 +228,20 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   if (!workspace) return TERN_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return TERN_ERR_WORKSPACE;
 
-  const int32_t kernel = p == TERN_PATH_VALU ? valu_stack_kernel_for(M) : (int32_t)SK_MFMA;
+  uint32_t used = 0;
+  for (int64_t i = 0; i < L; ++i) {
+    if (descs[i].N == 0) continue;
+    const int32_t v = descs[i].K % 64 ? (int32_t)VGEN : valu_variant_for(descs[i].K);
+    used |= 1u << v;
+  }
+  const bool ragged = (used >> VGEN) & 1u;
+  const int32_t kernel = p == TERN_PATH_VALU
+                             ? valu_stack_kernel_for((int32_t)M, used)
+                             : (int32_t)SK_MFMA + mfma_stack_variant((int32_t)M, ragged);
   const int cus = device_cus();
   if (cus <= 0) return hip_fail(hipErrorNoDevice);
-  int per_cu = p == TERN_PATH_VALU ? valu_stack_blocks_per_cu(kernel) : mfma_stack_blocks_per_cu((int32_t)M);
+  int per_cu = p == TERN_PATH_VALU ? valu_stack_blocks_per_cu(kernel)
+                                   : mfma_stack_blocks_per_cu(kernel - SK_MFMA);
   per_cu = std::min(per_cu, kMaxWavesPerCu / kWavesPerBlock);
   int grid = cus * per_cu;
   grid = std::max(8, grid / 8 * 8);  // a multiple of 8 for the XCD-aware numbering
@@ -320,6 +323,19 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   return TERN_OK;
 }
 
+int tern_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int blocks_per_cu, int unroll,
+                    int nontemporal, hipStream_t stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16 != 0) return TERN_ERR_INVALID_ARG;
+  if (blocks_per_cu < 1 || blocks_per_cu > kMaxWavesPerCu / kWavesPerBlock) return TERN_ERR_INVALID_ARG;
+  if (unroll != 4 && unroll != 8 && unroll != 16) return TERN_ERR_UNSUPPORTED;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return TERN_ERR_ALIGNMENT;
+  const int cus = device_cus();
+  if (cus <= 0) return hip_fail(hipErrorNoDevice);
+  const hipError_t e =
+      launch_read_probe(buf, bytes, sink, cus * blocks_per_cu, unroll, nontemporal != 0, stream);
+  return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
 int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream) {
   if (!plan) return TERN_ERR_INVALID_ARG;
   if (plan->L == 0 || plan->M == 0 || plan->workers == 0) return TERN_OK;
@@ -329,8 +345,8 @@ int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream) {
   shp.block = plan->block;
   shp.waves_per_block = plan->block / 64;
   if (shp.grid <= 0 || shp.block != kStackBlock) return TERN_ERR_INVALID_ARG;
-  const hipError_t e = plan->kernel == SK_MFMA
-                           ? launch_mfma_stack(plan->M, plan->workspace, shp, stream)
+  const hipError_t e = plan->kernel >= SK_MFMA
+                           ? launch_mfma_stack(plan->kernel - SK_MFMA, plan->workspace, shp, stream)
                            : launch_valu_stack(plan->kernel, plan->workspace, shp, stream);
   return e == hipSuccess ? TERN_OK : hip_fail(e);
 }

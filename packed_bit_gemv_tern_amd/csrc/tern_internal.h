@@ -55,12 +55,14 @@ struct alignas(256) StackHeader {
 constexpr int32_t kStackMagic = 0x7e54a11;
 
 // Kernel selectors of a prepared stack.
+// SK_VALU_M1 .. SK_VALU_M1 + 3 are the M = 1 kernel compiled for growing
+// variant sets (8B shapes, 0.6B shapes, every register variant, all).
 enum StackKernel : int32_t {
   SK_VALU_M1 = 0,
-  SK_VALU_M2 = 1,
-  SK_VALU_M4 = 2,
-  SK_VALU_M8 = 3,
-  SK_MFMA = 4
+  SK_VALU_M2 = 4,
+  SK_VALU_M4 = 5,
+  SK_VALU_M8 = 6,
+  SK_MFMA = 8  // SK_MFMA + mfma_stack_variant(M, ragged)
 };
 
 // Launch parameters chosen by the launchers below.
@@ -88,10 +90,15 @@ int mfma_unit_rows(int32_t M);
 int32_t valu_variant_for(int64_t K);
 
 // Persistent stack launches over a prepared workspace.
+int32_t valu_stack_kernel_for(int32_t M, uint32_t used_variants);
 hipError_t launch_valu_stack(int32_t kernel, const void* ws, const LaunchShape& shp,
                              hipStream_t s);
 int valu_stack_blocks_per_cu(int32_t kernel);
-hipError_t launch_mfma_stack(int32_t M, const void* ws, const LaunchShape& shp, hipStream_t s);
-int mfma_stack_blocks_per_cu(int32_t M);
+int32_t mfma_stack_variant(int32_t M, bool ragged);
+hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape& shp,
+                             hipStream_t s);
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int grid, int unroll,
+                             bool nontemporal, hipStream_t s);
+int mfma_stack_blocks_per_cu(int32_t variant);
 
 }  // namespace tern

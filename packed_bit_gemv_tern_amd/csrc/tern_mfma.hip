@@ -46,12 +46,9 @@ __device__ __forceinline__ i32x4 decode_word(uint32_t x) {
   return b;
 }
 
-// 16 activations of token row `qrow` starting at column j0, zero past K.
-__device__ __forceinline__ i32x4 load_q16(const int8_t* qrow, int K, int j0) {
-  if (j0 + 16 <= K) {
-    const u32x4 t = load16(qrow + j0);
-    return i32x4{(int32_t)t.x, (int32_t)t.y, (int32_t)t.z, (int32_t)t.w};
-  }
+// 16 activations of token row `qrow` starting at column j0, zero past K
+// (the ragged tail of K; K a multiple of 64 never takes this path).
+__device__ __forceinline__ i32x4 load_q16_tail(const int8_t* qrow, int K, int j0) {
   i32x4 v = {0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -66,53 +63,111 @@ __device__ __forceinline__ i32x4 load_q16(const int8_t* qrow, int K, int j0) {
   return v;
 }
 
+__device__ __forceinline__ i32x4 as_i32x4(u32x4 t) {
+  return i32x4{(int32_t)t.x, (int32_t)t.y, (int32_t)t.z, (int32_t)t.w};
+}
+
+// LDS tile of one wave: 16*R rows of one K-step (128 packed bytes = 512
+// weights per row), rows 144 bytes apart so that the 16 lanes reading 16
+// rows at the same offset hit 16 disjoint groups of 4 banks.
+constexpr int kStepBytes = 128;
+constexpr int kRowPitch = 144;
+
 // Units of 16*R rows, unit0 + k*ustride, inside [row_lo, row_hi); every
 // token group of T*16 tokens for each unit.
-template <int R, int T>
+//
+// Weights go HBM -> registers -> this wave's LDS tile -> registers:
+//  * global: wave-wide load i brings rows 8i..8i+7 of the tile, lane l the
+//    16 bytes at 16*(l%8) of row 8i + l/8 -- each instruction reads eight
+//    whole 128-byte lines, non-temporal (a pattern reading half lines made
+//    the L2 fetch every line twice);
+//  * LDS: lane (r, g) of row block b reads bytes [32g, 32g+32) of row
+//    16b + r, i.e. packed words 8g..8g+7 of the step; MFMA (half, j) takes
+//    word 8g + 4*half + j, weights 128g + 64*half + 16j .. +15 of the step,
+//    and the activations at the same 16 positions;
+//  * the next step's global loads are issued before the current step is
+//    consumed.  LDS accesses of one wave execute in order, so the tile needs
+//    no barrier.
+template <int R, int T, bool RAGGED>
 __device__ __forceinline__ void mfma_range(const LinearArgs& a, int row_lo, int row_hi, int unit0,
-                                           int ustride, int lane) {
+                                           int ustride, int lane, uint8_t* tile) {
   constexpr int UNIT = 16 * R;
+  constexpr int NLD = UNIT / 8;  // wave-wide 1 KB loads per K-step
   const int r = lane & 15, g = lane >> 4;
+  const int lrow = lane >> 3, lchunk = lane & 7;
   const int nch = a.nch, K = a.K, M = a.M;
-  const int nks = (nch + 3) / 4;  // K-steps of 4 chunks (256 weights)
+  const int nks = (nch + 7) / 8;
 
+#pragma unroll 1
   for (int unit = unit0;; unit += ustride) {
     const int base = row_lo + unit * UNIT;
     if (base >= row_hi) break;
+    const uint8_t* src[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+      src[i] = a.packed + (int64_t)min(base + 8 * i + lrow, row_hi - 1) * a.ld;
+
     for (int tok0 = 0; tok0 < M; tok0 += 16 * T) {
       i32x4 acc[R][T];
 #pragma unroll
       for (int b = 0; b < R; ++b)
 #pragma unroll
         for (int t = 0; t < T; ++t) acc[b][t] = i32x4{0, 0, 0, 0};
+      const int8_t* qrows[T];
+      bool tok_ok[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int m = tok0 + 16 * t + r;
+        tok_ok[t] = m < M;
+        qrows[t] = a.q + (int64_t)min(m, M - 1) * a.ldq;
+      }
 
+      u32x4 st[NLD];
+      {
+        const int ch = min(lchunk, nch - 1);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) st[i] = load_weights16(src[i] + 16 * ch);
+      }
       for (int ks = 0; ks < nks; ++ks) {
-        const int ch = 4 * ks + g;
-        const bool ch_ok = ch < nch;
-        u32x4 w[R];
 #pragma unroll
-        for (int b = 0; b < R; ++b) {
-          const int row = base + 16 * b + r;
-          w[b] = (ch_ok && row < row_hi) ? load_weights16(a.packed + (int64_t)row * a.ld + 16 * ch)
-                                         : u32x4{0, 0, 0, 0};
-        }
-        i32x4 qa[T][4];
+        for (int i = 0; i < NLD; ++i)
+          *reinterpret_cast<u32x4*>(tile + (8 * i + lrow) * kRowPitch + 16 * lchunk) = st[i];
+        if (ks + 1 < nks) {
+          const int ch = min(8 * (ks + 1) + lchunk, nch - 1);
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          const int m = tok0 + 16 * t + r;
-          const int8_t* qrow = a.q + (int64_t)m * a.ldq;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            qa[t][j] = (ch_ok && m < M) ? load_q16(qrow, K, 64 * ch + 16 * j) : i32x4{0, 0, 0, 0};
+          for (int i = 0; i < NLD; ++i) st[i] = load_weights16(src[i] + 16 * ch);
         }
 #pragma unroll
-        for (int b = 0; b < R; ++b) {
+        for (int half = 0; half < 2; ++half) {
+          const int ch = 8 * ks + 2 * g + half;
+          const bool ch_ok = ch < nch;
+          const int chc = min(ch, nch - 1);
+          i32x4 qa[T][4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const i32x4 wb = decode_word(w[b][j]);
+          for (int t = 0; t < T; ++t) {
+            const bool ok = ch_ok && tok_ok[t];
 #pragma unroll
-            for (int t = 0; t < T; ++t)
-              acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[t][j], wb, acc[b][t], 0, 0, 0);
+            for (int j = 0; j < 4; ++j) {
+              const int j0 = 64 * chc + 16 * j;
+              i32x4 v;
+              if (RAGGED && j0 + 16 > K)
+                v = load_q16_tail(qrows[t], K, j0);
+              else
+                v = as_i32x4(load16(qrows[t] + j0));
+              qa[t][j] = ok ? v : i32x4{0, 0, 0, 0};
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < R; ++b) {
+            const u32x4 wv = *reinterpret_cast<const u32x4*>(
+                tile + (16 * b + r) * kRowPitch + 32 * g + 16 * half);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const i32x4 wb = decode_word(wv[j]);
+#pragma unroll
+              for (int t = 0; t < T; ++t)
+                acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[t][j], wb, acc[b][t], 0, 0, 0);
+            }
           }
         }
       }
@@ -154,18 +209,26 @@ __device__ __forceinline__ int xcd_logical_block() {
 
 }  // namespace
 
-template <int T>
+constexpr int kTileBytes = 16 * kR * kRowPitch;
+
+template <int T, bool RAGGED>
 __global__ __launch_bounds__(kBlock) void mfma_linear_kernel(LinearArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[kWavesPerBlock][kTileBytes];
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * kWavesPerBlock + wave_id_uniform();
+  const int w = wave_id_uniform();
+  const int wave = blockIdx.x * kWavesPerBlock + w;
   const int nw = gridDim.x * kWavesPerBlock;
-  mfma_range<kR, T>(a, 0, a.N, wave, nw, lane);
+  mfma_range<kR, T, RAGGED>(a, 0, a.N, wave, nw, lane, tiles[w]);
 }
 
-template <int T>
+// RAGGED: the stack holds a linear whose K is not a multiple of 64 (compiled
+// in only then; it costs registers).
+template <int T, bool RAGGED>
 __global__ __launch_bounds__(kBlock) void mfma_stack_kernel(const StackHeader* __restrict__ h) {
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[kWavesPerBlock][kTileBytes];
   const int lane = threadIdx.x & 63;
-  const int worker = xcd_logical_block() * kWavesPerBlock + wave_id_uniform();
+  const int w = wave_id_uniform();
+  const int worker = xcd_logical_block() * kWavesPerBlock + w;
   if (worker >= h->workers) return;
   const char* base = reinterpret_cast<const char*>(h);
   const LinearArgs* lin = reinterpret_cast<const LinearArgs*>(base + h->off_lin);
@@ -175,7 +238,10 @@ __global__ __launch_bounds__(kBlock) void mfma_stack_kernel(const StackHeader* _
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
-    mfma_range<kR, T>(a, sg.row_begin, sg.row_end, 0, 1, lane);
+    if (RAGGED && (a.K & 63) != 0)
+      mfma_range<kR, T, RAGGED>(a, sg.row_begin, sg.row_end, 0, 1, lane, tiles[w]);
+    else
+      mfma_range<kR, T, false>(a, sg.row_begin, sg.row_end, 0, 1, lane, tiles[w]);
   }
 }
 
@@ -189,28 +255,49 @@ hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
   const dim3 grid((unsigned)blocks), block(kBlock);
-  if (mfma_t(a.M) == 1)
-    hipLaunchKernelGGL(mfma_linear_kernel<1>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(mfma_linear_kernel<4>, grid, block, 0, s, a);
+  const bool ragged = (a.K & 63) != 0;
+  if (mfma_t(a.M) == 1) {
+    if (ragged)
+      hipLaunchKernelGGL((mfma_linear_kernel<1, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((mfma_linear_kernel<1, false>), grid, block, 0, s, a);
+  } else {
+    if (ragged)
+      hipLaunchKernelGGL((mfma_linear_kernel<4, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((mfma_linear_kernel<4, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_mfma_stack(int32_t M, const void* ws, const LaunchShape& shp, hipStream_t s) {
+// kernel selector of a prepared MFMA stack: bit 0 = T is 4, bit 1 = ragged K
+int32_t mfma_stack_variant(int32_t M, bool ragged) { return (mfma_t(M) == 4 ? 1 : 0) | (ragged ? 2 : 0); }
+
+template <typename F>
+static hipError_t with_mfma_stack_kernel(int32_t variant, F&& f) {
+  switch (variant) {
+    case 0: return f(mfma_stack_kernel<1, false>);
+    case 1: return f(mfma_stack_kernel<4, false>);
+    case 2: return f(mfma_stack_kernel<1, true>);
+    case 3: return f(mfma_stack_kernel<4, true>);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape& shp, hipStream_t s) {
   const StackHeader* h = static_cast<const StackHeader*>(ws);
   const dim3 grid(shp.grid), block(shp.block);
-  if (mfma_t(M) == 1)
-    hipLaunchKernelGGL(mfma_stack_kernel<1>, grid, block, 0, s, h);
-  else
-    hipLaunchKernelGGL(mfma_stack_kernel<4>, grid, block, 0, s, h);
-  return hipGetLastError();
+  return with_mfma_stack_kernel(variant, [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, h);
+    return hipGetLastError();
+  });
 }
 
-int mfma_stack_blocks_per_cu(int32_t M) {
+int mfma_stack_blocks_per_cu(int32_t variant) {
   int n = 0;
-  hipError_t e = mfma_t(M) == 1
-                     ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mfma_stack_kernel<1>, kBlock, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mfma_stack_kernel<4>, kBlock, 0);
+  const hipError_t e = with_mfma_stack_kernel(variant, [&](auto kern) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kBlock, 0);
+  });
   if (e != hipSuccess || n < 1) n = 1;
   return n;
 }

@@ -145,27 +145,24 @@ __device__ __forceinline__ void valu_range_reg(const LinearArgs& a, int row_lo, 
   for (int unit = unit0;; unit += ustride) {
     const int base = row_lo + unit * UNIT;
     if (base >= row_hi) break;
+    // Unconditional loads from clamped (in-bounds) addresses: rows past
+    // row_hi repeat the last row and are never stored; chunks past the row
+    // meet zero activations.  No branch, so all loads issue back to back.
     u32x4 w[U][CPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int row = base + u * RPW + sub;
+      const int row = min(base + u * RPW + sub, row_hi - 1);
 #pragma unroll
       for (int t = 0; t < CPL; ++t) {
-        const int ch = r + LPR * t;
-        if (row < row_hi && ch < nch)
-          w[u][t] = load_weights16(a.packed + (int64_t)row * a.ld + 16 * ch);
-        else
-          w[u][t] = u32x4{0, 0, 0, 0};
+        const int ch = min(r + LPR * t, nch - 1);
+        w[u][t] = load_weights16(a.packed + (int64_t)row * a.ld + 16 * ch);
       }
     }
     const int my_row = base + my_u * RPW + sub;
     const bool do_store = writer && my_row < row_hi;
-    int32_t rs = 0;
-    float sr = 0.f;
-    if (do_store) {
-      rs = load_g(a.rowsum + my_row);
-      sr = load_g(a.s_row + my_row);
-    }
+    const int my_row_c = min(my_row, row_hi - 1);
+    const int32_t rs = load_g(a.rowsum + my_row_c);
+    const float sr = load_g(a.s_row + my_row_c);
     uint32_t part[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -223,12 +220,12 @@ __device__ __forceinline__ void valu_range_stream(const LinearArgs& a, int row_l
     for (int v = 0; v < NV; ++v) part[v] = 0;
     for (int c0 = 0; c0 < nch; c0 += 64) {
       const int ch = c0 + lane;
+      const int ch_c = min(ch, nch - 1);  // past the row: activations are zero
       u32x4 w[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int row = base + u;
-        w[u] = (row < row_hi && ch < nch) ? load_weights16(a.packed + (int64_t)row * a.ld + 16 * ch)
-                                          : u32x4{0, 0, 0, 0};
+        const int row = min(base + u, row_hi - 1);
+        w[u] = load_weights16(a.packed + (int64_t)row * a.ld + 16 * ch_c);
       }
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -276,24 +273,35 @@ __device__ __forceinline__ void run_reg(const LinearArgs& a, int lo, int hi, int
   valu_range_reg<C::LPR, C::CPL, C::U, RAGGED>(a, lo, hi, u0, us, lane);
 }
 
-// M = 1, one segment of a prepared stack: the register variants for K a
-// multiple of 64, the streaming variant for everything else.
+// M = 1, one segment of a prepared stack.  VSET is the set of variants the
+// kernel is compiled for (bit V for register variant V, bit VGEN for the
+// streaming one, which also takes K not a multiple of 64): each extra
+// variant in the switch can raise the register budget of the whole kernel,
+// so the host picks the smallest set that covers the stack.
+template <uint32_t VSET>
 __device__ __forceinline__ void valu_m1_segment(const LinearArgs& a, int lo, int hi, int lane) {
-  if ((a.K & 63) != 0) {
-    valu_range_stream<kStreamU, 1>(a, lo, hi, 0, 1, lane);
-    return;
+  if constexpr ((VSET >> VGEN) & 1u) {
+    if ((a.K & 63) != 0 || a.variant == VGEN) {
+      valu_range_stream<kStreamU, 1>(a, lo, hi, 0, 1, lane);
+      return;
+    }
   }
+#define TERN_SEG_CASE(V)                                  \
+  case V:                                                 \
+    if constexpr ((VSET >> V) & 1u) run_reg<V, false>(a, lo, hi, 0, 1, lane); \
+    break;
   switch (a.variant) {
-    case V8x1: run_reg<V8x1, false>(a, lo, hi, 0, 1, lane); break;
-    case V16x1: run_reg<V16x1, false>(a, lo, hi, 0, 1, lane); break;
-    case V32x1: run_reg<V32x1, false>(a, lo, hi, 0, 1, lane); break;
-    case V16x3: run_reg<V16x3, false>(a, lo, hi, 0, 1, lane); break;
-    case V64x1: run_reg<V64x1, false>(a, lo, hi, 0, 1, lane); break;
-    case V64x2: run_reg<V64x2, false>(a, lo, hi, 0, 1, lane); break;
-    case V64x3: run_reg<V64x3, false>(a, lo, hi, 0, 1, lane); break;
-    case V64x4: run_reg<V64x4, false>(a, lo, hi, 0, 1, lane); break;
-    default: valu_range_stream<kStreamU, 1>(a, lo, hi, 0, 1, lane); break;
+    TERN_SEG_CASE(V8x1)
+    TERN_SEG_CASE(V16x1)
+    TERN_SEG_CASE(V32x1)
+    TERN_SEG_CASE(V16x3)
+    TERN_SEG_CASE(V64x1)
+    TERN_SEG_CASE(V64x2)
+    TERN_SEG_CASE(V64x3)
+    TERN_SEG_CASE(V64x4)
+    default: break;
   }
+#undef TERN_SEG_CASE
 }
 
 constexpr int kBlock = 256;
@@ -328,7 +336,7 @@ __global__ __launch_bounds__(kBlock) void valu_stream_kernel(LinearArgs a) {
   valu_range_stream<(MT >= 8 ? 4 : kStreamU), MT>(a, 0, a.N, wave, nw, lane);
 }
 
-template <int MT>
+template <int MT, uint32_t VSET>
 __global__ __launch_bounds__(kBlock) void valu_stack_kernel(const StackHeader* __restrict__ h) {
   const int lane = threadIdx.x & 63;
   const int worker = xcd_logical_block() * kWavesPerBlock + wave_id_uniform();
@@ -344,7 +352,7 @@ __global__ __launch_bounds__(kBlock) void valu_stack_kernel(const StackHeader* _
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
     if constexpr (MT == 1)
-      valu_m1_segment(a, sg.row_begin, sg.row_end, lane);
+      valu_m1_segment<VSET>(a, sg.row_begin, sg.row_end, lane);
     else
       valu_range_stream<(MT >= 8 ? 4 : kStreamU), MT>(a, sg.row_begin, sg.row_end, 0, 1, lane);
   }
@@ -424,36 +432,55 @@ hipError_t launch_valu_linear(const LinearArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Variant sets the persistent M = 1 kernel is compiled for.
+constexpr uint32_t bit(int v) { return 1u << v; }
+constexpr uint32_t kSet8B = bit(V64x1) | bit(V64x3);
+constexpr uint32_t kSet06B = bit(V16x1) | bit(V32x1) | bit(V16x3);
+constexpr uint32_t kSetReg = bit(V8x1) | bit(V16x1) | bit(V32x1) | bit(V16x3) | bit(V64x1) |
+                             bit(V64x2) | bit(V64x3) | bit(V64x4);
+constexpr uint32_t kSetAll = kSetReg | bit(VGEN);
+constexpr uint32_t kSets[] = {kSet8B, kSet06B, kSetReg, kSetAll};
+constexpr uint32_t kNone = 0;
+
+int32_t valu_stack_kernel_for(int32_t M, uint32_t used_variants) {
+  if (M == 1) {
+    for (int i = 0; i < 4; ++i)
+      if ((used_variants & ~kSets[i]) == 0) return SK_VALU_M1 + i;
+    return SK_VALU_M1 + 3;
+  }
+  if (M == 2) return SK_VALU_M2;
+  if (M <= 4) return SK_VALU_M4;
+  return SK_VALU_M8;
+}
+
+template <typename F>
+static hipError_t with_valu_stack_kernel(int32_t kernel, F&& f) {
+  switch (kernel) {
+    case SK_VALU_M1 + 0: return f(valu_stack_kernel<1, kSets[0]>);
+    case SK_VALU_M1 + 1: return f(valu_stack_kernel<1, kSets[1]>);
+    case SK_VALU_M1 + 2: return f(valu_stack_kernel<1, kSets[2]>);
+    case SK_VALU_M1 + 3: return f(valu_stack_kernel<1, kSets[3]>);
+    case SK_VALU_M2: return f(valu_stack_kernel<2, kNone>);
+    case SK_VALU_M4: return f(valu_stack_kernel<4, kNone>);
+    case SK_VALU_M8: return f(valu_stack_kernel<8, kNone>);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_valu_stack(int32_t kernel, const void* ws, const LaunchShape& shp, hipStream_t s) {
   const StackHeader* h = static_cast<const StackHeader*>(ws);
   const dim3 grid(shp.grid), block(shp.block);
-  switch (kernel) {
-    case SK_VALU_M1: hipLaunchKernelGGL(valu_stack_kernel<1>, grid, block, 0, s, h); break;
-    case SK_VALU_M2: hipLaunchKernelGGL(valu_stack_kernel<2>, grid, block, 0, s, h); break;
-    case SK_VALU_M4: hipLaunchKernelGGL(valu_stack_kernel<4>, grid, block, 0, s, h); break;
-    case SK_VALU_M8: hipLaunchKernelGGL(valu_stack_kernel<8>, grid, block, 0, s, h); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return with_valu_stack_kernel(kernel, [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, h);
+    return hipGetLastError();
+  });
 }
 
 int valu_stack_blocks_per_cu(int32_t kernel) {
   int n = 0;
-  hipError_t e;
-  switch (kernel) {
-    case SK_VALU_M1:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_stack_kernel<1>, kBlock, 0);
-      break;
-    case SK_VALU_M2:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_stack_kernel<2>, kBlock, 0);
-      break;
-    case SK_VALU_M4:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_stack_kernel<4>, kBlock, 0);
-      break;
-    default:
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, valu_stack_kernel<8>, kBlock, 0);
-      break;
-  }
+  const hipError_t e = with_valu_stack_kernel(kernel, [&](auto kern) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kBlock, 0);
+  });
   if (e != hipSuccess || n < 1) n = 1;
   return n;
 }

@@ -125,6 +125,7 @@ class StackBinding:
                 self.host_act.append((q, s_act, z))
             descs.append(tern.make_desc(pl.packed, pl.s_row, pl.rowsum, pl.N, pl.K, qd, ldq, sd,
                                         zd, yd, pl.N, ad))
+        self.descs = descs
         L = len(descs)
         self.workspace = torch.empty(tern.tern_linear_stack_workspace_bytes(L, M),
                                      dtype=torch.uint8, device=dev)

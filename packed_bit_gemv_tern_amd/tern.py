@@ -29,7 +29,7 @@ TERN_VALU_MAX_M = 8
 EXPORTS = (
     "tern_row_bytes", "tern_pack", "tern_unpack", "tern_validate", "tern_gemv",
     "tern_gemm_smallM", "tern_linear_stack_workspace_bytes", "tern_linear_stack_prepare",
-    "tern_linear_stack", "tern_status_string", "tern_last_hip_error",
+    "tern_linear_stack", "tern_read_probe", "tern_status_string", "tern_last_hip_error",
 )
 
 
@@ -92,6 +92,7 @@ def _declare(lib):
         "tern_linear_stack_prepare": (i32, [ctypes.POINTER(tern_linear_desc), i64, i64, i32,
                                             vp, i64, ctypes.POINTER(tern_stack_plan), vp]),
         "tern_linear_stack": (i32, [ctypes.POINTER(tern_stack_plan), vp]),
+        "tern_read_probe": (i32, [vp, i64, vp, i32, i32, i32, vp]),
         "tern_status_string": (ctypes.c_char_p, [i32]),
         "tern_last_hip_error": (i32, []),
     }
@@ -189,3 +190,9 @@ def tern_linear_stack_prepare(descs, M, workspace, path=TERN_PATH_AUTO, stream=N
 
 def tern_linear_stack(plan, stream=None):
     _check(_lib().tern_linear_stack(ctypes.byref(plan), _stream(stream)), "tern_linear_stack")
+
+
+def tern_read_probe(buf, nbytes, sink, blocks_per_cu=4, unroll=8, nontemporal=True, stream=None):
+    _check(_lib().tern_read_probe(_ptr(buf), int(nbytes), _ptr(sink), int(blocks_per_cu),
+                                  int(unroll), int(bool(nontemporal)), _stream(stream)),
+           "tern_read_probe")

@@ -148,3 +148,13 @@ def test_stack_empty_plan(lib):
     assert lib.tern_linear_stack(ctypes.byref(plan), S) == tern.TERN_OK
     assert lib.tern_linear_stack_prepare(arr, 1, 0, 0, None, 0, ctypes.byref(plan), S) == tern.TERN_OK
     assert lib.tern_linear_stack(ctypes.byref(plan), S) == tern.TERN_OK
+
+
+def test_read_probe_argument_errors(lib):
+    sink = A16
+    assert lib.tern_read_probe(None, 1024, sink, 4, 8, 1, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_read_probe(A16, 1000, sink, 4, 8, 1, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_read_probe(A16, 1024, sink, 0, 8, 1, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_read_probe(A16, 1024, sink, 9, 8, 1, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_read_probe(A16, 1024, sink, 4, 5, 1, S) == tern.TERN_ERR_UNSUPPORTED
+    assert lib.tern_read_probe(ODD, 1024, sink, 4, 8, 1, S) == tern.TERN_ERR_ALIGNMENT
