@@ -66,7 +66,10 @@ def kernel_name(plan) -> str:
     if k in (4, 5, 6):
         return "valu_stack_kernel<%d, 0u>" % {4: 2, 5: 4, 6: 8}[k]
     v = k - 8
-    return "mfma_stack_kernel<%d, %s>" % (4 if v & 1 else 1, "true" if v & 2 else "false")
+    ragged = "true" if v & 2 else "false"
+    if v & 1:
+        return "mfma_stack_kernel<4, %s>" % ragged
+    return "mfma_wg_stack_kernel<%d, %s>" % (16 if v & 4 else 8, ragged)
 
 
 def read_probe(nbytes: int, reps: int = 5):

@@ -245,7 +245,10 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   per_cu = std::min(per_cu, kMaxWavesPerCu / kWavesPerBlock);
   int grid = cus * per_cu;
   grid = std::max(8, grid / 8 * 8);  // a multiple of 8 for the XCD-aware numbering
-  const int64_t workers = (int64_t)grid * kWavesPerBlock;
+  // schedule entries belong to waves, or to whole workgroups for the
+  // lockstep MFMA kernel
+  const bool per_wg = p == TERN_PATH_MFMA && mfma_per_workgroup(kernel - SK_MFMA);
+  const int64_t workers = (int64_t)grid * (per_wg ? 1 : kWavesPerBlock);
 
   // Granules: units of each linear's rows, cost = packed bytes + a fixed
   // per-unit overhead; contiguous granule runs balanced over the workers.
@@ -262,7 +265,7 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
                                d.y, d.ldy, d.acc);
     if (d.N == 0) continue;
     const int unit = p == TERN_PATH_VALU ? valu_unit_rows(lin[(size_t)i].variant, (int32_t)M)
-                                         : mfma_unit_rows((int32_t)M);
+                                         : mfma_unit_rows(kernel - SK_MFMA);
     const double ld = (double)row_bytes(d.K);
     for (int64_t r0 = 0; r0 < d.N; r0 += unit) {
       const int64_t r1 = std::min<int64_t>(d.N, r0 + unit);

@@ -86,7 +86,8 @@ hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s);
 
 // Rows handled per work unit (schedule granularity) of each path.
 int valu_unit_rows(int32_t variant, int32_t M);
-int mfma_unit_rows(int32_t M);
+int mfma_unit_rows(int32_t variant);
+bool mfma_per_workgroup(int32_t variant);
 int32_t valu_variant_for(int64_t K);
 
 // Persistent stack launches over a prepared workspace.

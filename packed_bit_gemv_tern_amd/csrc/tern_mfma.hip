@@ -198,6 +198,154 @@ __device__ __forceinline__ void mfma_range(const LinearArgs& a, int row_lo, int 
   }
 }
 
+// ---------------------------------------------------------------------------
+// M <= 16: the four waves of a workgroup take the four 64-row quarters of a
+// 256-row unit of one linear and walk K in lockstep.  Each K-step's
+// activations (MQ tokens x 512 bytes) are loaded once per workgroup with
+// whole-line loads -- wave w brings tokens 2*(QLD*w + i) and 2*(QLD*w + i) + 1
+// -- into a double-buffered LDS tile that every wave then reads its MFMA
+// operands from; weights keep the per-wave tile of mfma_range.  Reading the
+// activations straight from memory in MFMA layout touched 32 cache lines per
+// load instruction and stalled the address unit.  One barrier per K-step:
+// it publishes step ks+1's activations, and it also guarantees every wave
+// has finished with the buffer that step ks+2 will overwrite.
+constexpr int kQPitch = 528;  // 512 activation bytes of a step + 16 of padding
+constexpr int kWgRows = kWavesPerBlock * 16 * kR;
+
+template <int MQ>
+struct WgTiles {
+  uint8_t w[kWavesPerBlock][16 * kR * kRowPitch];
+  uint8_t q[2][MQ][kQPitch];
+  uint8_t zero[kQPitch];  // operand row of the MFMA token rows MQ..15
+};
+
+template <int MQ, bool RAGGED>
+__device__ __forceinline__ void mfma_wg_range(const LinearArgs& a, int row_lo, int row_hi, int unit0,
+                                              int ustride, int lane, int w, WgTiles<MQ>& L) {
+  constexpr int R = kR;
+  constexpr int NLD = 16 * R / 8;               // weight loads per wave per K-step
+  constexpr int QLD = MQ / (2 * kWavesPerBlock);  // activation loads per wave per K-step
+  static_assert(QLD >= 1, "MQ");
+  const int r = lane & 15, g = lane >> 4;
+  const int lrow = lane >> 3, lchunk = lane & 7;
+  const int nch = a.nch, K = a.K, M = a.M;
+  const int nks = (nch + 7) / 8;
+  uint8_t* tile = L.w[w];
+  const int qoff = 16 * (lane & 31);  // step byte this lane stages
+
+  auto load_q = [&](int ks, u32x4 (&qv)[QLD]) {
+#pragma unroll
+    for (int i = 0; i < QLD; ++i) {
+      const int tq = 2 * (QLD * w + i) + (lane >> 5);
+      const int ch = 8 * ks + qoff / 64;
+      const int8_t* qr = a.q + (int64_t)min(tq, M - 1) * a.ldq;
+      const int j0 = 64 * min(ch, nch - 1) + qoff % 64;
+      u32x4 v;
+      if (RAGGED && j0 + 16 > K) {
+        const i32x4 t = load_q16_tail(qr, K, j0);
+        v = u32x4{(uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w};
+      } else {
+        v = load16(qr + j0);
+      }
+      qv[i] = (tq < M && ch < nch) ? v : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_q = [&](int buf, const u32x4 (&qv)[QLD]) {
+#pragma unroll
+    for (int i = 0; i < QLD; ++i) {
+      const int tq = 2 * (QLD * w + i) + (lane >> 5);
+      *reinterpret_cast<u32x4*>(&L.q[buf][tq][qoff]) = qv[i];
+    }
+  };
+
+#pragma unroll 1
+  for (int unit = unit0;; unit += ustride) {
+    const int ubase = row_lo + unit * kWgRows;
+    if (ubase >= row_hi) break;  // the same for every wave of the workgroup
+    const int base = ubase + 16 * R * w;
+    const uint8_t* src[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i)
+      src[i] = a.packed + (int64_t)min(base + 8 * i + lrow, row_hi - 1) * a.ld;
+    i32x4 acc[R];
+#pragma unroll
+    for (int b = 0; b < R; ++b) acc[b] = i32x4{0, 0, 0, 0};
+
+    u32x4 st[NLD];
+    u32x4 qv[QLD];
+    {
+      const int ch = min(lchunk, nch - 1);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) st[i] = load_weights16(src[i] + 16 * ch);
+      load_q(0, qv);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        *reinterpret_cast<u32x4*>(tile + (8 * i + lrow) * kRowPitch + 16 * lchunk) = st[i];
+      store_q(0, qv);
+    }
+    __syncthreads();
+    for (int ks = 0; ks < nks; ++ks) {
+      const bool more = ks + 1 < nks;
+      if (more) {
+        const int ch = min(8 * (ks + 1) + lchunk, nch - 1);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) st[i] = load_weights16(src[i] + 16 * ch);
+        load_q(ks + 1, qv);
+      }
+      const uint8_t* qrow = r < MQ ? &L.q[ks & 1][r][0] : L.zero;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        i32x4 qa[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          qa[j] = as_i32x4(*reinterpret_cast<const u32x4*>(qrow + 128 * g + 64 * half + 16 * j));
+#pragma unroll
+        for (int b = 0; b < R; ++b) {
+          const u32x4 wv = *reinterpret_cast<const u32x4*>(
+              tile + (16 * b + r) * kRowPitch + 32 * g + 16 * half);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[j], decode_word(wv[j]), acc[b], 0, 0, 0);
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+          *reinterpret_cast<u32x4*>(tile + (8 * i + lrow) * kRowPitch + 16 * lchunk) = st[i];
+        store_q((ks + 1) & 1, qv);
+      }
+      __syncthreads();
+    }
+
+    // epilogue: lane holds tokens 4g + v of row base + 16b + r
+#pragma unroll
+    for (int b = 0; b < R; ++b) {
+      const int row = base + 16 * b + r;
+      if (row >= row_hi) continue;
+      const int32_t rs = load_g(a.rowsum + row);
+      const float sr = load_g(a.s_row + row);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * g + v;
+        if (m < M) {
+          const int32_t accv =
+              (int32_t)((uint32_t)acc[b][v] - (uint32_t)load_g(a.z + m) * (uint32_t)rs);
+          const int64_t o = (int64_t)m * a.ldy + row;
+          store_g(a.y + o, epilogue(sr, accv, load_g(a.s_act + m)));
+          if (a.acc) store_g(a.acc + o, accv);
+        }
+      }
+    }
+  }
+}
+
+template <int MQ>
+__device__ __forceinline__ void clear_zero_row(WgTiles<MQ>& L) {
+  for (int i = threadIdx.x; i < kQPitch / 4; i += blockDim.x)
+    reinterpret_cast<uint32_t*>(L.zero)[i] = 0;
+  __syncthreads();
+}
+
 __device__ __forceinline__ int wave_id_uniform() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
@@ -211,6 +359,7 @@ __device__ __forceinline__ int xcd_logical_block() {
 
 constexpr int kTileBytes = 16 * kR * kRowPitch;
 
+// M > 16: every wave on its own rows (per-wave schedule).
 template <int T, bool RAGGED>
 __global__ __launch_bounds__(kBlock) void mfma_linear_kernel(LinearArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t tiles[kWavesPerBlock][kTileBytes];
@@ -221,8 +370,6 @@ __global__ __launch_bounds__(kBlock) void mfma_linear_kernel(LinearArgs a) {
   mfma_range<kR, T, RAGGED>(a, 0, a.N, wave, nw, lane, tiles[w]);
 }
 
-// RAGGED: the stack holds a linear whose K is not a multiple of 64 (compiled
-// in only then; it costs registers).
 template <int T, bool RAGGED>
 __global__ __launch_bounds__(kBlock) void mfma_stack_kernel(const StackHeader* __restrict__ h) {
   __shared__ __attribute__((aligned(16))) uint8_t tiles[kWavesPerBlock][kTileBytes];
@@ -245,43 +392,77 @@ __global__ __launch_bounds__(kBlock) void mfma_stack_kernel(const StackHeader* _
   }
 }
 
-int mfma_unit_rows(int32_t /*M*/) { return 16 * kR; }
-
-static int mfma_t(int32_t M) { return M <= 16 ? 1 : 4; }
-
-hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
-  const int64_t units = (a.N + 16 * kR - 1) / (16 * kR);
-  int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks < 1) blocks = 1;
-  const dim3 grid((unsigned)blocks), block(kBlock);
-  const bool ragged = (a.K & 63) != 0;
-  if (mfma_t(a.M) == 1) {
-    if (ragged)
-      hipLaunchKernelGGL((mfma_linear_kernel<1, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((mfma_linear_kernel<1, false>), grid, block, 0, s, a);
-  } else {
-    if (ragged)
-      hipLaunchKernelGGL((mfma_linear_kernel<4, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((mfma_linear_kernel<4, false>), grid, block, 0, s, a);
-  }
-  return hipGetLastError();
+// M <= 16: workgroups of four lockstep waves (per-workgroup schedule).
+template <int MQ, bool RAGGED>
+__global__ __launch_bounds__(kBlock) void mfma_wg_linear_kernel(LinearArgs a) {
+  __shared__ __attribute__((aligned(16))) WgTiles<MQ> L;
+  clear_zero_row(L);
+  const int lane = threadIdx.x & 63;
+  mfma_wg_range<MQ, RAGGED>(a, 0, a.N, blockIdx.x, gridDim.x, lane, wave_id_uniform(), L);
 }
 
-// kernel selector of a prepared MFMA stack: bit 0 = T is 4, bit 1 = ragged K
-int32_t mfma_stack_variant(int32_t M, bool ragged) { return (mfma_t(M) == 4 ? 1 : 0) | (ragged ? 2 : 0); }
+template <int MQ, bool RAGGED>
+__global__ __launch_bounds__(kBlock) void mfma_wg_stack_kernel(const StackHeader* __restrict__ h) {
+  __shared__ __attribute__((aligned(16))) WgTiles<MQ> L;
+  const int worker = xcd_logical_block();
+  if (worker >= h->workers) return;  // the same for the whole workgroup
+  clear_zero_row(L);
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id_uniform();
+  const char* base = reinterpret_cast<const char*>(h);
+  const LinearArgs* lin = reinterpret_cast<const LinearArgs*>(base + h->off_lin);
+  const int32_t* seg_start = reinterpret_cast<const int32_t*>(base + h->off_seg_start);
+  const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
+  const int s1 = seg_start[worker + 1];
+  for (int s = seg_start[worker]; s < s1; ++s) {
+    const Segment sg = seg[s];
+    const LinearArgs a = lin[sg.lin];
+    if (RAGGED && (a.K & 63) != 0)
+      mfma_wg_range<MQ, RAGGED>(a, sg.row_begin, sg.row_end, 0, 1, lane, w, L);
+    else
+      mfma_wg_range<MQ, false>(a, sg.row_begin, sg.row_end, 0, 1, lane, w, L);
+  }
+}
+
+// Kernel selector of the MFMA path: bit 0 = M > 16 (per-wave kernel, T = 4),
+// bit 1 = ragged K compiled in, bit 2 = 9 <= M <= 16 (16 activation rows).
+int32_t mfma_stack_variant(int32_t M, bool ragged) {
+  return (M > 16 ? 1 : 0) | (ragged ? 2 : 0) | (M > 8 && M <= 16 ? 4 : 0);
+}
+
+bool mfma_per_workgroup(int32_t variant) { return (variant & 1) == 0; }
+
+int mfma_unit_rows(int32_t variant) { return mfma_per_workgroup(variant) ? kWgRows : 16 * kR; }
 
 template <typename F>
 static hipError_t with_mfma_stack_kernel(int32_t variant, F&& f) {
   switch (variant) {
-    case 0: return f(mfma_stack_kernel<1, false>);
-    case 1: return f(mfma_stack_kernel<4, false>);
-    case 2: return f(mfma_stack_kernel<1, true>);
-    case 3: return f(mfma_stack_kernel<4, true>);
+    case 0: return f(mfma_wg_stack_kernel<8, false>);
+    case 2: return f(mfma_wg_stack_kernel<8, true>);
+    case 4: return f(mfma_wg_stack_kernel<16, false>);
+    case 6: return f(mfma_wg_stack_kernel<16, true>);
+    case 1: case 5: return f(mfma_stack_kernel<4, false>);
+    case 3: case 7: return f(mfma_stack_kernel<4, true>);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
+  const int32_t v = mfma_stack_variant(a.M, (a.K & 63) != 0);
+  const int64_t units = (a.N + mfma_unit_rows(v) - 1) / mfma_unit_rows(v);
+  int64_t blocks = mfma_per_workgroup(v) ? units : (units + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks), block(kBlock);
+  switch (v) {
+    case 0: hipLaunchKernelGGL((mfma_wg_linear_kernel<8, false>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((mfma_wg_linear_kernel<8, true>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((mfma_wg_linear_kernel<16, false>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((mfma_wg_linear_kernel<16, true>), grid, block, 0, s, a); break;
+    case 1: case 5: hipLaunchKernelGGL((mfma_linear_kernel<4, false>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((mfma_linear_kernel<4, true>), grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape& shp, hipStream_t s) {
