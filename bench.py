@@ -66,6 +66,8 @@ def kernel_name(plan) -> str:
     if k in (4, 5, 6):
         return "valu_stack_kernel<%d, 0u>" % {4: 2, 5: 4, 6: 8}[k]
     v = k - 8
+    if v == 8:
+        return "mfma_win_stack_kernel"
     ragged = "true" if v & 2 else "false"
     if v & 1:
         return "mfma_stack_kernel<4, %s>" % ragged

@@ -346,6 +346,141 @@ __device__ __forceinline__ void clear_zero_row(WgTiles<MQ>& L) {
   __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// M <= 8, K a multiple of 64: the activation window.  A workgroup keeps the
+// activations of 8 tokens x 4096 K positions in LDS and restages them only
+// when its (linear, window) changes -- once per segment for K <= 4096 and
+// once per window per unit beyond -- so the K loop itself has no barrier and
+// no activation traffic.  Weights go from HBM straight into a per-wave LDS
+// tile (global_load_lds_dwordx4, 16 bytes per lane at tile + 1 KB*i +
+// 16*lane): load i brings rows 8i..8i+7 of the wave's 32 rows, lane l chunk
+// (l%8) ^ (row%8) of row 8i + l/8 of the K-step -- whole 128-byte lines per
+// instruction, and the XOR spreads the 16 lanes that later read one chunk of
+// 16 rows over the banks.  The next step's load is issued as soon as the
+// current tile has been read into registers.
+constexpr int kWinK = 4096;                   // activation window (K positions)
+constexpr int kWinPitch = kWinK + 16;
+constexpr int kWinTokens = 8;
+constexpr int kWinR = 2;                      // row blocks of 16 per wave
+constexpr int kWinRows = kWavesPerBlock * 16 * kWinR;
+
+struct WinTiles {
+  uint8_t w[kWavesPerBlock][16 * kWinR * kStepBytes];
+  uint8_t q[kWinTokens][kWinPitch];
+};
+
+// waits on the global loads (and LDS DMA) of this wave, or on its LDS reads
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, int row_hi, int unit0,
+                                               int ustride, int lane, int w, WinTiles& L,
+                                               const int8_t*& staged_q, int& staged_k) {
+  constexpr int R = kWinR;
+  constexpr int NLD = 16 * R / 8;  // 1 KB wave loads per K-step
+  const int r = lane & 15, g = lane >> 4;
+  const int lrow = lane >> 3, lpos = lane & 7;
+  const int nch = a.nch, K = a.K, M = a.M;
+  const int nks = (nch + 7) / 8;
+  const int nwin = (K + kWinK - 1) / kWinK;
+  uint8_t* tile = L.w[w];
+
+#pragma unroll 1
+  for (int unit = unit0;; unit += ustride) {
+    const int ubase = row_lo + unit * kWinRows;
+    if (ubase >= row_hi) break;  // the same for every wave of the workgroup
+    const int base = ubase + 16 * R * w;
+    const uint8_t* src[NLD];
+    int sw[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int row = 8 * i + lrow;  // row of the wave's tile
+      src[i] = a.packed + (int64_t)min(base + row, row_hi - 1) * a.ld;
+      sw[i] = lpos ^ (row & 7);      // chunk this lane brings
+    }
+    auto issue = [&](int ks) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int ch = min(8 * ks + sw[i], nch - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(src[i] + 16 * ch),
+                                         (lds_ptr)(tile + 1024 * i), 16, 0, 2 /* nt */);
+      }
+    };
+    i32x4 acc[R];
+#pragma unroll
+    for (int b = 0; b < R; ++b) acc[b] = i32x4{0, 0, 0, 0};
+    issue(0);
+    for (int ks = 0; ks < nks; ++ks) {
+      if ((ks & 7) == 0) {
+        const int win = ks >> 3;
+        // a single-window linear whose activations are already staged (same
+        // q buffer and K, e.g. the previous unit) skips the restaging
+        if (nwin > 1 || staged_q != a.q || staged_k != K) {
+          // every wave is done with the previous window before it is replaced
+          __syncthreads();
+          for (int e = threadIdx.x; e < kWinTokens * (kWinK / 16); e += blockDim.x) {
+            const int tq = e / (kWinK / 16), off = 16 * (e % (kWinK / 16));
+            const int pos = win * kWinK + off;  // K position
+            u32x4 v = u32x4{0, 0, 0, 0};
+            if (tq < M && pos < K) v = load16(a.q + (int64_t)tq * a.ldq + pos);
+            *reinterpret_cast<u32x4*>(&L.q[tq][off]) = v;
+          }
+          __syncthreads();
+          staged_q = nwin > 1 ? nullptr : a.q;
+          staged_k = K;
+        }
+      }
+      wait_vm();  // this step's weight tile has landed
+      u32x4 wv[R][2];
+#pragma unroll
+      for (int b = 0; b < R; ++b)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          wv[b][half] = *reinterpret_cast<const u32x4*>(
+              tile + (16 * b + r) * kStepBytes + 16 * ((2 * g + half) ^ (r & 7)));
+      const uint8_t* qrow = &L.q[r & 7][64 * (8 * (ks & 7) + 2 * g)];
+      u32x4 qv[2][4];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          qv[half][j] = *reinterpret_cast<const u32x4*>(qrow + 64 * half + 16 * j);
+      wait_lgkm();  // tile read: it may be overwritten
+      if (ks + 1 < nks) issue(ks + 1);
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int b = 0; b < R; ++b)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[half][j]),
+                                                           decode_word(wv[b][half][j]), acc[b], 0, 0, 0);
+    }
+
+    // epilogue: lane holds tokens 4g + v of row base + 16b + r
+#pragma unroll
+    for (int b = 0; b < R; ++b) {
+      const int row = base + 16 * b + r;
+      if (row >= row_hi) continue;
+      const int32_t rs = load_g(a.rowsum + row);
+      const float sr = load_g(a.s_row + row);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * g + v;
+        if (m < M) {
+          const int32_t accv =
+              (int32_t)((uint32_t)acc[b][v] - (uint32_t)load_g(a.z + m) * (uint32_t)rs);
+          const int64_t o = (int64_t)m * a.ldy + row;
+          store_g(a.y + o, epilogue(sr, accv, load_g(a.s_act + m)));
+          if (a.acc) store_g(a.acc + o, accv);
+        }
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ int wave_id_uniform() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
@@ -424,15 +559,51 @@ __global__ __launch_bounds__(kBlock) void mfma_wg_stack_kernel(const StackHeader
   }
 }
 
+// M <= 8, every K a multiple of 64: the activation-window kernel.
+__global__ __launch_bounds__(kBlock) void mfma_win_linear_kernel(LinearArgs a) {
+  __shared__ __attribute__((aligned(16))) WinTiles L;
+  const int8_t* staged_q = nullptr;
+  int staged_k = 0;
+  mfma_win_range(a, 0, a.N, blockIdx.x, gridDim.x, threadIdx.x & 63, wave_id_uniform(), L, staged_q,
+                 staged_k);
+}
+
+__global__ __launch_bounds__(kBlock) void mfma_win_stack_kernel(const StackHeader* __restrict__ h) {
+  __shared__ __attribute__((aligned(16))) WinTiles L;
+  const int worker = xcd_logical_block();
+  if (worker >= h->workers) return;  // the same for the whole workgroup
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id_uniform();
+  const char* base = reinterpret_cast<const char*>(h);
+  const LinearArgs* lin = reinterpret_cast<const LinearArgs*>(base + h->off_lin);
+  const int32_t* seg_start = reinterpret_cast<const int32_t*>(base + h->off_seg_start);
+  const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
+  const int s1 = seg_start[worker + 1];
+  const int8_t* staged_q = nullptr;
+  int staged_k = 0;
+  for (int s = seg_start[worker]; s < s1; ++s) {
+    const Segment sg = seg[s];
+    const LinearArgs a = lin[sg.lin];
+    mfma_win_range(a, sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged_q, staged_k);
+  }
+}
+
 // Kernel selector of the MFMA path: bit 0 = M > 16 (per-wave kernel, T = 4),
-// bit 1 = ragged K compiled in, bit 2 = 9 <= M <= 16 (16 activation rows).
+// bit 1 = ragged K compiled in, bit 2 = 9 <= M <= 16 (16 activation rows);
+// 8 = the activation-window kernel (M <= 8, no ragged K).
+constexpr int32_t kWinVariant = 8;
+
 int32_t mfma_stack_variant(int32_t M, bool ragged) {
+  if (M <= kWinTokens && !ragged) return kWinVariant;
   return (M > 16 ? 1 : 0) | (ragged ? 2 : 0) | (M > 8 && M <= 16 ? 4 : 0);
 }
 
 bool mfma_per_workgroup(int32_t variant) { return (variant & 1) == 0; }
 
-int mfma_unit_rows(int32_t variant) { return mfma_per_workgroup(variant) ? kWgRows : 16 * kR; }
+int mfma_unit_rows(int32_t variant) {
+  if (variant == kWinVariant) return kWinRows;
+  return mfma_per_workgroup(variant) ? kWgRows : 16 * kR;
+}
 
 template <typename F>
 static hipError_t with_mfma_stack_kernel(int32_t variant, F&& f) {
@@ -443,6 +614,7 @@ static hipError_t with_mfma_stack_kernel(int32_t variant, F&& f) {
     case 6: return f(mfma_wg_stack_kernel<16, true>);
     case 1: case 5: return f(mfma_stack_kernel<4, false>);
     case 3: case 7: return f(mfma_stack_kernel<4, true>);
+    case kWinVariant: return f(mfma_win_stack_kernel);
     default: return hipErrorInvalidValue;
   }
 }
@@ -455,6 +627,7 @@ hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
   if (blocks < 1) blocks = 1;
   const dim3 grid((unsigned)blocks), block(kBlock);
   switch (v) {
+    case kWinVariant: hipLaunchKernelGGL(mfma_win_linear_kernel, grid, block, 0, s, a); break;
     case 0: hipLaunchKernelGGL((mfma_wg_linear_kernel<8, false>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((mfma_wg_linear_kernel<8, true>), grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL((mfma_wg_linear_kernel<16, false>), grid, block, 0, s, a); break;
