@@ -358,19 +358,38 @@ __device__ __forceinline__ void clear_zero_row(WgTiles<MQ>& L) {
 // instruction, and the XOR spreads the 16 lanes that later read one chunk of
 // 16 rows over the banks.  The next step's load is issued as soon as the
 // current tile has been read into registers.
-constexpr int kWinK = 4096;                   // activation window (K positions)
+// Decode by code planes: word & (0x03030303 << 2k) holds the codes c = w + 1
+// of weights 4k..4k+3 of the word scaled by 4^k (the top plane is shifted
+// down instead), so plane k of four words is one MFMA operand for four ANDs.
+// MFMA k of a chunk pairs plane k of its four words with the activations at
+// 16j + 4k + {0..3}, j = 0..3 -- 16 contiguous bytes once every 64-byte
+// chunk of the staged window is stored as a transposed 4x4 block of dwords.
+// Planes 0 and 3 accumulate into one register set, planes 1 and 2 into two
+// more; sum(c*q) = acc1 + acc4/4 + acc16/16 exactly, and sum(w*q) =
+// sum(c*q) - sum(q).
+constexpr int kWinK = 4096;    // activation window (K positions)
 constexpr int kWinPitch = kWinK + 16;
 constexpr int kWinTokens = 8;
-constexpr int kWinR = 2;                      // row blocks of 16 per wave
-constexpr int kWinRows = kWavesPerBlock * 16 * kWinR;
+constexpr int kWinR = 2;       // row blocks of 16 per wave
+constexpr int kWinDepth = 1;   // weight tiles per wave (K-steps loaded ahead)
+constexpr int kWinWaves = 8;   // waves per workgroup
+constexpr int kWinBlock = 64 * kWinWaves;
+constexpr int kWinRows = kWinWaves * 16 * kWinR;
+constexpr int kWinTile = 16 * kWinR * kStepBytes;
 
 struct WinTiles {
-  uint8_t w[kWavesPerBlock][16 * kWinR * kStepBytes];
-  uint8_t q[kWinTokens][kWinPitch];
+  uint8_t w[kWinWaves][kWinDepth][kWinTile];
+  uint8_t q[kWinTokens][kWinPitch];  // each 64-byte chunk stored dword-transposed
+  int32_t qsum[kWinTokens];          // sum of the token's activations over all of K
 };
 
-// waits on the global loads (and LDS DMA) of this wave, or on its LDS reads
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt on this wave's global loads (LDS DMA included): at most N still
+// outstanding; or on its LDS reads (lgkmcnt 0)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -385,8 +404,6 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   const int nch = a.nch, K = a.K, M = a.M;
   const int nks = (nch + 7) / 8;
   const int nwin = (K + kWinK - 1) / kWinK;
-  uint8_t* tile = L.w[w];
-
 #pragma unroll 1
   for (int unit = unit0;; unit += ustride) {
     const int ubase = row_lo + unit * kWinRows;
@@ -401,6 +418,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
       sw[i] = lpos ^ (row & 7);      // chunk this lane brings
     }
     auto issue = [&](int ks) {
+      uint8_t* tile = L.w[w][ks % kWinDepth];
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const int ch = min(8 * ks + sw[i], nch - 1);
@@ -408,11 +426,14 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
                                          (lds_ptr)(tile + 1024 * i), 16, 0, 2 /* nt */);
       }
     };
-    i32x4 acc[R];
+    i32x4 acc1[R], acc4[R], acc16[R];
 #pragma unroll
-    for (int b = 0; b < R; ++b) acc[b] = i32x4{0, 0, 0, 0};
-    issue(0);
+    for (int b = 0; b < R; ++b) acc1[b] = acc4[b] = acc16[b] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int d = 0; d < kWinDepth; ++d)
+      if (d < nks) issue(d);
     for (int ks = 0; ks < nks; ++ks) {
+      const uint8_t* tile = L.w[w][ks % kWinDepth];
       if ((ks & 7) == 0) {
         const int win = ks >> 3;
         // a single-window linear whose activations are already staged (same
@@ -425,14 +446,34 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
             const int pos = win * kWinK + off;  // K position
             u32x4 v = u32x4{0, 0, 0, 0};
             if (tq < M && pos < K) v = load16(a.q + (int64_t)tq * a.ldq + pos);
-            *reinterpret_cast<u32x4*>(&L.q[tq][off]) = v;
+            // word j = (off % 64) / 16 of its chunk: dword k goes to 16k + 4j
+            uint32_t* dst = reinterpret_cast<uint32_t*>(&L.q[tq][off & ~63]) + ((off % 64) / 16);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dst[4 * k] = v[k];
+          }
+          __syncthreads();
+          // per-token activation sums of this window; wave w owns tokens
+          // w, w + kWinWaves, ... so no two waves write one entry
+          for (int tq = w; tq < kWinTokens; tq += kWinWaves) {
+            uint32_t part = 0;
+            for (int off = 16 * lane; off < kWinK; off += 16 * 64) {
+              const u32x4 v = *reinterpret_cast<const u32x4*>(&L.q[tq][off]);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) part = (uint32_t)__builtin_amdgcn_sdot4((int)v[k], 0x01010101, (int)part, false);
+            }
+            const int32_t tot = (int32_t)group_sum<64>(part);
+            if (lane == 0) L.qsum[tq] = (win == 0 ? 0 : L.qsum[tq]) + tot;
           }
           __syncthreads();
           staged_q = nwin > 1 ? nullptr : a.q;
           staged_k = K;
         }
       }
-      wait_vm();  // this step's weight tile has landed
+      // this step's weight tile has landed (later steps' loads may still fly)
+      if (kWinDepth > 1 && ks + 1 < nks)
+        wait_vm<(kWinDepth > 1 ? NLD : 0)>();
+      else
+        wait_vm<0>();
       u32x4 wv[R][2];
 #pragma unroll
       for (int b = 0; b < R; ++b)
@@ -448,15 +489,19 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
         for (int j = 0; j < 4; ++j)
           qv[half][j] = *reinterpret_cast<const u32x4*>(qrow + 64 * half + 16 * j);
       wait_lgkm();  // tile read: it may be overwritten
-      if (ks + 1 < nks) issue(ks + 1);
+      if (ks + kWinDepth < nks) issue(ks + kWinDepth);
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
-        for (int b = 0; b < R; ++b)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[half][j]),
-                                                           decode_word(wv[b][half][j]), acc[b], 0, 0, 0);
+        for (int b = 0; b < R; ++b) {
+          const u32x4 x = wv[b][half];
+          const i32x4 p0 = as_i32x4(x & 0x03030303u), p1 = as_i32x4(x & 0x0C0C0C0Cu);
+          const i32x4 p2 = as_i32x4(x & 0x30303030u), p3 = as_i32x4((x >> 6) & 0x03030303u);
+          acc1[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[half][0]), p0, acc1[b], 0, 0, 0);
+          acc4[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[half][1]), p1, acc4[b], 0, 0, 0);
+          acc16[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[half][2]), p2, acc16[b], 0, 0, 0);
+          acc1[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[half][3]), p3, acc1[b], 0, 0, 0);
+        }
     }
 
     // epilogue: lane holds tokens 4g + v of row base + 16b + r
@@ -470,8 +515,9 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * g + v;
         if (m < M) {
-          const int32_t accv =
-              (int32_t)((uint32_t)acc[b][v] - (uint32_t)load_g(a.z + m) * (uint32_t)rs);
+          const int32_t cq = acc1[b][v] + (acc4[b][v] >> 2) + (acc16[b][v] >> 4);  // sum(c*q)
+          const int32_t accv = (int32_t)((uint32_t)cq - (uint32_t)L.qsum[m] -
+                                         (uint32_t)load_g(a.z + m) * (uint32_t)rs);
           const int64_t o = (int64_t)m * a.ldy + row;
           store_g(a.y + o, epilogue(sr, accv, load_g(a.s_act + m)));
           if (a.acc) store_g(a.acc + o, accv);
@@ -560,7 +606,7 @@ __global__ __launch_bounds__(kBlock) void mfma_wg_stack_kernel(const StackHeader
 }
 
 // M <= 8, every K a multiple of 64: the activation-window kernel.
-__global__ __launch_bounds__(kBlock) void mfma_win_linear_kernel(LinearArgs a) {
+__global__ __launch_bounds__(kWinBlock) void mfma_win_linear_kernel(LinearArgs a) {
   __shared__ __attribute__((aligned(16))) WinTiles L;
   const int8_t* staged_q = nullptr;
   int staged_k = 0;
@@ -568,7 +614,7 @@ __global__ __launch_bounds__(kBlock) void mfma_win_linear_kernel(LinearArgs a) {
                  staged_k);
 }
 
-__global__ __launch_bounds__(kBlock) void mfma_win_stack_kernel(const StackHeader* __restrict__ h) {
+__global__ __launch_bounds__(kWinBlock) void mfma_win_stack_kernel(const StackHeader* __restrict__ h) {
   __shared__ __attribute__((aligned(16))) WinTiles L;
   const int worker = xcd_logical_block();
   if (worker >= h->workers) return;  // the same for the whole workgroup
@@ -627,7 +673,7 @@ hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
   if (blocks < 1) blocks = 1;
   const dim3 grid((unsigned)blocks), block(kBlock);
   switch (v) {
-    case kWinVariant: hipLaunchKernelGGL(mfma_win_linear_kernel, grid, block, 0, s, a); break;
+    case kWinVariant: hipLaunchKernelGGL(mfma_win_linear_kernel, grid, dim3(kWinBlock), 0, s, a); break;
     case 0: hipLaunchKernelGGL((mfma_wg_linear_kernel<8, false>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((mfma_wg_linear_kernel<8, true>), grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL((mfma_wg_linear_kernel<16, false>), grid, block, 0, s, a); break;
@@ -640,7 +686,7 @@ hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
 
 hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape& shp, hipStream_t s) {
   const StackHeader* h = static_cast<const StackHeader*>(ws);
-  const dim3 grid(shp.grid), block(shp.block);
+  const dim3 grid(shp.grid), block(variant == kWinVariant ? kWinBlock : shp.block);
   return with_mfma_stack_kernel(variant, [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, s, h);
     return hipGetLastError();
@@ -649,8 +695,9 @@ hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape&
 
 int mfma_stack_blocks_per_cu(int32_t variant) {
   int n = 0;
+  const int block = variant == kWinVariant ? kWinBlock : kBlock;
   const hipError_t e = with_mfma_stack_kernel(variant, [&](auto kern) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kBlock, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, block, 0);
   });
   if (e != hipSuccess || n < 1) n = 1;
   return n;
