@@ -229,15 +229,17 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   if (!aligned(workspace, 256)) return TERN_ERR_WORKSPACE;
 
   uint32_t used = 0;
+  bool big = false;
   for (int64_t i = 0; i < L; ++i) {
     if (descs[i].N == 0) continue;
     const int32_t v = descs[i].K % 64 ? (int32_t)VGEN : valu_variant_for(descs[i].K);
     used |= 1u << v;
+    big = big || descs[i].N * row_bytes(descs[i].K) >= (1ll << 32);
   }
   const bool ragged = (used >> VGEN) & 1u;
   const int32_t kernel = p == TERN_PATH_VALU
                              ? valu_stack_kernel_for((int32_t)M, used)
-                             : (int32_t)SK_MFMA + mfma_stack_variant((int32_t)M, ragged);
+                             : (int32_t)SK_MFMA + mfma_stack_variant((int32_t)M, ragged, big);
   const int cus = device_cus();
   if (cus <= 0) return hip_fail(hipErrorNoDevice);
   int per_cu = p == TERN_PATH_VALU ? valu_stack_blocks_per_cu(kernel)
@@ -274,26 +276,65 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
       total += c;
     }
   }
+  // Contiguous runs of granules, the largest run as small as it can be: the
+  // smallest cap C for which runs of total cost <= C need at most `workers`
+  // runs (bisection on C, each probe a greedy fill over the prefix sums).
+  // When fewer runs suffice, the idle workers are spread evenly over the
+  // worker numbering (and so over the XCDs).
+  const size_t G = gran.size();
+  std::vector<double> pre(G + 1, 0.0);
+  double gmax = 0.0;
+  for (size_t i = 0; i < G; ++i) {
+    pre[i + 1] = pre[i] + gran[i].cost;
+    gmax = std::max(gmax, gran[i].cost);
+  }
+  auto runs_for = [&](double cap, std::vector<size_t>* ends) {
+    int64_t n = 0;
+    size_t i = 0;
+    while (i < G) {
+      // last j with pre[j] - pre[i] <= cap; at least one granule per run
+      size_t j = (size_t)(std::upper_bound(pre.begin() + (ptrdiff_t)i + 1, pre.end(), pre[i] + cap) -
+                          pre.begin()) - 1;
+      if (j <= i) j = i + 1;
+      if (ends) ends->push_back(j);
+      ++n;
+      i = j;
+    }
+    return n;
+  };
+  double lo = std::max(total / (double)workers, gmax), hi = lo + gmax;
+  if (runs_for(lo, nullptr) <= workers) hi = lo;
+  for (int it = 0; it < 60 && hi - lo > 1e-6 * hi; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (runs_for(mid, nullptr) <= workers)
+      hi = mid;
+    else
+      lo = mid;
+  }
+  std::vector<size_t> ends;
+  ends.reserve((size_t)workers);
+  const int64_t nruns = runs_for(hi, &ends);
   std::vector<int32_t> seg_start((size_t)workers + 1, 0);
   std::vector<Segment> segs;
-  segs.reserve(gran.size() / 4 + (size_t)workers + (size_t)L);
-  double cum = 0.0;
-  int64_t cur_w = -1;
-  for (const Gran& g : gran) {
-    int64_t w = (int64_t)((cum + 0.5 * g.cost) / total * (double)workers);
-    if (w >= workers) w = workers - 1;
-    cum += g.cost;
-    if (!segs.empty() && w == cur_w && segs.back().lin == g.lin && segs.back().row_end == g.r0) {
-      segs.back().row_end = g.r1;
-      continue;
+  segs.reserve(G / 4 + (size_t)workers + (size_t)L);
+  size_t gi = 0;
+  int64_t wk = 0;
+  for (int64_t k = 0; k < nruns; ++k) {
+    // run k goes to worker floor(k * workers / nruns); the workers skipped
+    // over get empty ranges
+    const int64_t target = k * workers / nruns;
+    while (wk <= target) seg_start[(size_t)wk++] = (int32_t)segs.size();
+    for (; gi < ends[(size_t)k]; ++gi) {
+      const Gran& g = gran[gi];
+      if (gi > 0 && gi != (k == 0 ? 0 : ends[(size_t)k - 1]) && segs.back().lin == g.lin &&
+          segs.back().row_end == g.r0) {
+        segs.back().row_end = g.r1;
+        continue;
+      }
+      segs.push_back({g.lin, g.r0, g.r1, 0});
     }
-    while (cur_w < w) seg_start[(size_t)(++cur_w)] = (int32_t)segs.size();
-    segs.push_back({g.lin, g.r0, g.r1, 0});
   }
-  while (cur_w < workers) seg_start[(size_t)(++cur_w)] = (int32_t)segs.size();
-  // the loop above sets seg_start[w] for w <= cur_w as "first segment of w";
-  // worker w owns [seg_start[w], seg_start[w + 1]); the final entry is nseg
-  seg_start[(size_t)workers] = (int32_t)segs.size();
+  while (wk <= workers) seg_start[(size_t)wk++] = (int32_t)segs.size();
 
   const Layout lay = layout_for(L, workers, (int64_t)segs.size());
   if (workspace_bytes < lay.total) return TERN_ERR_WORKSPACE;

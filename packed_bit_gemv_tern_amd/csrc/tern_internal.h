@@ -95,7 +95,8 @@ int32_t valu_stack_kernel_for(int32_t M, uint32_t used_variants);
 hipError_t launch_valu_stack(int32_t kernel, const void* ws, const LaunchShape& shp,
                              hipStream_t s);
 int valu_stack_blocks_per_cu(int32_t kernel);
-int32_t mfma_stack_variant(int32_t M, bool ragged);
+// big: some linear has N * row_bytes >= 2^32
+int32_t mfma_stack_variant(int32_t M, bool ragged, bool big);
 hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape& shp,
                              hipStream_t s);
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int grid, int unroll,

@@ -381,6 +381,8 @@ struct WinTiles {
   uint8_t w[kWinWaves][kWinDepth][kWinTile];
   uint8_t q[kWinTokens][kWinPitch];  // each 64-byte chunk stored dword-transposed
   int32_t qsum[kWinTokens];          // sum of the token's activations over all of K
+  int32_t z[kWinTokens];             // zero points and scales of the staged tokens
+  float s_act[kWinTokens];
 };
 
 // s_waitcnt on this wave's global loads (LDS DMA included): at most N still
@@ -392,11 +394,38 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// A register copy the compiler cannot look through.  Placed right after an
+// explicit wait for all of the wave's loads, it hands on a loaded value as
+// one the compiler knows is present: otherwise a value loaded inside the
+// K-step loop and used after it makes the compiler wait for every load and
+// store in flight (the next unit's tile, earlier outputs) at each use.
+__device__ __forceinline__ int32_t settled(int32_t x) {
+  int32_t y;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+  return y;
+}
+__device__ __forceinline__ float settled(float x) {
+  return __int_as_float(settled(__float_as_int(x)));
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// What the workgroup's window holds: the activations, zero points and scales
+// of one single-window linear, reused by the next segment when that reads the
+// same buffers (q == nullptr: nothing reusable is staged).
+struct WinStaged {
+  const int8_t* q = nullptr;
+  const int32_t* z = nullptr;
+  const float* s_act = nullptr;
+  int K = 0, ldq = 0;
+  __device__ bool holds(const LinearArgs& a) const {
+    return q && q == a.q && z == a.z && s_act == a.s_act && K == a.K && ldq == a.ldq;
+  }
+};
 
 __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, int row_hi, int unit0,
                                                int ustride, int lane, int w, WinTiles& L,
-                                               const int8_t*& staged_q, int& staged_k) {
+                                               WinStaged& staged) {
   constexpr int R = kWinR;
   constexpr int NLD = 16 * R / 8;  // 1 KB wave loads per K-step
   const int r = lane & 15, g = lane >> 4;
@@ -404,41 +433,65 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   const int nch = a.nch, K = a.K, M = a.M;
   const int nks = (nch + 7) / 8;
   const int nwin = (K + kWinK - 1) / kWinK;
+  // byte offsets (below 2^32: checked by the host) of the wave's weight rows
+  // within a unit, and the chunk each lane brings
+  auto unit_src = [&](int unit, uint32_t (&src)[NLD]) {
+    const int base = row_lo + unit * kWinRows + 16 * R * w;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) src[i] = (uint32_t)min(base + 8 * i + lrow, row_hi - 1) * (uint32_t)a.ld;
+  };
+  auto issue = [&](const uint32_t (&src)[NLD], int ks) {
+    uint8_t* tile = L.w[w][ks % kWinDepth];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int ch = min(8 * ks + (lpos ^ ((8 * i + lrow) & 7)), nch - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(a.packed + src[i] + 16 * ch),
+                                       (lds_ptr)(tile + 1024 * i), 16, 0, 2 /* nt */);
+    }
+  };
+  // rowsum and s_row of a unit's rows, loaded one unit ahead
+  auto load_rowops = [&](int unit, int32_t (&rs)[R], float (&sr)[R]) {
+    const int base = row_lo + unit * kWinRows + 16 * R * w;
+#pragma unroll
+    for (int b = 0; b < R; ++b) {
+      const int row = min(base + 16 * b + r, row_hi - 1);
+      rs[b] = load_g(a.rowsum + row);
+      sr[b] = load_g(a.s_row + row);
+    }
+  };
+  uint32_t src[NLD];
+  int32_t nrs[R];
+  float nsr[R];
+#pragma unroll
+  for (int b = 0; b < R; ++b) nrs[b] = 0, nsr[b] = 0.0f;
+  if (row_lo + unit0 * kWinRows < row_hi) {
+    unit_src(unit0, src);
+#pragma unroll
+    for (int d = 0; d < kWinDepth; ++d)
+      if (d < nks) issue(src, d);
+    load_rowops(unit0, nrs, nsr);
+  }
+
 #pragma unroll 1
   for (int unit = unit0;; unit += ustride) {
     const int ubase = row_lo + unit * kWinRows;
     if (ubase >= row_hi) break;  // the same for every wave of the workgroup
     const int base = ubase + 16 * R * w;
-    const uint8_t* src[NLD];
-    int sw[NLD];
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int row = 8 * i + lrow;  // row of the wave's tile
-      src[i] = a.packed + (int64_t)min(base + row, row_hi - 1) * a.ld;
-      sw[i] = lpos ^ (row & 7);      // chunk this lane brings
-    }
-    auto issue = [&](int ks) {
-      uint8_t* tile = L.w[w][ks % kWinDepth];
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int ch = min(8 * ks + sw[i], nch - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(src[i] + 16 * ch),
-                                         (lds_ptr)(tile + 1024 * i), 16, 0, 2 /* nt */);
-      }
-    };
+    const bool has_next = ubase + ustride * kWinRows < row_hi;
+    uint32_t nsrc[NLD];
+    if (has_next) unit_src(unit + ustride, nsrc);
+    int32_t rs[R];
+    float sr[R];
     i32x4 acc1[R], acc4[R], acc16[R];
 #pragma unroll
     for (int b = 0; b < R; ++b) acc1[b] = acc4[b] = acc16[b] = i32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int d = 0; d < kWinDepth; ++d)
-      if (d < nks) issue(d);
     for (int ks = 0; ks < nks; ++ks) {
       const uint8_t* tile = L.w[w][ks % kWinDepth];
       if ((ks & 7) == 0) {
         const int win = ks >> 3;
-        // a single-window linear whose activations are already staged (same
-        // q buffer and K, e.g. the previous unit) skips the restaging
-        if (nwin > 1 || staged_q != a.q || staged_k != K) {
+        // a single-window linear whose activations are already staged (the
+        // same buffers, e.g. the previous unit) skips the restaging
+        if (nwin > 1 || !staged.holds(a)) {
           // every wave is done with the previous window before it is replaced
           __syncthreads();
           for (int e = threadIdx.x; e < kWinTokens * (kWinK / 16); e += blockDim.x) {
@@ -464,9 +517,17 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
             const int32_t tot = (int32_t)group_sum<64>(part);
             if (lane == 0) L.qsum[tq] = (win == 0 ? 0 : L.qsum[tq]) + tot;
           }
+          if (win == 0 && threadIdx.x < kWinTokens) {
+            const int tq = threadIdx.x;
+            L.z[tq] = tq < M ? load_g(a.z + tq) : 0;
+            L.s_act[tq] = tq < M ? load_g(a.s_act + tq) : 0.0f;
+          }
           __syncthreads();
-          staged_q = nwin > 1 ? nullptr : a.q;
-          staged_k = K;
+          staged.q = nwin > 1 ? nullptr : a.q;
+          staged.z = a.z;
+          staged.s_act = a.s_act;
+          staged.K = K;
+          staged.ldq = a.ldq;
         }
       }
       // this step's weight tile has landed (later steps' loads may still fly)
@@ -474,6 +535,14 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
         wait_vm<(kWinDepth > 1 ? NLD : 0)>();
       else
         wait_vm<0>();
+      if (ks == 0) {
+        // this unit's row operands arrived with (or before) its first tile
+        // (the wait above covers them); the next unit's are loaded now, a
+        // whole unit ahead of their use
+#pragma unroll
+        for (int b = 0; b < R; ++b) rs[b] = settled(nrs[b]), sr[b] = settled(nsr[b]);
+        if (has_next) load_rowops(unit + ustride, nrs, nsr);
+      }
       u32x4 wv[R][2];
 #pragma unroll
       for (int b = 0; b < R; ++b)
@@ -481,49 +550,56 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
         for (int half = 0; half < 2; ++half)
           wv[b][half] = *reinterpret_cast<const u32x4*>(
               tile + (16 * b + r) * kStepBytes + 16 * ((2 * g + half) ^ (r & 7)));
+      wait_lgkm();  // tile read: it may be overwritten
+      if (ks + kWinDepth < nks)
+        issue(src, ks + kWinDepth);
+      else if (has_next && ks + kWinDepth - nks < nks)
+        issue(nsrc, ks + kWinDepth - nks);  // the next unit's first tiles
+      // activations come from the window, which the loads never overwrite
       const uint8_t* qrow = &L.q[r & 7][64 * (8 * (ks & 7) + 2 * g)];
-      u32x4 qv[2][4];
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
+      for (int half = 0; half < 2; ++half) {
+        u32x4 qv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          qv[half][j] = *reinterpret_cast<const u32x4*>(qrow + 64 * half + 16 * j);
-      wait_lgkm();  // tile read: it may be overwritten
-      if (ks + kWinDepth < nks) issue(ks + kWinDepth);
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
+          qv[j] = *reinterpret_cast<const u32x4*>(qrow + 64 * half + 16 * j);
 #pragma unroll
         for (int b = 0; b < R; ++b) {
           const u32x4 x = wv[b][half];
           const i32x4 p0 = as_i32x4(x & 0x03030303u), p1 = as_i32x4(x & 0x0C0C0C0Cu);
           const i32x4 p2 = as_i32x4(x & 0x30303030u), p3 = as_i32x4((x >> 6) & 0x03030303u);
-          acc1[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[half][0]), p0, acc1[b], 0, 0, 0);
-          acc4[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[half][1]), p1, acc4[b], 0, 0, 0);
-          acc16[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[half][2]), p2, acc16[b], 0, 0, 0);
-          acc1[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[half][3]), p3, acc1[b], 0, 0, 0);
+          acc1[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[0]), p0, acc1[b], 0, 0, 0);
+          acc4[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[1]), p1, acc4[b], 0, 0, 0);
+          acc16[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[2]), p2, acc16[b], 0, 0, 0);
+          acc1[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[3]), p3, acc1[b], 0, 0, 0);
         }
+      }
     }
 
     // epilogue: lane holds tokens 4g + v of row base + 16b + r
+    int32_t zt[4];
+    float sa[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) zt[v] = L.z[(4 * g + v) & 7], sa[v] = L.s_act[(4 * g + v) & 7];
 #pragma unroll
     for (int b = 0; b < R; ++b) {
       const int row = base + 16 * b + r;
       if (row >= row_hi) continue;
-      const int32_t rs = load_g(a.rowsum + row);
-      const float sr = load_g(a.s_row + row);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = 4 * g + v;
         if (m < M) {
           const int32_t cq = acc1[b][v] + (acc4[b][v] >> 2) + (acc16[b][v] >> 4);  // sum(c*q)
           const int32_t accv = (int32_t)((uint32_t)cq - (uint32_t)L.qsum[m] -
-                                         (uint32_t)load_g(a.z + m) * (uint32_t)rs);
+                                         (uint32_t)zt[v] * (uint32_t)rs[b]);
           const int64_t o = (int64_t)m * a.ldy + row;
-          store_g(a.y + o, epilogue(sr, accv, load_g(a.s_act + m)));
+          store_g(a.y + o, epilogue(sr[b], accv, sa[v]));
           if (a.acc) store_g(a.acc + o, accv);
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) src[i] = nsrc[i];
   }
 }
 
@@ -608,13 +684,11 @@ __global__ __launch_bounds__(kBlock) void mfma_wg_stack_kernel(const StackHeader
 // M <= 8, every K a multiple of 64: the activation-window kernel.
 __global__ __launch_bounds__(kWinBlock) void mfma_win_linear_kernel(LinearArgs a) {
   __shared__ __attribute__((aligned(16))) WinTiles L;
-  const int8_t* staged_q = nullptr;
-  int staged_k = 0;
-  mfma_win_range(a, 0, a.N, blockIdx.x, gridDim.x, threadIdx.x & 63, wave_id_uniform(), L, staged_q,
-                 staged_k);
+  WinStaged staged;
+  mfma_win_range(a, 0, a.N, blockIdx.x, gridDim.x, threadIdx.x & 63, wave_id_uniform(), L, staged);
 }
 
-__global__ __launch_bounds__(kWinBlock) void mfma_win_stack_kernel(const StackHeader* __restrict__ h) {
+__global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void mfma_win_stack_kernel(const StackHeader* __restrict__ h) {
   __shared__ __attribute__((aligned(16))) WinTiles L;
   const int worker = xcd_logical_block();
   if (worker >= h->workers) return;  // the same for the whole workgroup
@@ -625,12 +699,11 @@ __global__ __launch_bounds__(kWinBlock) void mfma_win_stack_kernel(const StackHe
   const int32_t* seg_start = reinterpret_cast<const int32_t*>(base + h->off_seg_start);
   const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
   const int s1 = seg_start[worker + 1];
-  const int8_t* staged_q = nullptr;
-  int staged_k = 0;
+  WinStaged staged;
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
-    mfma_win_range(a, sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged_q, staged_k);
+    mfma_win_range(a, sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged);
   }
 }
 
@@ -639,8 +712,8 @@ __global__ __launch_bounds__(kWinBlock) void mfma_win_stack_kernel(const StackHe
 // 8 = the activation-window kernel (M <= 8, no ragged K).
 constexpr int32_t kWinVariant = 8;
 
-int32_t mfma_stack_variant(int32_t M, bool ragged) {
-  if (M <= kWinTokens && !ragged) return kWinVariant;
+int32_t mfma_stack_variant(int32_t M, bool ragged, bool big) {
+  if (M <= kWinTokens && !ragged && !big) return kWinVariant;
   return (M > 16 ? 1 : 0) | (ragged ? 2 : 0) | (M > 8 && M <= 16 ? 4 : 0);
 }
 
@@ -666,7 +739,7 @@ static hipError_t with_mfma_stack_kernel(int32_t variant, F&& f) {
 }
 
 hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
-  const int32_t v = mfma_stack_variant(a.M, (a.K & 63) != 0);
+  const int32_t v = mfma_stack_variant(a.M, (a.K & 63) != 0, (int64_t)a.N * a.ld >= (1ll << 32));
   const int64_t units = (a.N + mfma_unit_rows(v) - 1) / mfma_unit_rows(v);
   int64_t blocks = mfma_per_workgroup(v) ? units : (units + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks > 8192) blocks = 8192;
