@@ -234,7 +234,7 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
     if (descs[i].N == 0) continue;
     const int32_t v = descs[i].K % 64 ? (int32_t)VGEN : valu_variant_for(descs[i].K);
     used |= 1u << v;
-    big = big || descs[i].N * row_bytes(descs[i].K) >= (1ll << 32);
+    big = big || !mfma_win_offsets_fit(descs[i].N, row_bytes(descs[i].K), M, descs[i].ldy);
   }
   const bool ragged = (used >> VGEN) & 1u;
   const int32_t kernel = p == TERN_PATH_VALU

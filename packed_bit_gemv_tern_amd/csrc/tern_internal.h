@@ -95,8 +95,10 @@ int32_t valu_stack_kernel_for(int32_t M, uint32_t used_variants);
 hipError_t launch_valu_stack(int32_t kernel, const void* ws, const LaunchShape& shp,
                              hipStream_t s);
 int valu_stack_blocks_per_cu(int32_t kernel);
-// big: some linear has N * row_bytes >= 2^32
+// big: some linear's weight or output offsets do not fit the 32-bit offsets
+// of the activation-window kernel (see mfma_win_offsets_fit)
 int32_t mfma_stack_variant(int32_t M, bool ragged, bool big);
+bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy);
 hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape& shp,
                              hipStream_t s);
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int grid, int unroll,

@@ -592,9 +592,11 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
           const int32_t cq = acc1[b][v] + (acc4[b][v] >> 2) + (acc16[b][v] >> 4);  // sum(c*q)
           const int32_t accv = (int32_t)((uint32_t)cq - (uint32_t)L.qsum[m] -
                                          (uint32_t)zt[v] * (uint32_t)rs[b]);
-          const int64_t o = (int64_t)m * a.ldy + row;
-          store_g(a.y + o, epilogue(sr[b], accv, sa[v]));
-          if (a.acc) store_g(a.acc + o, accv);
+          // byte offset of (m, row) in y and acc: below 2^32 (checked by the host)
+          const uint32_t off = ((uint32_t)m * (uint32_t)a.ldy + (uint32_t)row) * 4u;
+          store_g(reinterpret_cast<float*>(reinterpret_cast<char*>(a.y) + off),
+                  epilogue(sr[b], accv, sa[v]));
+          if (a.acc) store_g(reinterpret_cast<int32_t*>(reinterpret_cast<char*>(a.acc) + off), accv);
         }
       }
     }
@@ -682,7 +684,7 @@ __global__ __launch_bounds__(kBlock) void mfma_wg_stack_kernel(const StackHeader
 }
 
 // M <= 8, every K a multiple of 64: the activation-window kernel.
-__global__ __launch_bounds__(kWinBlock) void mfma_win_linear_kernel(LinearArgs a) {
+__global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void mfma_win_linear_kernel(LinearArgs a) {
   __shared__ __attribute__((aligned(16))) WinTiles L;
   WinStaged staged;
   mfma_win_range(a, 0, a.N, blockIdx.x, gridDim.x, threadIdx.x & 63, wave_id_uniform(), L, staged);
@@ -712,6 +714,11 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4)
 // 8 = the activation-window kernel (M <= 8, no ragged K).
 constexpr int32_t kWinVariant = 8;
 
+bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy) {
+  // weight row offsets and output byte offsets are 32-bit in that kernel
+  return N * ld < (1ll << 32) && M * ldy * 4 < (1ll << 32);
+}
+
 int32_t mfma_stack_variant(int32_t M, bool ragged, bool big) {
   if (M <= kWinTokens && !ragged && !big) return kWinVariant;
   return (M > 16 ? 1 : 0) | (ragged ? 2 : 0) | (M > 8 && M <= 16 ? 4 : 0);
@@ -739,7 +746,7 @@ static hipError_t with_mfma_stack_kernel(int32_t variant, F&& f) {
 }
 
 hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
-  const int32_t v = mfma_stack_variant(a.M, (a.K & 63) != 0, (int64_t)a.N * a.ld >= (1ll << 32));
+  const int32_t v = mfma_stack_variant(a.M, (a.K & 63) != 0, !mfma_win_offsets_fit(a.N, a.ld, a.M, a.ldy));
   const int64_t units = (a.N + mfma_unit_rows(v) - 1) / mfma_unit_rows(v);
   int64_t blocks = mfma_per_workgroup(v) ? units : (units + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks > 8192) blocks = 8192;

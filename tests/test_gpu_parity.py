@@ -262,3 +262,35 @@ def test_stack_mixed_shapes_and_empty_linear():
         for lin, up in zip(lins, ups):
             y, acc = up.results()
             assert_parity(y, acc, oracle_ref(lin), "mixed %s M=%d" % (lin.name, M))
+
+
+@pytest.mark.parametrize("ldy", [(1 << 29) - 64, 1 << 29])
+def test_outputs_near_32bit_offsets(ldy):
+    """M = 2 outputs rows ldy apart: (M * ldy * 4) just below 2^32 keeps the
+    activation-window kernel (32-bit output offsets); 2^32 sends the call to
+    the other MFMA kernel.  Both through gemm_smallM and through the stack."""
+    N, K, M = 300, 4096, 2
+    lin = make(N, K, M, seed=41)
+    up = Uploaded(lin)
+    ref = oracle_ref(lin)
+    y = torch.full((M, ldy), float("nan"), dtype=torch.float32, device=DEV)
+    acc = torch.full((M, ldy), -7, dtype=torch.int32, device=DEV)
+
+    def fetch():
+        torch.cuda.synchronize()
+        return y[:, :N].cpu().numpy(), acc[:, :N].cpu().numpy()
+
+    tern.tern_gemm_smallM(up.packed, up.s_row, up.rowsum, N, K, M, up.q, up.ldq, up.s_act, up.z,
+                          y, ldy, acc, tern.TERN_PATH_MFMA)
+    assert_parity(*fetch(), ref, "gemm ldy=%d" % ldy)
+    torch.cuda.synchronize()
+    assert torch.isnan(y[:, N:N + 64]).all() and torch.isnan(y[:, -64:]).all()
+
+    y.fill_(float("nan"))
+    acc.fill_(-7)
+    desc = tern.make_desc(up.packed, up.s_row, up.rowsum, N, K, up.q, up.ldq, up.s_act, up.z, y,
+                          ldy, acc)
+    ws = torch.empty(tern.tern_linear_stack_workspace_bytes(1, M), dtype=torch.uint8, device=DEV)
+    plan = tern.tern_linear_stack_prepare([desc], M, ws, tern.TERN_PATH_MFMA)
+    tern.tern_linear_stack(plan)
+    assert_parity(*fetch(), ref, "stack ldy=%d" % ldy)
