@@ -14,6 +14,13 @@ is for the launch that takes longer, timed with HIP events on the stream the
 kernels run on; ``cpu_baseline`` is the CPU oracle on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+``--suite`` instead measures the other workloads of the method, one JSON line
+each: the single 256 x 512 GEMV; one 8B layer at M = 1 per linear and per
+layer (eight rotating copies, 390 MB, more than the 256 MB Infinity Cache);
+the 0.6B stack as seven M = 1 passes per step (three rotating copies, and
+warm); and the prefill sweep M = 1 .. 512 on one 8B layer (eight copies).
+Each line carries the oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -137,6 +144,178 @@ def cpu_baseline(seconds: float):
     }
 
 
+INT8_DENSE_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, published peak
+
+
+def _event_times(fn, calls: int, warm: int = 3):
+    """Per-call HIP-event durations (us, sorted) of fn(i), i = 0..calls-1,
+    after `warm` untimed calls, on the current stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warm):
+        fn(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    torch.cuda.synchronize()
+    for i in range(calls):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+
+def _stats(us, nbytes=None):
+    n = len(us)
+    med = us[n // 2]
+    out = {"median_us": round(med, 3), "p10_us": round(us[n // 10], 3),
+           "p90_us": round(us[(9 * n) // 10], 3), "calls": n}
+    if nbytes is not None:
+        out["bytes"] = int(nbytes)
+        out["GBps"] = round(nbytes / med / 1e3, 1)
+        out["frac_of_peak"] = round(nbytes / med / 1e3 / HBM_PEAK_GBS, 4)
+    return out
+
+
+def _oracle_rate(cases, seconds: float):
+    """The oracle on `cases` [(packed, s_row, rowsum, K, q, s_act, z, nbytes)],
+    repeated until `seconds` have passed: (GB/s of algorithmic bytes, us per
+    pass over the cases, repetitions)."""
+    import oracle
+    lib = oracle.load()
+    t, done, reps = 0.0, 0, 0
+    while t < seconds or reps == 0:
+        for (packed, s_row, rowsum, K, q, s_act, z, nbytes) in cases:
+            t0 = time.perf_counter()
+            oracle.linear(packed, s_row, rowsum, K, q, s_act, z, lib=lib)
+            t += time.perf_counter() - t0
+            done += nbytes
+        reps += 1
+    return done / t / 1e9, t / reps * 1e6, reps
+
+
+def suite(args):
+    """The measurement suite (one JSON line per workload)."""
+    import numpy as np
+    import torch
+    import oracle
+    from packed_bit_gemv_tern_amd import synth, tern
+    from packed_bit_gemv_tern_amd.stack import DeviceStack
+
+    dev = "cuda:0"
+    olib = oracle.load()
+    cores = oracle.threads()
+
+    def emit(d):
+        print(json.dumps(d), flush=True)
+
+    def linear_bytes(N, K, M):
+        return N * tern.tern_row_bytes(K) + 8 * N + M * K + 8 * M + 4 * M * N
+
+    # --- single GEMV, 256 x 512 (cache-resident, launch-bound: microseconds only)
+    lin = synth.single_gemv_case()
+    N, K = lin.w.shape
+    wd = torch.from_numpy(lin.w).to(dev)
+    packed = torch.empty((N, tern.tern_row_bytes(K)), dtype=torch.uint8, device=dev)
+    rowsum = torch.empty(N, dtype=torch.int32, device=dev)
+    tern.tern_pack(wd, N, K, K, packed, rowsum)
+    s_row = torch.from_numpy(lin.s_row).to(dev)
+    q = torch.from_numpy(lin.q.reshape(-1)).to(dev)
+    s_act = torch.from_numpy(lin.s_act).to(dev)
+    z = torch.from_numpy(lin.z).to(dev)
+    y = torch.empty(N, dtype=torch.float32, device=dev)
+    us = _event_times(lambda i: tern.tern_gemv(packed, s_row, rowsum, N, K, q, s_act, z, y), 200)
+    opk, ors, _ = oracle.pack(lin.w, lib=olib)
+    ogb, ous, oreps = _oracle_rate([(opk, lin.s_row, ors, K, lin.q, lin.s_act, lin.z,
+                                     linear_bytes(N, K, 1))], 2.0)
+    emit({"suite": "single_gemv", "workload": "one 256 x 512 ternary GEMV (seed 0), M = 1",
+          "kernel": "valu_linear_kernel", **_stats(us, linear_bytes(N, K, 1)),
+          "note": "cache-resident and launch-bound: microseconds, no roofline claim",
+          "cpu_oracle": {"us": round(ous, 2), "cores": cores, "reps": oreps}})
+
+    # --- one 8B layer at M = 1: per linear and per layer, eight rotating copies
+    copies = [DeviceStack("8b", layers=1, seed=c, threads=16) for c in range(8)]
+    specs = copies[0].specs
+    b1 = [st.bind(1) for st in copies]
+    for idx, (layer, _, name, N, K, p0) in enumerate(specs):
+        def call(i, idx=idx):
+            c = i % 8
+            pl, b = copies[c].linears[idx], b1[c]
+            tern.tern_gemv(pl.packed, pl.s_row, pl.rowsum, pl.N, pl.K, b.q[idx].view(-1),
+                           b.s_act[idx], b.z[idx], b.y[idx].view(-1))
+        us = _event_times(call, 64)
+        emit({"suite": "layer8b_linear", "workload": "8B layer 0 %s (%d x %d), M = 1, 8 rotating "
+              "copies" % (name, N, K), "linear": name, "N": N, "K": K,
+              "kernel": "valu_linear_kernel", **_stats(us, linear_bytes(N, K, 1))})
+    us = _event_times(lambda i: b1[i % 8].run(), 64)
+    lb = b1[0].bytes
+    # oracle: layer 0 at M = 1
+    cases = []
+    for (layer, idx, name, N, K, p0) in specs:
+        w, sr = synth.make_weights(0, layer, idx, N, K, p0)
+        pk, rs, _ = oracle.pack(w, lib=olib)
+        qq, sa, zz = synth.make_activations(0, layer, idx, K, 1)
+        cases.append((pk, sr, rs, K, qq, sa, zz, linear_bytes(N, K, 1)))
+    ogb, ous, oreps = _oracle_rate(cases, 5.0)
+    emit({"suite": "layer8b", "workload": "one 8B layer (7 linears), M = 1, one stack launch, "
+          "8 rotating copies (390 MB)", "kernel": kernel_name(b1[0].plan), **_stats(us, lb),
+          "cpu_oracle": {"GBps": round(ogb, 4), "us": round(ous, 1), "cores": cores,
+                         "reps": oreps}})
+    del b1, cases
+
+    # --- prefill sweep on one 8B layer, eight rotating copies
+    for M in (1, 2, 4, 8, 16, 64, 512):
+        bm = [st.bind(M) for st in copies]
+        us = _event_times(lambda i: bm[i % 8].run(), 48)
+        st = _stats(us, bm[0].bytes)
+        dense_ops = 2 * M * sum(N * K for (_, _, _, N, K, _) in specs)
+        st["dense_TOPS"] = round(dense_ops / st["median_us"] / 1e6, 2)
+        st["frac_of_int8_peak"] = round(st["dense_TOPS"] / INT8_DENSE_PEAK_TOPS, 4)
+        rec = {"suite": "prefill_sweep", "workload": "one 8B layer (7 linears), M = %d, one "
+               "stack launch, 8 rotating copies" % M, "M": M, "kernel": kernel_name(bm[0].plan),
+               **st}
+        if M == 512:
+            # oracle on a row sample: 32 rows of each linear at M = 512
+            cases = []
+            for (layer, idx, name, N, K, p0) in specs:
+                w, sr = synth.make_weights(0, layer, idx, N, K, p0)
+                rows = np.arange(0, N, N // 32)[:32]
+                pk, rs, _ = oracle.pack(w[rows], lib=olib)
+                qq, sa, zz = synth.make_activations(0, layer, idx, K, M)
+                cases.append((pk, sr[rows], rs, K, qq, sa, zz, 2 * M * 32 * K))
+            ogb, ous, oreps = _oracle_rate(cases, 5.0)
+            rec["cpu_oracle"] = {"dense_GOPS": round(ogb, 3), "cores": cores, "reps": oreps,
+                                 "sample": "32 rows of each of the 7 linears at M = 512"}
+        emit(rec)
+        del bm
+    del copies
+
+    # --- 0.6B stack, M = 1, seven passes per step: 3 rotating copies, and warm
+    st06 = [DeviceStack("0.6b", seed=c, threads=16) for c in range(3)]
+    b06 = [st.bind(1) for st in st06]
+    pb = b06[0].bytes
+    us = _event_times(lambda i: b06[i % 3].run(), 63)
+    rot = _stats(us, pb)
+    us = _event_times(lambda i: b06[0].run(), 63)
+    warm = _stats(us, pb)
+    warm.pop("frac_of_peak")
+    cases = []
+    for (layer, idx, name, N, K, p0) in synth.stack_specs("0.6b"):
+        w, sr = synth.make_weights(0, layer, idx, N, K, p0)
+        pk, rs, _ = oracle.pack(w, lib=olib)
+        qq, sa, zz = synth.make_activations(0, layer, idx, K, 1)
+        cases.append((pk, sr, rs, K, qq, sa, zz, linear_bytes(N, K, 1)))
+    ogb, ous, oreps = _oracle_rate(cases, 5.0)
+    emit({"suite": "stack06b", "workload": "0.6B-shaped stack (196 linears), M = 1; a step is "
+          "seven passes (one per drafted token)", "kernel": kernel_name(b06[0].plan),
+          "pass_rotating_3_copies": rot, "step_us_rotating": round(7 * rot["median_us"], 2),
+          "pass_warm_same_copy": warm,
+          "note": "warm passes re-read a stack that fits the 256 MB Infinity Cache: no HBM "
+                  "fraction is claimed for them",
+          "cpu_oracle": {"GBps": round(ogb, 4), "us_per_pass": round(ous, 1), "cores": cores,
+                         "reps": oreps}})
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +327,9 @@ def main():
     ap.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth probe")
     ap.add_argument("--only", choices=["m1", "m8"], default=None,
                     help="launch a single pass per step (for profiling)")
+    ap.add_argument("--suite", action="store_true",
+                    help="measure the single GEMV, one 8B layer, the prefill sweep and the "
+                         "0.6B stack instead (one JSON line each)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times "
                          "(reference for the HBM byte counters) and exit")
@@ -174,6 +356,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
+    if args.suite:
+        suite(args)
         return
     # Each pass gets its own copy of the stack (different seeds): the two
     # passes never share weights, so neither can hit lines the other left in
