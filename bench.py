@@ -75,6 +75,8 @@ def kernel_name(plan) -> str:
     v = k - 8
     if v == 8:
         return "mfma_win_stack_kernel"
+    if v in (9, 10):
+        return "gemm_stack_kernel<%d>" % (64 if v == 9 else 128)
     ragged = "true" if v & 2 else "false"
     if v & 1:
         return "mfma_stack_kernel<4, %s>" % ragged

@@ -261,6 +261,9 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   };
   std::vector<Gran> gran;
   double total = 0.0;
+  // 0: segments hold rows; else the prefill GEMM's token tiles per row unit
+  // (its segments hold tile indices)
+  const int32_t ntok = p == TERN_PATH_VALU ? 0 : mfma_token_tiles(kernel - SK_MFMA, (int32_t)M);
   for (int64_t i = 0; i < L; ++i) {
     const tern_linear_desc& d = descs[i];
     lin[(size_t)i] = make_args(d.packed, d.s_row, d.rowsum, d.N, d.K, M, d.q, d.ldq, d.s_act, d.z,
@@ -272,8 +275,15 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
     for (int64_t r0 = 0; r0 < d.N; r0 += unit) {
       const int64_t r1 = std::min<int64_t>(d.N, r0 + unit);
       const double c = (double)(r1 - r0) * ld + 256.0;
-      gran.push_back({(int32_t)i, (int32_t)r0, (int32_t)r1, c});
-      total += c;
+      if (ntok == 0) {
+        gran.push_back({(int32_t)i, (int32_t)r0, (int32_t)r1, c});
+      } else {
+        // prefill GEMM: one granule per (row tile, token tile), numbered
+        // row tile first, so a run keeps reusing one weight tile
+        const int32_t t0 = (int32_t)(r0 / unit) * ntok;
+        for (int32_t tt = 0; tt < ntok; ++tt) gran.push_back({(int32_t)i, t0 + tt, t0 + tt + 1, c});
+      }
+      total += c * (ntok == 0 ? 1 : ntok);
     }
   }
   // Contiguous runs of granules, the largest run as small as it can be: the

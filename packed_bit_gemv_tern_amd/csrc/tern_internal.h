@@ -41,7 +41,9 @@ struct alignas(16) LinearArgs {
 };
 static_assert(sizeof(LinearArgs) == 96, "LinearArgs layout");
 
-// One schedule entry: rows [row_begin, row_end) of linear `lin`.
+// One schedule entry: rows [row_begin, row_end) of linear `lin` (all
+// tokens); for the prefill GEMM instead its tiles [row_begin, row_end) in
+// (row tile, token tile) order, tile = row_tile * token_tiles + token_tile.
 struct Segment {
   int32_t lin, row_begin, row_end, pad;
 };
@@ -99,6 +101,17 @@ int valu_stack_blocks_per_cu(int32_t kernel);
 // of the activation-window kernel (see mfma_win_offsets_fit)
 int32_t mfma_stack_variant(int32_t M, bool ragged, bool big);
 bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy);
+
+// Prefill GEMM (M > 16; tern_gemm.hip): tiles of gemm_unit_rows(bm) rows x
+// bm = gemm_tile_tokens(M) tokens, one workgroup per tile.
+int gemm_tile_tokens(int32_t M);
+int gemm_unit_rows(int bm);
+hipError_t launch_gemm_linear(const LinearArgs& a, hipStream_t s);
+hipError_t launch_gemm_stack(int bm, const void* ws, const LaunchShape& shp, hipStream_t s);
+int gemm_stack_blocks_per_cu(int bm);
+// token tiles of the prefill GEMM per row unit (its schedule counts tiles);
+// 0 for every other kernel (its schedule counts rows)
+int32_t mfma_token_tiles(int32_t variant, int32_t M);
 hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape& shp,
                              hipStream_t s);
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int grid, int unroll,

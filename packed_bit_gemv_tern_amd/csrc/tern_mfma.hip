@@ -1,5 +1,6 @@
-// tern_mfma.hip -- MFMA int8 path of the ternary linear, for M >= 2 tokens
-// (the batched verify pass of drafted decoding, and prefill-sized batches).
+// tern_mfma.hip -- MFMA int8 path of the ternary linear for 2 <= M <= 16
+// tokens (the batched verify pass of drafted decoding), and the MFMA path's
+// kernel selection (M > 16 goes to the prefill GEMM in tern_gemm.hip).
 //
 // The same packed weights serve M tokens (wiki entry "Neutrino-1", "What is
 // actually new here": the 8B scores up to seven drafted tokens in one batched
@@ -19,9 +20,8 @@
 //    sum is over all of K whatever order the hardware pairs them in;
 //  * result: lane l, register v holds token 4*(l/16)+v of row l%16.
 //
-// A wave computes R blocks of 16 rows for T blocks of 16 tokens; weights are
-// loaded once per (R-unit, token group) with coalesced 16-byte non-temporal
-// loads.
+// Two kernels: the lockstep workgroup kernel (9 <= M <= 16, or any K) and
+// the activation-window kernel (M <= 8, K a multiple of 64).
 #include "tern_device.h"
 
 namespace tern {
@@ -73,138 +73,14 @@ __device__ __forceinline__ i32x4 as_i32x4(u32x4 t) {
 constexpr int kStepBytes = 128;
 constexpr int kRowPitch = 144;
 
-// Units of 16*R rows, unit0 + k*ustride, inside [row_lo, row_hi); every
-// token group of T*16 tokens for each unit.
-//
-// Weights go HBM -> registers -> this wave's LDS tile -> registers:
-//  * global: wave-wide load i brings rows 8i..8i+7 of the tile, lane l the
-//    16 bytes at 16*(l%8) of row 8i + l/8 -- each instruction reads eight
-//    whole 128-byte lines, non-temporal (a pattern reading half lines made
-//    the L2 fetch every line twice);
-//  * LDS: lane (r, g) of row block b reads bytes [32g, 32g+32) of row
-//    16b + r, i.e. packed words 8g..8g+7 of the step; MFMA (half, j) takes
-//    word 8g + 4*half + j, weights 128g + 64*half + 16j .. +15 of the step,
-//    and the activations at the same 16 positions;
-//  * the next step's global loads are issued before the current step is
-//    consumed.  LDS accesses of one wave execute in order, so the tile needs
-//    no barrier.
-template <int R, int T, bool RAGGED>
-__device__ __forceinline__ void mfma_range(const LinearArgs& a, int row_lo, int row_hi, int unit0,
-                                           int ustride, int lane, uint8_t* tile) {
-  constexpr int UNIT = 16 * R;
-  constexpr int NLD = UNIT / 8;  // wave-wide 1 KB loads per K-step
-  const int r = lane & 15, g = lane >> 4;
-  const int lrow = lane >> 3, lchunk = lane & 7;
-  const int nch = a.nch, K = a.K, M = a.M;
-  const int nks = (nch + 7) / 8;
-
-#pragma unroll 1
-  for (int unit = unit0;; unit += ustride) {
-    const int base = row_lo + unit * UNIT;
-    if (base >= row_hi) break;
-    const uint8_t* src[NLD];
-#pragma unroll
-    for (int i = 0; i < NLD; ++i)
-      src[i] = a.packed + (int64_t)min(base + 8 * i + lrow, row_hi - 1) * a.ld;
-
-    for (int tok0 = 0; tok0 < M; tok0 += 16 * T) {
-      i32x4 acc[R][T];
-#pragma unroll
-      for (int b = 0; b < R; ++b)
-#pragma unroll
-        for (int t = 0; t < T; ++t) acc[b][t] = i32x4{0, 0, 0, 0};
-      const int8_t* qrows[T];
-      bool tok_ok[T];
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int m = tok0 + 16 * t + r;
-        tok_ok[t] = m < M;
-        qrows[t] = a.q + (int64_t)min(m, M - 1) * a.ldq;
-      }
-
-      u32x4 st[NLD];
-      {
-        const int ch = min(lchunk, nch - 1);
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) st[i] = load_weights16(src[i] + 16 * ch);
-      }
-      for (int ks = 0; ks < nks; ++ks) {
-#pragma unroll
-        for (int i = 0; i < NLD; ++i)
-          *reinterpret_cast<u32x4*>(tile + (8 * i + lrow) * kRowPitch + 16 * lchunk) = st[i];
-        if (ks + 1 < nks) {
-          const int ch = min(8 * (ks + 1) + lchunk, nch - 1);
-#pragma unroll
-          for (int i = 0; i < NLD; ++i) st[i] = load_weights16(src[i] + 16 * ch);
-        }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int ch = 8 * ks + 2 * g + half;
-          const bool ch_ok = ch < nch;
-          const int chc = min(ch, nch - 1);
-          i32x4 qa[T][4];
-#pragma unroll
-          for (int t = 0; t < T; ++t) {
-            const bool ok = ch_ok && tok_ok[t];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int j0 = 64 * chc + 16 * j;
-              i32x4 v;
-              if (RAGGED && j0 + 16 > K)
-                v = load_q16_tail(qrows[t], K, j0);
-              else
-                v = as_i32x4(load16(qrows[t] + j0));
-              qa[t][j] = ok ? v : i32x4{0, 0, 0, 0};
-            }
-          }
-#pragma unroll
-          for (int b = 0; b < R; ++b) {
-            const u32x4 wv = *reinterpret_cast<const u32x4*>(
-                tile + (16 * b + r) * kRowPitch + 32 * g + 16 * half);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const i32x4 wb = decode_word(wv[j]);
-#pragma unroll
-              for (int t = 0; t < T; ++t)
-                acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[t][j], wb, acc[b][t], 0, 0, 0);
-            }
-          }
-        }
-      }
-
-      // epilogue: lane holds tokens tok0 + 16t + 4g + v of row base + 16b + r
-#pragma unroll
-      for (int b = 0; b < R; ++b) {
-        const int row = base + 16 * b + r;
-        if (row >= row_hi) continue;
-        const int32_t rs = load_g(a.rowsum + row);
-        const float sr = load_g(a.s_row + row);
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int m = tok0 + 16 * t + 4 * g + v;
-            if (m < M) {
-              const int32_t accv =
-                  (int32_t)((uint32_t)acc[b][t][v] - (uint32_t)load_g(a.z + m) * (uint32_t)rs);
-              const int64_t o = (int64_t)m * a.ldy + row;
-              store_g(a.y + o, epilogue(sr, accv, load_g(a.s_act + m)));
-              if (a.acc) store_g(a.acc + o, accv);
-            }
-          }
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // M <= 16: the four waves of a workgroup take the four 64-row quarters of a
 // 256-row unit of one linear and walk K in lockstep.  Each K-step's
 // activations (MQ tokens x 512 bytes) are loaded once per workgroup with
 // whole-line loads -- wave w brings tokens 2*(QLD*w + i) and 2*(QLD*w + i) + 1
 // -- into a double-buffered LDS tile that every wave then reads its MFMA
-// operands from; weights keep the per-wave tile of mfma_range.  Reading the
+// operands from; weights go through a per-wave LDS tile (rows kRowPitch apart,
+// whole 128-byte lines per global load instruction).  Reading the
 // activations straight from memory in MFMA layout touched 32 cache lines per
 // load instruction and stalled the address unit.  One barrier per K-step:
 // it publishes step ks+1's activations, and it also guarantees every wave
@@ -616,41 +492,6 @@ __device__ __forceinline__ int xcd_logical_block() {
 
 }  // namespace
 
-constexpr int kTileBytes = 16 * kR * kRowPitch;
-
-// M > 16: every wave on its own rows (per-wave schedule).
-template <int T, bool RAGGED>
-__global__ __launch_bounds__(kBlock) void mfma_linear_kernel(LinearArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[kWavesPerBlock][kTileBytes];
-  const int lane = threadIdx.x & 63;
-  const int w = wave_id_uniform();
-  const int wave = blockIdx.x * kWavesPerBlock + w;
-  const int nw = gridDim.x * kWavesPerBlock;
-  mfma_range<kR, T, RAGGED>(a, 0, a.N, wave, nw, lane, tiles[w]);
-}
-
-template <int T, bool RAGGED>
-__global__ __launch_bounds__(kBlock) void mfma_stack_kernel(const StackHeader* __restrict__ h) {
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[kWavesPerBlock][kTileBytes];
-  const int lane = threadIdx.x & 63;
-  const int w = wave_id_uniform();
-  const int worker = xcd_logical_block() * kWavesPerBlock + w;
-  if (worker >= h->workers) return;
-  const char* base = reinterpret_cast<const char*>(h);
-  const LinearArgs* lin = reinterpret_cast<const LinearArgs*>(base + h->off_lin);
-  const int32_t* seg_start = reinterpret_cast<const int32_t*>(base + h->off_seg_start);
-  const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
-  const int s1 = seg_start[worker + 1];
-  for (int s = seg_start[worker]; s < s1; ++s) {
-    const Segment sg = seg[s];
-    const LinearArgs a = lin[sg.lin];
-    if (RAGGED && (a.K & 63) != 0)
-      mfma_range<kR, T, RAGGED>(a, sg.row_begin, sg.row_end, 0, 1, lane, tiles[w]);
-    else
-      mfma_range<kR, T, false>(a, sg.row_begin, sg.row_end, 0, 1, lane, tiles[w]);
-  }
-}
-
 // M <= 16: workgroups of four lockstep waves (per-workgroup schedule).
 template <int MQ, bool RAGGED>
 __global__ __launch_bounds__(kBlock) void mfma_wg_linear_kernel(LinearArgs a) {
@@ -709,10 +550,13 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4)
   }
 }
 
-// Kernel selector of the MFMA path: bit 0 = M > 16 (per-wave kernel, T = 4),
-// bit 1 = ragged K compiled in, bit 2 = 9 <= M <= 16 (16 activation rows);
-// 8 = the activation-window kernel (M <= 8, no ragged K).
+// Kernel selector of the MFMA path: bit 1 = ragged K compiled in, bit 2 =
+// 9 <= M <= 16 (16 activation rows) for the lockstep workgroup kernel;
+// 8 = the activation-window kernel (M <= 8, no ragged K); 9 and 10 = the
+// prefill GEMM (M > 16) with 64- and 128-token tiles.
 constexpr int32_t kWinVariant = 8;
+constexpr int32_t kGemm64Variant = 9;
+constexpr int32_t kGemm128Variant = 10;
 
 bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy) {
   // weight row offsets and output byte offsets are 32-bit in that kernel
@@ -720,15 +564,24 @@ bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy) {
 }
 
 int32_t mfma_stack_variant(int32_t M, bool ragged, bool big) {
+  if (M > 16) return gemm_tile_tokens(M) == 128 ? kGemm128Variant : kGemm64Variant;
   if (M <= kWinTokens && !ragged && !big) return kWinVariant;
-  return (M > 16 ? 1 : 0) | (ragged ? 2 : 0) | (M > 8 && M <= 16 ? 4 : 0);
+  return (ragged ? 2 : 0) | (M > 8 ? 4 : 0);
 }
 
-bool mfma_per_workgroup(int32_t variant) { return (variant & 1) == 0; }
+int32_t mfma_token_tiles(int32_t variant, int32_t M) {
+  if (variant != kGemm64Variant && variant != kGemm128Variant) return 0;
+  const int bm = variant == kGemm128Variant ? 128 : 64;
+  return (M + bm - 1) / bm;
+}
+
+bool mfma_per_workgroup(int32_t) { return true; }
 
 int mfma_unit_rows(int32_t variant) {
   if (variant == kWinVariant) return kWinRows;
-  return mfma_per_workgroup(variant) ? kWgRows : 16 * kR;
+  if (variant == kGemm64Variant || variant == kGemm128Variant)
+    return gemm_unit_rows(variant == kGemm128Variant ? 128 : 64);
+  return kWgRows;
 }
 
 template <typename F>
@@ -738,8 +591,6 @@ static hipError_t with_mfma_stack_kernel(int32_t variant, F&& f) {
     case 2: return f(mfma_wg_stack_kernel<8, true>);
     case 4: return f(mfma_wg_stack_kernel<16, false>);
     case 6: return f(mfma_wg_stack_kernel<16, true>);
-    case 1: case 5: return f(mfma_stack_kernel<4, false>);
-    case 3: case 7: return f(mfma_stack_kernel<4, true>);
     case kWinVariant: return f(mfma_win_stack_kernel);
     default: return hipErrorInvalidValue;
   }
@@ -747,8 +598,9 @@ static hipError_t with_mfma_stack_kernel(int32_t variant, F&& f) {
 
 hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
   const int32_t v = mfma_stack_variant(a.M, (a.K & 63) != 0, !mfma_win_offsets_fit(a.N, a.ld, a.M, a.ldy));
+  if (v == kGemm64Variant || v == kGemm128Variant) return launch_gemm_linear(a, s);
   const int64_t units = (a.N + mfma_unit_rows(v) - 1) / mfma_unit_rows(v);
-  int64_t blocks = mfma_per_workgroup(v) ? units : (units + kWavesPerBlock - 1) / kWavesPerBlock;
+  int64_t blocks = units;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
   const dim3 grid((unsigned)blocks), block(kBlock);
@@ -758,13 +610,14 @@ hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
     case 2: hipLaunchKernelGGL((mfma_wg_linear_kernel<8, true>), grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL((mfma_wg_linear_kernel<16, false>), grid, block, 0, s, a); break;
     case 6: hipLaunchKernelGGL((mfma_wg_linear_kernel<16, true>), grid, block, 0, s, a); break;
-    case 1: case 5: hipLaunchKernelGGL((mfma_linear_kernel<4, false>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((mfma_linear_kernel<4, true>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape& shp, hipStream_t s) {
+  if (variant == kGemm64Variant || variant == kGemm128Variant)
+    return launch_gemm_stack(variant == kGemm128Variant ? 128 : 64, ws, shp, s);
   const StackHeader* h = static_cast<const StackHeader*>(ws);
   const dim3 grid(shp.grid), block(variant == kWinVariant ? kWinBlock : shp.block);
   return with_mfma_stack_kernel(variant, [&](auto kern) {
@@ -774,6 +627,8 @@ hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape&
 }
 
 int mfma_stack_blocks_per_cu(int32_t variant) {
+  if (variant == kGemm64Variant || variant == kGemm128Variant)
+    return gemm_stack_blocks_per_cu(variant == kGemm128Variant ? 128 : 64);
   int n = 0;
   const int block = variant == kWinVariant ? kWinBlock : kBlock;
   const hipError_t e = with_mfma_stack_kernel(variant, [&](auto kern) {

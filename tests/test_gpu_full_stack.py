@@ -47,3 +47,33 @@ def test_full_8b_stack_sampled(stack, M):
         assert np.array_equal(y.view(np.uint32), ry32.view(np.uint32)), pl.name
         checked += rows.size
     assert checked >= 252 * 256
+
+
+@pytest.fixture(scope="module")
+def layer8b():
+    from packed_bit_gemv_tern_amd.stack import DeviceStack
+    st = DeviceStack("8b", layers=1, seed=3, threads=16, sample_rows=96)
+    yield st
+    del st
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("M", [16, 64, 512])
+def test_8b_layer_prefill_sampled(layer8b, M):
+    """One 8B layer as one stack launch at prefill M (the configuration the
+    prefill sweep times): sampled rows of every linear against the oracle."""
+    b = layer8b.bind(M, with_acc=True)
+    b.run()
+    b.run()
+    torch.cuda.synchronize()
+    for i, pl in enumerate(layer8b.linears):
+        rows = pl.sample_rows
+        q, s_act, z = b.host_act[i]
+        rp, rr, bad = oracle.pack(pl.sample_w)
+        racc, ry32, ry64 = oracle.linear(rp, pl.sample_s_row, rr, pl.K, q, s_act, z)
+        acc = b.acc[i].cpu().numpy()[:, rows]
+        y = b.y[i].cpu().numpy()[:, rows]
+        assert np.array_equal(acc, racc), (pl.name, M)
+        assert np.all(np.abs(y.astype(np.float64) - ry64) <= RTOL * np.abs(ry64)), (pl.name, M)
+        assert np.array_equal(y.view(np.uint32), ry32.view(np.uint32)), (pl.name, M)

@@ -248,7 +248,7 @@ def test_stack_8b_one_layer(M):
 
 def test_stack_mixed_shapes_and_empty_linear():
     specs = [(5, 1, 1), (300, 4096, 2), (0, 64, 3), (77, 100, 4), (40, 12288, 5), (129, 1000, 6)]
-    for M in (1, 3):
+    for M in (1, 3, 8, 12, 40, 130):
         lins = [synth.make_linear(9, s, 0, N, K, 0.626, M, "m%d" % s) for (N, K, s) in specs]
         ups = [Uploaded(lin) for lin in lins if lin.N > 0]
         lins = [lin for lin in lins if lin.N > 0]
