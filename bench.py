@@ -149,13 +149,20 @@ def cpu_baseline(seconds: float):
 INT8_DENSE_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, published peak
 
 
-def _event_times(fn, calls: int, warm: int = 3):
+def _event_times(fn, calls: int, warm: int = 3, warm_s: float = 0.2):
     """Per-call HIP-event durations (us, sorted) of fn(i), i = 0..calls-1,
-    after `warm` untimed calls, on the current stream."""
+    after at least `warm` untimed calls and `warm_s` seconds of them (the
+    first launches after a change of workload run several percent slow),
+    on the current stream."""
     import torch
     stream = torch.cuda.current_stream()
-    for i in range(warm):
+    t_end = time.perf_counter() + warm_s
+    i = 0
+    while i < warm or time.perf_counter() < t_end:
         fn(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(calls)]
     torch.cuda.synchronize()

@@ -184,44 +184,55 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
 #pragma unroll
     for (int t = 0; t < S::WT; ++t) acc[b][t] = i32x4{0, 0, 0, 0};
 
+  // a step's operands in registers: packed weight dwords and activation
+  // fragments (the tail of K zeroed)
+  struct Ops {
+    uint32_t wd[S::WR];
+    i32x4 qa[S::WT];
+  };
+  auto load_ops = [&](int k, Ops& o) {
+    const int s = k % S::STAGES;
+#pragma unroll
+    for (int b = 0; b < S::WR; ++b)
+      o.wd[b] = *reinterpret_cast<const uint32_t*>(&L.w[s][16 * (rbase + 16 * b + r) + 4 * g]);
+#pragma unroll
+    for (int t = 0; t < S::WT; ++t) {
+      const int tt = tbase + 16 * t + r;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&L.q[s][64 * tt + 16 * (g ^ gemm_qswz(tt))]);
+      o.qa[t] = i32x4{(int32_t)v.x, (int32_t)v.y, (int32_t)v.z, (int32_t)v.w};
+    }
+    if (64 * k + 64 > K) {
+#pragma unroll
+      for (int t = 0; t < S::WT; ++t) o.qa[t] = gemm_mask_tail(o.qa[t], 64 * k + 16 * g, K);
+    }
+  };
+  auto compute = [&](const Ops& o) {
+#pragma unroll
+    for (int b = 0; b < S::WR; ++b) {
+      const i32x4 wb = gemm_decode(o.wd[b]);
+#pragma unroll
+      for (int t = 0; t < S::WT; ++t)
+        acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(o.qa[t], wb, acc[b][t], 0, 0, 0);
+    }
+  };
   issue_meta();  // older than every step's loads, so step 0's wait covers it
 #pragma unroll
   for (int s = 0; s < S::STAGES - 1; ++s)
     if (s < nks) issue(s);
-
+  // step k: my loads landed (later steps may still fly), then everybody's;
+  // the barrier also frees the buffer the next issue reuses
   for (int k = 0; k < nks; ++k) {
-    // this step's buffers: my DMAs landed (later steps may still fly), then
-    // everybody's; the barrier also frees the buffer the next issue reuses
     if (k + S::STAGES - 2 < nks)
       gemm_wait_vm<S::PER * (S::STAGES - 2)>();
     else
       gemm_wait_vm<0>();
     gemm_barrier();
     if (k + S::STAGES - 1 < nks) issue(k + S::STAGES - 1);
-    const int s = k % S::STAGES;
-    uint32_t wd[S::WR];
-#pragma unroll
-    for (int b = 0; b < S::WR; ++b)
-      wd[b] = *reinterpret_cast<const uint32_t*>(&L.w[s][16 * (rbase + 16 * b + r) + 4 * g]);
-    i32x4 qa[S::WT];
-#pragma unroll
-    for (int t = 0; t < S::WT; ++t) {
-      const int tt = tbase + 16 * t + r;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(&L.q[s][64 * tt + 16 * (g ^ gemm_qswz(tt))]);
-      qa[t] = i32x4{(int32_t)v.x, (int32_t)v.y, (int32_t)v.z, (int32_t)v.w};
-    }
-    if (64 * k + 64 > K) {
-#pragma unroll
-      for (int t = 0; t < S::WT; ++t) qa[t] = gemm_mask_tail(qa[t], 64 * k + 16 * g, K);
-    }
-#pragma unroll
-    for (int b = 0; b < S::WR; ++b) {
-      const i32x4 wb = gemm_decode(wd[b]);
-#pragma unroll
-      for (int t = 0; t < S::WT; ++t)
-        acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[t], wb, acc[b][t], 0, 0, 0);
-    }
+    Ops o;
+    load_ops(k, o);
+    compute(o);
   }
+
   // epilogue: lane holds tokens tok0 + tbase + 16t + 4g + v of row row0 + rbase + 16b + r
 #pragma unroll
   for (int b = 0; b < S::WR; ++b) {
