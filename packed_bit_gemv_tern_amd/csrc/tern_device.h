@@ -36,6 +36,32 @@ __device__ __forceinline__ void store_g(T* p, T v) {
   *(T __attribute__((address_space(1)))*)(p) = v;
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (stride 0, gfx9 format
+// word).  A buffer store whose offset lies outside the range is dropped by
+// the hardware, so a wave can issue a store on every lane and let the range
+// check mask it: no branch around the store, and the store is always in
+// the instruction stream (loads issued after it can then be waited for
+// without also waiting for it).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kDropOffset = 0x80000000u;  // beyond any range used here
+
+__device__ __forceinline__ void buffer_store_u32(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+
+// Range-checked loads (a load outside the range returns zero and touches no
+// memory).  The whole offset is the per-lane one: the range check covers it.
+// Weights use the non-temporal policy, as load_weights16.
+constexpr int kCpolNT = 2;
+__device__ __forceinline__ u32x4 buffer_load_weights16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCpolNT));
+}
+__device__ __forceinline__ uint32_t buffer_load_u32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 // ---- cross-lane exchange within a wave64 -------------------------------
 // dpp_partner<D>(v) returns v from a partner lane at "distance" D inside the
 // same 16-lane DPP row: for D = 8 the lane l ^ 8 (row_ror:8), for D = 4 the

@@ -141,38 +141,79 @@ __device__ __forceinline__ void valu_range_reg(const LinearArgs& a, int row_lo, 
   const float sa = load_g(a.s_act);
   const int32_t zb = load_g(a.z) + 128;
 
-#pragma unroll 1
-  for (int unit = unit0;; unit += ustride) {
-    const int base = row_lo + unit * UNIT;
-    if (base >= row_hi) break;
-    // Unconditional loads from clamped (in-bounds) addresses: rows past
-    // row_hi repeat the last row and are never stored; chunks past the row
-    // meet zero activations.  No branch, so all loads issue back to back.
+  // One unit's loads: U*CPL 16-byte weight chunks per lane plus the row sum
+  // and scale of the row this lane may store, all range-checked buffer
+  // loads over the unit's rows: rows past row_hi read as zero and are never
+  // stored, and a unit with live == false (there is no next unit) reads
+  // nothing at all -- the loads are still issued, so the wait counts are the
+  // same on every iteration.  Chunks past the row (K < 64 * LPR * CPL) are
+  // clamped to the row's last chunk; they meet zero activations.  All
+  // offsets below are fixed per lane.
+  struct Unit {
     u32x4 w[U][CPL];
+    int32_t rs;
+    float sr;
+  };
+  uint32_t woff[U][CPL];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int row = min(base + u * RPW + sub, row_hi - 1);
+  for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int t = 0; t < CPL; ++t) {
-        const int ch = min(r + LPR * t, nch - 1);
-        w[u][t] = load_weights16(a.packed + (int64_t)row * a.ld + 16 * ch);
-      }
-    }
-    const int my_row = base + my_u * RPW + sub;
-    const bool do_store = writer && my_row < row_hi;
-    const int my_row_c = min(my_row, row_hi - 1);
-    const int32_t rs = load_g(a.rowsum + my_row_c);
-    const float sr = load_g(a.s_row + my_row_c);
+    for (int t = 0; t < CPL; ++t)
+      woff[u][t] = (uint32_t)(u * RPW + sub) * (uint32_t)a.ld + 16u * (uint32_t)min(r + LPR * t, nch - 1);
+  const uint32_t roff = (uint32_t)(my_u * RPW + sub) * 4u;
+  auto issue = [&](int base, bool live, Unit& b) {
+    const uint32_t n = live ? (uint32_t)min(UNIT, row_hi - base) : 0u;
+    const auto rw = buffer_rsrc(const_cast<uint8_t*>(a.packed) + (int64_t)base * a.ld, n * (uint32_t)a.ld);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < CPL; ++t) b.w[u][t] = buffer_load_weights16(rw, woff[u][t]);
+    b.rs = (int32_t)buffer_load_u32(buffer_rsrc(const_cast<int32_t*>(a.rowsum) + base, 4u * n), roff);
+    b.sr = __uint_as_float(buffer_load_u32(buffer_rsrc(const_cast<float*>(a.s_row) + base, 4u * n), roff));
+  };
+
+  // Two units in flight: the next unit's loads are issued before the
+  // current one is reduced, so each wave keeps its memory queue busy while
+  // it computes.  The loop alternates two buffers (no copy between them,
+  // which would wait for the loads in flight).  Outputs go out through
+  // range-checked buffer stores (rows of the unit past row_hi and
+  // non-writer lanes are dropped).
+  auto finish = [&](const Unit& c, int base) {
     uint32_t part[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       uint32_t p[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int t = 0; t < CPL; ++t) dot_chunk(w[u][t], qc[t], p);
+      for (int t = 0; t < CPL; ++t) dot_chunk(c.w[u][t], qc[t], p);
       part[u] = combine_scaled(p);
     }
     const uint32_t tot = reduce_split<LPR, U>(part, lane);
-    if (do_store) store_out(a, 0, my_row, tot >> 6, qb_sum, zb, rs, sr, sa);
+    const int32_t acc = (int32_t)((tot >> 6) - qb_sum - (uint32_t)zb * (uint32_t)c.rs);
+    const uint32_t rows = (uint32_t)min(UNIT, row_hi - base) * 4u;
+    const uint32_t off = writer ? roff : kDropOffset;
+    buffer_store_u32(__float_as_uint(epilogue(c.sr, acc, sa)), buffer_rsrc(a.y + base, rows), off);
+    buffer_store_u32((uint32_t)acc, buffer_rsrc(a.acc ? a.acc + base : nullptr, a.acc ? rows : 0u), off);
+  };
+  const int step = ustride * UNIT;
+  if ((int64_t)row_lo + (int64_t)unit0 * UNIT >= row_hi) return;
+  int base = row_lo + unit0 * UNIT;
+  Unit ua, ub;
+  issue(base, true, ua);
+#pragma unroll 1
+  for (;;) {
+    // (64-bit compare: base + step may pass INT_MAX for N near it)
+    bool more = (int64_t)base + step < row_hi;
+    issue(more ? base + step : base, more, ub);
+    __builtin_amdgcn_sched_barrier(0);  // the next unit's loads go out first
+    finish(ua, base);
+    if (!more) break;
+    base += step;
+    more = (int64_t)base + step < row_hi;
+    issue(more ? base + step : base, more, ua);
+    __builtin_amdgcn_sched_barrier(0);
+    finish(ub, base);
+    if (!more) break;
+    base += step;
   }
 }
 
@@ -213,8 +254,8 @@ __device__ __forceinline__ void valu_range_stream(const LinearArgs& a, int row_l
 
 #pragma unroll 1
   for (int unit = unit0;; unit += ustride) {
+    if ((int64_t)row_lo + (int64_t)unit * U >= row_hi) break;
     const int base = row_lo + unit * U;
-    if (base >= row_hi) break;
     uint32_t part[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) part[v] = 0;
@@ -260,10 +301,10 @@ struct ValuCfg;
 template <> struct ValuCfg<V8x1>  { static constexpr int LPR = 8,  CPL = 1, U = 8; };
 template <> struct ValuCfg<V16x1> { static constexpr int LPR = 16, CPL = 1, U = 8; };
 template <> struct ValuCfg<V32x1> { static constexpr int LPR = 32, CPL = 1, U = 8; };
-template <> struct ValuCfg<V16x3> { static constexpr int LPR = 16, CPL = 3, U = 4; };
+template <> struct ValuCfg<V16x3> { static constexpr int LPR = 16, CPL = 3, U = 2; };
 template <> struct ValuCfg<V64x1> { static constexpr int LPR = 64, CPL = 1, U = 8; };
 template <> struct ValuCfg<V64x2> { static constexpr int LPR = 64, CPL = 2, U = 4; };
-template <> struct ValuCfg<V64x3> { static constexpr int LPR = 64, CPL = 3, U = 4; };
+template <> struct ValuCfg<V64x3> { static constexpr int LPR = 64, CPL = 3, U = 2; };
 template <> struct ValuCfg<V64x4> { static constexpr int LPR = 64, CPL = 4, U = 2; };
 constexpr int kStreamU = 8;
 
