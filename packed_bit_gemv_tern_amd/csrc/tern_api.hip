@@ -93,6 +93,11 @@ constexpr int kMaxWavesPerCu = 32;  // 8 waves per SIMD x 4 SIMDs
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
+// Schedule cost of one activation-window restage, in streamed bytes
+// (measured: ~5.8 us per restage at ~10 GB/s per workgroup at M = 8, and
+// 30-60 KB the best setting in a sweep).
+constexpr double kRestageCost = 40000.0;
+
 struct Layout {
   int64_t off_lin, off_seg_start, off_seg, total;
 };
@@ -272,9 +277,13 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
     const int unit = p == TERN_PATH_VALU ? valu_unit_rows(lin[(size_t)i].variant, (int32_t)M)
                                          : mfma_unit_rows(kernel - SK_MFMA);
     const double ld = (double)row_bytes(d.K);
+    // a unit that restages the activation window stalls its workgroup for
+    // about as long as streaming kRestageCost bytes takes
+    const double fixed =
+        256.0 + (p == TERN_PATH_VALU ? 0.0 : kRestageCost * mfma_unit_restages(kernel - SK_MFMA, d.K));
     for (int64_t r0 = 0; r0 < d.N; r0 += unit) {
       const int64_t r1 = std::min<int64_t>(d.N, r0 + unit);
-      const double c = (double)(r1 - r0) * ld + 256.0;
+      const double c = (double)(r1 - r0) * ld + fixed;
       if (ntok == 0) {
         gran.push_back({(int32_t)i, (int32_t)r0, (int32_t)r1, c});
       } else {

@@ -89,6 +89,9 @@ hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s);
 // Rows handled per work unit (schedule granularity) of each path.
 int valu_unit_rows(int32_t variant, int32_t M);
 int mfma_unit_rows(int32_t variant);
+// activation-window restages per unit of a linear with K columns (the
+// window kernel restages once per 4096 columns when K exceeds one window)
+int mfma_unit_restages(int32_t variant, int64_t K);
 bool mfma_per_workgroup(int32_t variant);
 int32_t valu_variant_for(int64_t K);
 

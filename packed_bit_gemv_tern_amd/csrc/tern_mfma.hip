@@ -584,6 +584,10 @@ int mfma_unit_rows(int32_t variant) {
   return kWgRows;
 }
 
+int mfma_unit_restages(int32_t variant, int64_t K) {
+  return variant == kWinVariant && K > kWinK ? (int)((K + kWinK - 1) / kWinK) : 0;
+}
+
 template <typename F>
 static hipError_t with_mfma_stack_kernel(int32_t variant, F&& f) {
   switch (variant) {

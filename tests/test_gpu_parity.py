@@ -161,7 +161,7 @@ def test_gemv_acc_optional_and_repeatable():
 
 # --------------------------------------------------------------- small M --
 
-SMALLM_K = [64, 100, 1024, 3072, 4096, 12288]
+SMALLM_K = [64, 100, 576, 1024, 3072, 4096, 4160, 12288]
 
 
 @pytest.mark.parametrize("M", list(range(1, 17)) + [17, 31, 64])
