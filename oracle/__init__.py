@@ -38,7 +38,7 @@ def build(force: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
         return out
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp%d" % os.getpid()
-    subprocess.run(["gcc", *CFLAGS, "-o", tmp, src], check=True)
+    subprocess.run(["gcc", *CFLAGS, "-o", tmp, src, "-lm"], check=True)
     os.replace(tmp, out)
     return out
 
@@ -82,6 +82,23 @@ def _declare(lib):
         _p(ctypes.c_int8), i64, _p(ctypes.c_float), i64, i64, i64,
         _p(ctypes.c_int8), i64, _p(ctypes.c_float), _p(i32),
         _p(i64), _p(ctypes.c_double), i64]
+    lib.oracle_head_rowsum.restype = None
+    lib.oracle_head_rowsum.argtypes = [_p(ctypes.c_int8), i64, i64, i64, _p(i32)]
+    lib.oracle_head.restype = ctypes.c_int
+    lib.oracle_head.argtypes = [
+        _p(ctypes.c_int8), i64, _p(ctypes.c_float), _p(i32), i64, i64, i64,
+        _p(ctypes.c_int8), i64, _p(ctypes.c_float), _p(i32),
+        _p(i32), _p(ctypes.c_float), _p(ctypes.c_double), i64]
+    lib.oracle_quantize_act.restype = None
+    lib.oracle_quantize_act.argtypes = [
+        _p(ctypes.c_float), i64, i64, i64, _p(ctypes.c_int8), i64, _p(ctypes.c_float), _p(i32)]
+    lib.oracle_block_rowsum.restype = None
+    lib.oracle_block_rowsum.argtypes = [_p(ctypes.c_int8), i64, i64, i64, i64, _p(i32)]
+    lib.oracle_linear_blocked.restype = ctypes.c_int
+    lib.oracle_linear_blocked.argtypes = [
+        _p(ctypes.c_uint8), _p(ctypes.c_float), _p(i32), i64, i64, i64, i64,
+        _p(ctypes.c_int8), i64, _p(ctypes.c_float), _p(i32),
+        _p(ctypes.c_float), _p(ctypes.c_double), _p(ctypes.c_double), i64]
     return lib
 
 
@@ -183,3 +200,91 @@ def linear_direct(w, s_row, q, s_act, z, lib=None):
                              _ptr(z, ctypes.c_int32), _ptr(acc, ctypes.c_int64),
                              _ptr(y64, ctypes.c_double), N)
     return acc, y64
+
+
+def _tokens(q, s_act, z, K):
+    q = _c(np.atleast_2d(q), np.int8)
+    M = q.shape[0]
+    assert q.shape[1] == K
+    s_act = _c(np.broadcast_to(np.asarray(s_act, np.float32).reshape(-1), (M,)), np.float32)
+    z = _c(np.broadcast_to(np.asarray(z, np.int32).reshape(-1), (M,)), np.int32)
+    return q, s_act, z, M
+
+
+def head_rowsum(W, lib=None):
+    """int32 (N,) row sums of an int8 (N, K) output-head matrix."""
+    lib = lib or load()
+    W = _c(np.atleast_2d(W), np.int8)
+    N, K = W.shape
+    rowsum = np.empty(N, np.int32)
+    lib.oracle_head_rowsum(_ptr(W, ctypes.c_int8), N, K, K, _ptr(rowsum, ctypes.c_int32))
+    return rowsum
+
+
+def head(W, s_row, rowsum, q, s_act, z, lib=None, check=True):
+    """Output-head logits: acc (int32), y32 (fp32), y64 (fp64), each (M, N)."""
+    lib = lib or load()
+    W = _c(np.atleast_2d(W), np.int8)
+    N, K = W.shape
+    q, s_act, z, M = _tokens(q, s_act, z, K)
+    s_row = _c(s_row, np.float32).reshape(-1)
+    rowsum = _c(rowsum, np.int32).reshape(-1)
+    assert s_row.shape[0] == N and rowsum.shape[0] == N
+    acc = np.empty((M, N), np.int32)
+    y32 = np.empty((M, N), np.float32)
+    y64 = np.empty((M, N), np.float64)
+    st = lib.oracle_head(_ptr(W, ctypes.c_int8), K, _ptr(s_row, ctypes.c_float),
+                         _ptr(rowsum, ctypes.c_int32), N, K, M, _ptr(q, ctypes.c_int8), K,
+                         _ptr(s_act, ctypes.c_float), _ptr(z, ctypes.c_int32),
+                         _ptr(acc, ctypes.c_int32), _ptr(y32, ctypes.c_float),
+                         _ptr(y64, ctypes.c_double), N)
+    if check and st != OK:
+        raise ValueError("oracle_head status %d" % st)
+    return acc, y32, y64
+
+
+def quantize_act(x, lib=None):
+    """Per-token asymmetric int8: x (M, K) float32 -> (q int8 (M, K), s_act (M,), z (M,))."""
+    lib = lib or load()
+    x = _c(np.atleast_2d(x), np.float32)
+    M, K = x.shape
+    q = np.empty((M, K), np.int8)
+    s_act = np.empty(M, np.float32)
+    z = np.empty(M, np.int32)
+    lib.oracle_quantize_act(_ptr(x, ctypes.c_float), M, K, K, _ptr(q, ctypes.c_int8), K,
+                            _ptr(s_act, ctypes.c_float), _ptr(z, ctypes.c_int32))
+    return q, s_act, z
+
+
+def block_rowsum(w, B, lib=None):
+    """int32 (N, ceil(K / B)) per-block row sums of an int8 ternary (N, K) matrix."""
+    lib = lib or load()
+    w = _c(np.atleast_2d(w), np.int8)
+    N, K = w.shape
+    nb = (K + B - 1) // B
+    out = np.empty((N, nb), np.int32)
+    lib.oracle_block_rowsum(_ptr(w, ctypes.c_int8), N, K, K, B, _ptr(out, ctypes.c_int32))
+    return out
+
+
+def linear_blocked(packed, s_b, rowsum_b, K, B, q, s_act, z, lib=None, check=True):
+    """Block-scaled linear: y32 (reference fp32 order), y64, yabs, each (M, N)."""
+    lib = lib or load()
+    q, s_act, z, M = _tokens(q, s_act, z, K)
+    packed = _c(packed, np.uint8)
+    s_b = _c(np.atleast_2d(s_b), np.float32)
+    rowsum_b = _c(np.atleast_2d(rowsum_b), np.int32)
+    N, nb = s_b.shape
+    assert nb == (K + B - 1) // B and rowsum_b.shape == (N, nb)
+    assert packed.size == N * row_bytes(K)
+    y32 = np.empty((M, N), np.float32)
+    y64 = np.empty((M, N), np.float64)
+    yabs = np.empty((M, N), np.float64)
+    st = lib.oracle_linear_blocked(_ptr(packed, ctypes.c_uint8), _ptr(s_b, ctypes.c_float),
+                                   _ptr(rowsum_b, ctypes.c_int32), N, K, B, M,
+                                   _ptr(q, ctypes.c_int8), K, _ptr(s_act, ctypes.c_float),
+                                   _ptr(z, ctypes.c_int32), _ptr(y32, ctypes.c_float),
+                                   _ptr(y64, ctypes.c_double), _ptr(yabs, ctypes.c_double), N)
+    if check and st != OK:
+        raise ValueError("oracle_linear_blocked status %d" % st)
+    return y32, y64, yabs

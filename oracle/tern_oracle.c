@@ -46,6 +46,7 @@
  */
 #include <stddef.h>
 #include <stdint.h>
+#include <math.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -228,4 +229,175 @@ int oracle_linear_direct(const int8_t* w, int64_t ldw, const float* s_row,
     }
   }
   return ORACLE_OK;
+}
+
+/* ====================== neighbours of the ternary linear ======================
+ *
+ * Output head.  The token embedding and the output head stay int8 with one
+ * scale per row; they are not ternary because no long sum hides their
+ * rounding (Neutrino-1 8B model card, "Where the bytes live"; article,
+ * "What's actually ternary").  Against the same per-token activations
+ * (q, s_act, z) the head's logits are
+ *
+ *     rowsum_i  = sum_j W_ij
+ *     acc[m][i] = sum_j W_ij * q[m][j]  -  z[m] * rowsum_i          (exact)
+ *     y[m][i]   = (s_row[i] * (float)acc[m][i]) * s_act[m]
+ *
+ * Here |acc| can pass 2^24, so the conversion to float is itself rounded
+ * (to nearest even): y32 is three roundings in that order.  The sum is
+ * taken in int64 and must fit in int32 (else ORACLE_OVERFLOW).
+ */
+void oracle_head_rowsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw,
+                        int32_t* rowsum) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < N; ++i) {
+    int64_t s = 0;
+    for (int64_t j = 0; j < K; ++j) s += W[i * ldw + j];
+    rowsum[i] = (int32_t)s;
+  }
+}
+
+int oracle_head(const int8_t* W, int64_t ldw, const float* s_row,
+                const int32_t* rowsum, int64_t N, int64_t K, int64_t M,
+                const int8_t* q, int64_t ldq, const float* s_act,
+                const int32_t* z, int32_t* acc, float* y32, double* y64,
+                int64_t ldy) {
+  int status = ORACLE_OK;
+#pragma omp parallel for schedule(static) collapse(2)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t i = 0; i < N; ++i) {
+      int64_t sum = 0;
+      for (int64_t j = 0; j < K; ++j)
+        sum += (int64_t)W[i * ldw + j] * (int64_t)q[m * ldq + j];
+      const int64_t a = sum - (int64_t)z[m] * (int64_t)rowsum[i];
+      if (a > INT32_MAX || a < INT32_MIN) {
+#pragma omp critical
+        if (status == ORACLE_OK) status = ORACLE_OVERFLOW;
+      }
+      if (acc) acc[m * ldy + i] = (int32_t)a;
+      if (y64) y64[m * ldy + i] = (double)s_row[i] * (double)a * (double)s_act[m];
+      if (y32) {
+        float fa = (float)(int32_t)a;    /* rounded when |a| > 2^24 */
+        float t = s_row[i] * fa;
+        y32[m * ldy + i] = t * s_act[m];
+      }
+    }
+  }
+  return status;
+}
+
+/*
+ * Activation quantiser.  The pages use int8 activations with a per-token
+ * scale and zero point but never say how they are made, so this is the
+ * plainest reading: asymmetric int8 over the token's range widened to
+ * contain zero (so that zero is exact and |z| <= 128):
+ *
+ *     lo  = min(0, min_j x_j),   hi = max(0, max_j x_j)
+ *     s   = (hi - lo) / 255          (fp32; s = 1 when hi == lo: all zeros)
+ *     z   = -128 - rint(lo / s)
+ *     q_j = clamp(rint(x_j / s) + z, -128, 127)
+ *
+ * Each division is one correctly rounded fp32 division; rint rounds half to
+ * even.  Then s * (q_j - z) is within s / 2 of x_j.  x holds M rows of K
+ * finite floats (row stride ldx); q is written with row stride ldq.
+ */
+void oracle_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx,
+                         int8_t* q, int64_t ldq, float* s_act, int32_t* z) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    const float* r = x + m * ldx;
+    float lo = 0.0f, hi = 0.0f;
+    for (int64_t j = 0; j < K; ++j) {
+      if (r[j] < lo) lo = r[j];
+      if (r[j] > hi) hi = r[j];
+    }
+    float s = (hi - lo) / 255.0f;
+    if (s == 0.0f) s = 1.0f;
+    const int32_t zm = -128 - (int32_t)rintf(lo / s);
+    for (int64_t j = 0; j < K; ++j) {
+      int32_t v = (int32_t)rintf(r[j] / s) + zm;
+      if (v < -128) v = -128;
+      if (v > 127) v = 127;
+      q[m * ldq + j] = (int8_t)v;
+    }
+    s_act[m] = s;
+    z[m] = zm;
+  }
+}
+
+/*
+ * Block-wise scales along K.  The article ("What's actually ternary") groups
+ * a row's weights into fixed-size blocks along the input dimension, each with
+ * its own higher-precision scale ("state times scale"); one scale per row is
+ * the coarsest case.  With block size B, block b of a row holds columns
+ * [b*B, min((b+1)*B, K)), nb = ceil(K / B) blocks, and
+ *
+ *     rowsum_b[i][b] = sum_{j in b} w_ij
+ *     acc_b          = sum_{j in b} w_ij * q[m][j]  -  z[m] * rowsum_b[i][b]  (exact)
+ *     y[m][i]        = (sum_{b = 0 .. nb-1} s_b[i][b] * acc_b) * s_act[m]
+ *
+ * y32 evaluates that in fp32 in the order written (each product rounded, a
+ * running sum from b = 0 up, then the product with s_act); y64 in fp64; and
+ * yabs = s_act * sum_b |s_b * acc_b| (fp64), which bounds the rounding of any
+ * fp32 evaluation order: |y_fp32 - y| <= (nb + 1) * 2^-24 * yabs to first
+ * order.  Metadata rows have stride nb.
+ */
+void oracle_block_rowsum(const int8_t* w, int64_t N, int64_t K, int64_t ldw,
+                         int64_t B, int32_t* rowsum_b) {
+  const int64_t nb = (K + B - 1) / B;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < N; ++i) {
+    for (int64_t b = 0; b < nb; ++b) {
+      int64_t s = 0;
+      for (int64_t j = b * B; j < K && j < (b + 1) * B; ++j) s += w[i * ldw + j];
+      rowsum_b[i * nb + b] = (int32_t)s;
+    }
+  }
+}
+
+int oracle_linear_blocked(const uint8_t* packed, const float* s_b,
+                          const int32_t* rowsum_b, int64_t N, int64_t K,
+                          int64_t B, int64_t M, const int8_t* q, int64_t ldq,
+                          const float* s_act, const int32_t* z, float* y32,
+                          double* y64, double* yabs, int64_t ldy) {
+  const int64_t ld = oracle_row_bytes(K);
+  const int64_t nb = (K + B - 1) / B;
+  const int64_t limit = (int64_t)1 << 24;
+  int status = ORACLE_OK;
+#pragma omp parallel for schedule(static) collapse(2)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t i = 0; i < N; ++i) {
+      const uint8_t* row = packed + i * ld;
+      float run = 0.0f;
+      double exact = 0.0, mag = 0.0;
+      int err = 0;
+      for (int64_t b = 0; b < nb; ++b) {
+        int64_t sum = 0;
+        for (int64_t j = b * B; j < K && j < (b + 1) * B; ++j) {
+          unsigned c = read_code(row, j);
+          if (c == 3u) {
+            err = ORACLE_INVALID_CODE;
+            continue;
+          }
+          int wv = (int)c - 1;
+          if (wv > 0) sum += q[m * ldq + j];
+          else if (wv < 0) sum -= q[m * ldq + j];
+        }
+        const int64_t a = sum - (int64_t)z[m] * (int64_t)rowsum_b[i * nb + b];
+        if (!err && (a >= limit || a <= -limit)) err = ORACLE_OVERFLOW;
+        const float sb = s_b[i * nb + b];
+        run = run + sb * (float)a; /* one rounding for the product, one for the sum */
+        exact += (double)sb * (double)a;
+        mag += fabs((double)sb * (double)a);
+      }
+      if (err) {
+#pragma omp critical
+        if (status == ORACLE_OK) status = err;
+      }
+      if (y32) y32[m * ldy + i] = run * s_act[m];
+      if (y64) y64[m * ldy + i] = exact * (double)s_act[m];
+      if (yabs) yabs[m * ldy + i] = mag * fabs((double)s_act[m]);
+    }
+  }
+  return status;
 }
