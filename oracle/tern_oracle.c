@@ -269,7 +269,7 @@ int oracle_head(const int8_t* W, int64_t ldw, const float* s_row,
       int64_t sum = 0;
       for (int64_t j = 0; j < K; ++j)
         sum += (int64_t)W[i * ldw + j] * (int64_t)q[m * ldq + j];
-      const int64_t a = sum - (int64_t)z[m] * (int64_t)rowsum[i];
+      const int64_t a = sum - (int64_t)rowsum[i] * (int64_t)z[m];
       if (a > INT32_MAX || a < INT32_MIN) {
 #pragma omp critical
         if (status == ORACLE_OK) status = ORACLE_OVERFLOW;
@@ -379,9 +379,7 @@ int oracle_linear_blocked(const uint8_t* packed, const float* s_b,
             err = ORACLE_INVALID_CODE;
             continue;
           }
-          int wv = (int)c - 1;
-          if (wv > 0) sum += q[m * ldq + j];
-          else if (wv < 0) sum -= q[m * ldq + j];
+          sum += (int64_t)((int)c - 1) * q[m * ldq + j]; /* add, subtract or skip */
         }
         const int64_t a = sum - (int64_t)z[m] * (int64_t)rowsum_b[i * nb + b];
         if (!err && (a >= limit || a <= -limit)) err = ORACLE_OVERFLOW;

@@ -62,3 +62,67 @@ def test_pins_catch_mutant(name, tmp_path):
         except BaseException:  # AssertionError, ValueError, pytest's Failed
             caught.append(check.__name__)
     assert caught, "no pin caught mutant %s" % name
+
+
+# ---- the neighbours (output head, activation quantiser, block scales) ----
+
+import test_oracle_neighbours as nbr  # noqa: E402
+
+NEIGHBOUR_CHECKS = [
+    nbr.test_quantize_hand_worked,
+    nbr.test_quantize_special_tokens,
+    lambda: [nbr.test_quantize_invariants(s) for s in range(3)],
+    nbr.test_quantize_power_of_two_scaling,
+    nbr.test_head_hand_worked,
+    nbr.test_head_int_to_float_rounding,
+    lambda: nbr.test_head_against_integer_matmul(3, 1000),
+    nbr.test_head_overflow_reported,
+    lambda: nbr.test_one_block_is_the_per_row_layer(100),
+    lambda: nbr.test_blocked_against_integer_sums(1000, 128),
+    nbr.test_blocked_equal_scales_reduce_to_row_scale,
+]
+
+NEIGHBOUR_MUTANTS = {
+    "quant_range_not_widened": ("float lo = 0.0f, hi = 0.0f;", "float lo = r[0], hi = r[0];"),
+    "quant_round_half_away": ("int32_t v = (int32_t)rintf(r[j] / s) + zm;",
+                              "int32_t v = (int32_t)roundf(r[j] / s) + zm;"),
+    "quant_256_steps": ("float s = (hi - lo) / 255.0f;", "float s = (hi - lo) / 256.0f;"),
+    "quant_zero_point_sign": ("const int32_t zm = -128 - (int32_t)rintf(lo / s);",
+                              "const int32_t zm = -128 + (int32_t)rintf(lo / s);"),
+    "head_rowsum_skips_last": ("for (int64_t j = 0; j < K; ++j) s += W[i * ldw + j];",
+                               "for (int64_t j = 0; j + 1 < K; ++j) s += W[i * ldw + j];"),
+    "head_zero_point_dropped": ("const int64_t a = sum - (int64_t)rowsum[i] * (int64_t)z[m];",
+                                "const int64_t a = sum;"),
+    "head_single_rounding": ("float t = s_row[i] * fa;\n        y32[m * ldy + i] = t * s_act[m];",
+                             "y32[m * ldy + i] = (float)((double)s_row[i] * (double)a * (double)s_act[m]);"
+                             " (void)fa;"),
+    "block_rowsum_overlaps": ("for (int64_t j = b * B; j < K && j < (b + 1) * B; ++j) s += w[i * ldw + j];",
+                              "for (int64_t j = b * B; j < K && j <= (b + 1) * B; ++j) s += w[i * ldw + j];"),
+    "block_scale_of_first_block": ("const float sb = s_b[i * nb + b];", "const float sb = s_b[i * nb];"),
+    "block_zero_point_dropped": ("const int64_t a = sum - (int64_t)z[m] * (int64_t)rowsum_b[i * nb + b];",
+                                 "const int64_t a = sum;"),
+    "block_act_scale_dropped": ("if (y64) y64[m * ldy + i] = exact * (double)s_act[m];",
+                                "if (y64) y64[m * ldy + i] = exact;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(NEIGHBOUR_MUTANTS))
+def test_neighbour_pins_catch_mutant(name, tmp_path, monkeypatch):
+    old, new = NEIGHBOUR_MUTANTS[name]
+    with open(oracle._SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, "mutation anchor not found once: %s" % name
+    path = os.path.join(str(tmp_path), "mutant.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.load(oracle.build(force=True, src=path, out=os.path.join(str(tmp_path), "libmut.so")))
+    monkeypatch.setattr(oracle, "_lib", lib)  # the neighbour pins use the default library
+    caught = 0
+    for check in NEIGHBOUR_CHECKS:
+        try:
+            check()
+        except (KeyboardInterrupt, SystemExit):
+            raise
+        except BaseException:
+            caught += 1
+    assert caught, "no pin caught mutant %s" % name

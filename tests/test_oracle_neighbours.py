@@ -119,6 +119,18 @@ def test_head_against_integer_matmul(M, K):
     assert np.all(np.abs(y32.astype(np.float64) - exact) <= 3.01 * U * np.abs(exact))
 
 
+def test_head_int_to_float_rounding():
+    # acc = 1040 * 127 * 127 + 127 * 24 + 1 * 9 = 16,777,217 = 2^24 + 1, which
+    # float rounds (to even) to 2^24; with s_row = 3 the three-rounding result
+    # is 3 * 2^24 = 50,331,648, while rounding 3 * (2^24 + 1) once would give
+    # 50,331,652 (fp32 spacing 4 there)
+    W = np.array([[127] * 1040 + [127, 1]], np.int8)
+    q = np.array([[127] * 1040 + [24, 9]], np.int8)
+    acc, y32, _ = oracle.head(W, [3.0], oracle.head_rowsum(W), q, 1.0, 0)
+    assert acc[0, 0] == 2 ** 24 + 1
+    assert y32[0, 0] == np.float32(50331648.0)
+
+
 def test_head_overflow_reported():
     # acc = K * (-128 * 127) - (-128) * (K * -128) = -32640 K, past -2^31
     K = 70000
