@@ -210,6 +210,51 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
 int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream);
 
 /*
+ * The int8 output head.  The token embedding and the output head are not
+ * ternary: they stay int8 with one scale per row (Neutrino-1 8B model card,
+ * "Where the bytes live"), because nothing sums their rounding errors away
+ * and the head decides tokens by small logit margins (article, "What's
+ * actually ternary").  Against the same per-token activations as the
+ * ternary calls the logits are
+ *
+ *     acc[m][i] = sum_j W_ij * q[m][j]  -  z[m] * rowsum[i]        (int32, exact)
+ *     y[m][i]   = (s_row[i] * (float)acc[m][i]) * s_act[m]         (fp32, RNE, in
+ *                                                                   this order)
+ *
+ * with rowsum[i] = sum_j W_ij from tern_head_rowsum.  |acc| may pass 2^24,
+ * so the conversion to float rounds too.  K <= TERN_HEAD_MAX_K keeps every
+ * intermediate inside int32 for |z| <= 255.
+ */
+#define TERN_HEAD_MAX_M 8
+#define TERN_HEAD_MAX_K 43803
+
+/*
+ * tern_head_rowsum -- load-time row sums of an int8 matrix.
+ *   W       device, N x K int8, row stride ldw >= K elements;
+ *   rowsum  device, N int32 (written).
+ */
+int tern_head_rowsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw, int32_t* rowsum,
+                     hipStream_t stream);
+
+/*
+ * tern_head_gemv -- logits of M <= TERN_HEAD_MAX_M tokens (M = 1 for plain
+ * decode, up to 8 for a drafted-and-verified step).
+ *   W       device, N x K int8, 16-byte aligned, row stride ldw >= K a
+ *           multiple of 16 (at most 2^28);
+ *   s_row   device, N floats;  rowsum  device, N int32 (tern_head_rowsum);
+ *   q       device, M x K int8, 16-byte aligned, row stride ldq >= K (a
+ *           multiple of 16 when M > 1);  s_act, z  device, M each;
+ *   y       device, M x N floats, row stride ldy >= N (written);
+ *   acc     device, M x N int32 with stride ldy (written) or NULL.
+ * M > TERN_HEAD_MAX_M gives TERN_ERR_UNSUPPORTED; a K whose activations do
+ * not fit the kernel's 64 KB of staging (about 7,900 columns at M > 4,
+ * 15,900 at M = 3..4) gives TERN_ERR_RANGE.
+ */
+int tern_head_gemv(const int8_t* W, const float* s_row, const int32_t* rowsum, int64_t N, int64_t K,
+                   int64_t ldw, int64_t M, const int8_t* q, int64_t ldq, const float* s_act,
+                   const int32_t* z, float* y, int64_t ldy, int32_t* acc, hipStream_t stream);
+
+/*
  * tern_read_probe -- a measurement aid, not part of the method: reads `bytes`
  * bytes of `buf` (device, 16-byte aligned, bytes a multiple of 16) with the
  * same 16-byte loads and workgroup shape as the GEMV kernels and does nothing

@@ -195,6 +195,44 @@ int tern_gemv(const uint8_t* packed, const float* s_row, const int32_t* rowsum, 
                           TERN_PATH_AUTO, stream);
 }
 
+int tern_head_rowsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw, int32_t* rowsum,
+                     hipStream_t stream) {
+  if (N < 0 || K < 1 || ldw < K) return TERN_ERR_INVALID_ARG;
+  if (K > TERN_HEAD_MAX_K || N > kI32Max) return TERN_ERR_RANGE;
+  if (N == 0) return TERN_OK;
+  if (!W || !rowsum) return TERN_ERR_INVALID_ARG;
+  if (!aligned(rowsum, 4)) return TERN_ERR_ALIGNMENT;
+  const hipError_t e = launch_head_rowsum(W, N, K, ldw, rowsum, stream);
+  return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
+int tern_head_gemv(const int8_t* W, const float* s_row, const int32_t* rowsum, int64_t N, int64_t K,
+                   int64_t ldw, int64_t M, const int8_t* q, int64_t ldq, const float* s_act,
+                   const int32_t* z, float* y, int64_t ldy, int32_t* acc, hipStream_t stream) {
+  if (N < 0 || M < 0 || K < 1 || ldw < K) return TERN_ERR_INVALID_ARG;
+  if (M > TERN_HEAD_MAX_M) return TERN_ERR_UNSUPPORTED;
+  if (K > TERN_HEAD_MAX_K || N > kI32Max || ldw > (1 << 28)) return TERN_ERR_RANGE;
+  if (N == 0 || M == 0) return TERN_OK;
+  if (!W || !s_row || !rowsum || !q || !s_act || !z || !y) return TERN_ERR_INVALID_ARG;
+  if (M > 1 && (ldq < K || ldy < N)) return TERN_ERR_INVALID_ARG;
+  if (ldq > kI32Max || ldy > kI32Max) return TERN_ERR_RANGE;
+  if (!aligned(W, 16) || (ldw % 16) != 0 || !aligned(q, 16) || (M > 1 && (ldq % 16) != 0))
+    return TERN_ERR_ALIGNMENT;
+  if (!aligned(y, 4) || !aligned(s_row, 4) || !aligned(rowsum, 4) || !aligned(s_act, 4) ||
+      !aligned(z, 4) || (acc && !aligned(acc, 4)))
+    return TERN_ERR_ALIGNMENT;
+  // a workgroup per ~4 of each CU's slots, with a whole number of units
+  const int cus = device_cus();
+  if (cus <= 0) return hip_fail(hipErrorNoDevice);
+  const int64_t unit = head_rows_per_unit(M);
+  const int64_t per = (N + 4 * (int64_t)cus - 1) / (4 * (int64_t)cus);
+  const int64_t rows = (per + unit - 1) / unit * unit;
+  if (head_lds_bytes(M, K, rows) > 65536) return TERN_ERR_RANGE;
+  const hipError_t e = launch_head(W, s_row, rowsum, N, K, ldw, M, q, M > 1 ? ldq : K, s_act, z, y,
+                                   M > 1 ? ldy : N, acc, rows, stream);
+  return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
 int64_t tern_linear_stack_workspace_bytes(int64_t L, int64_t M) {
   if (L < 0 || M < 0 || L > kI32Max) return 0;
   int cus = device_cus();

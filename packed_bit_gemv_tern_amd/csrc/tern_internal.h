@@ -117,6 +117,16 @@ int gemm_stack_blocks_per_cu(int bm);
 int32_t mfma_token_tiles(int32_t variant, int32_t M);
 hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape& shp,
                              hipStream_t s);
+// int8 output head (tern_head.hip): M <= 8 tokens, workgroups of contiguous rows
+int head_tokens(int64_t M);
+int head_rows_per_unit(int64_t M);  // rows a workgroup takes per pass of its waves
+int64_t head_lds_bytes(int64_t M, int64_t K, int64_t rows);
+hipError_t launch_head(const int8_t* W, const float* s_row, const int32_t* rowsum, int64_t N, int64_t K,
+                       int64_t ldw, int64_t M, const int8_t* q, int64_t ldq, const float* s_act,
+                       const int32_t* z, float* y, int64_t ldy, int32_t* acc, int64_t rows_per_wg,
+                       hipStream_t s);
+hipError_t launch_head_rowsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw, int32_t* rowsum,
+                              hipStream_t s);
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int grid, int unroll,
                              bool nontemporal, hipStream_t s);
 int mfma_stack_blocks_per_cu(int32_t variant);

@@ -212,3 +212,18 @@ def _take(futs, pos, out, consume):
         out.append(lin)
     else:
         consume(pos, lin)
+
+
+# The 8B's output head: vocabulary x hidden width (model card "Architecture":
+# vocabulary 151,936, hidden 4,096), int8 with one scale per row ("Where the
+# bytes live").  Trained values are not available: entries are uniform int8
+# in [-127, 127] and row scales U(1e-3, 1e-2).
+HEAD_8B = (151936, 4096)
+
+
+def make_head(seed, N: int = HEAD_8B[0], K: int = HEAD_8B[1]):
+    """(W int8 (N, K), s_row float32 (N,)) of a synthetic int8 output head."""
+    rng = np.random.default_rng([seed, 151936])
+    W = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    s_row = rng.uniform(1e-3, 1e-2, N).astype(np.float32)
+    return W, s_row

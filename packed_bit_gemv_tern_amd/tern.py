@@ -24,12 +24,15 @@ TERN_ERR_HIP = 6
 TERN_PATH_AUTO, TERN_PATH_VALU, TERN_PATH_MFMA = 0, 1, 2
 TERN_MAX_K = 5600000
 TERN_VALU_MAX_M = 8
+TERN_HEAD_MAX_M = 8
+TERN_HEAD_MAX_K = 43803
 
 # Every function include/tern.h declares.
 EXPORTS = (
     "tern_row_bytes", "tern_pack", "tern_unpack", "tern_validate", "tern_gemv",
     "tern_gemm_smallM", "tern_linear_stack_workspace_bytes", "tern_linear_stack_prepare",
-    "tern_linear_stack", "tern_read_probe", "tern_status_string", "tern_last_hip_error",
+    "tern_linear_stack", "tern_head_rowsum", "tern_head_gemv", "tern_read_probe",
+    "tern_status_string", "tern_last_hip_error",
 )
 
 
@@ -92,6 +95,8 @@ def _declare(lib):
         "tern_linear_stack_prepare": (i32, [ctypes.POINTER(tern_linear_desc), i64, i64, i32,
                                             vp, i64, ctypes.POINTER(tern_stack_plan), vp]),
         "tern_linear_stack": (i32, [ctypes.POINTER(tern_stack_plan), vp]),
+        "tern_head_rowsum": (i32, [vp, i64, i64, i64, vp, vp]),
+        "tern_head_gemv": (i32, [vp, vp, vp, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, vp]),
         "tern_read_probe": (i32, [vp, i64, vp, i32, i32, i32, vp]),
         "tern_status_string": (ctypes.c_char_p, [i32]),
         "tern_last_hip_error": (i32, []),
@@ -159,6 +164,17 @@ def tern_gemm_smallM(packed, s_row, rowsum, N, K, M, q, ldq, s_act, z, y, ldy, a
     _check(_lib().tern_gemm_smallM(_ptr(packed), _ptr(s_row), _ptr(rowsum), N, K, M, _ptr(q), ldq,
                                    _ptr(s_act), _ptr(z), _ptr(y), ldy, _ptr(acc), int(path),
                                    _stream(stream)), "tern_gemm_smallM")
+
+
+def tern_head_rowsum(W, N, K, ldw, rowsum, stream=None):
+    _check(_lib().tern_head_rowsum(_ptr(W), N, K, ldw, _ptr(rowsum), _stream(stream)),
+           "tern_head_rowsum")
+
+
+def tern_head_gemv(W, s_row, rowsum, N, K, ldw, M, q, ldq, s_act, z, y, ldy, acc=None, stream=None):
+    _check(_lib().tern_head_gemv(_ptr(W), _ptr(s_row), _ptr(rowsum), N, K, ldw, M, _ptr(q), ldq,
+                                 _ptr(s_act), _ptr(z), _ptr(y), ldy, _ptr(acc), _stream(stream)),
+           "tern_head_gemv")
 
 
 def tern_linear_stack_workspace_bytes(L: int, M: int) -> int:
