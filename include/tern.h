@@ -210,6 +210,23 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
 int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream);
 
 /*
+ * tern_quantize_act -- per-token asymmetric int8 activations for the calls
+ * above (they take x_j = s_act * (q_j - z)).  The pages do not describe the
+ * activation quantiser; this is the plainest reading, the token's range
+ * widened to contain zero, in 255 steps:
+ *     lo = min(0, min_j x_j),  hi = max(0, max_j x_j)
+ *     s_act = (hi - lo) / 255   (1 for an all-zero token)
+ *     z = -128 - rint(lo / s_act),  q_j = clamp(rint(x_j / s_act) + z, -128, 127)
+ * with correctly rounded fp32 divisions and rint rounding half to even, so
+ * zero is exact, |z| <= 128 and s_act * (q_j - z) is within s_act / 2 of x_j.
+ *   x      device, M x K finite floats, row stride ldx >= K;
+ *   q      device, M x K int8, row stride ldq >= K (columns < K written);
+ *   s_act  device, M floats (written);  z  device, M int32 (written).
+ */
+int tern_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
+                      float* s_act, int32_t* z, hipStream_t stream);
+
+/*
  * The int8 output head.  The token embedding and the output head are not
  * ternary: they stay int8 with one scale per row (Neutrino-1 8B model card,
  * "Where the bytes live"), because nothing sums their rounding errors away

@@ -195,6 +195,17 @@ int tern_gemv(const uint8_t* packed, const float* s_row, const int32_t* rowsum, 
                           TERN_PATH_AUTO, stream);
 }
 
+int tern_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
+                      float* s_act, int32_t* z, hipStream_t stream) {
+  if (M < 0 || K < 1 || ldx < K || ldq < K) return TERN_ERR_INVALID_ARG;
+  if (M > kI32Max) return TERN_ERR_RANGE;
+  if (M == 0) return TERN_OK;
+  if (!x || !q || !s_act || !z) return TERN_ERR_INVALID_ARG;
+  if (!aligned(x, 4) || !aligned(s_act, 4) || !aligned(z, 4)) return TERN_ERR_ALIGNMENT;
+  const hipError_t e = launch_quantize_act(x, M, K, ldx, q, ldq, s_act, z, stream);
+  return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
 int tern_head_rowsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw, int32_t* rowsum,
                      hipStream_t stream) {
   if (N < 0 || K < 1 || ldw < K) return TERN_ERR_INVALID_ARG;

@@ -127,6 +127,9 @@ hipError_t launch_head(const int8_t* W, const float* s_row, const int32_t* rowsu
                        hipStream_t s);
 hipError_t launch_head_rowsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw, int32_t* rowsum,
                               hipStream_t s);
+// per-token asymmetric int8 quantisation of activations (tern_quant.hip)
+hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                               int64_t ldq, float* s_act, int32_t* z, hipStream_t s);
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int grid, int unroll,
                              bool nontemporal, hipStream_t s);
 int mfma_stack_blocks_per_cu(int32_t variant);

@@ -1,0 +1,79 @@
+// tern_quant.hip -- per-token asymmetric int8 quantisation of activations.
+//
+// The ternary linears and the int8 head take each token's activations as
+// int8 q with an fp32 scale s_act and an int32 zero point z (x ~= s_act *
+// (q - z)).  The pages never describe how those are made, so this is the
+// plainest reading: the token's range widened to contain zero, in 255 steps
+// (zero stays exact and |z| <= 128):
+//
+//     lo = min(0, min_j x_j),  hi = max(0, max_j x_j)
+//     s  = (hi - lo) / 255          (s = 1 when hi == lo: an all-zero token)
+//     z  = -128 - rint(lo / s)
+//     q_j = clamp(rint(x_j / s) + z, -128, 127)
+//
+// Every division is one correctly rounded fp32 division and rint rounds half
+// to even, so the integer codes are a function of the fp32 inputs alone.
+// One workgroup per token: a min/max pass over the row, then the codes.
+#include "tern_device.h"
+
+namespace tern {
+
+namespace {
+
+constexpr int kQuantBlock = 256;
+
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fminf(v, __shfl_xor(v, d, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+  return v;
+}
+
+__global__ __launch_bounds__(kQuantBlock) void quant_kernel(const float* x, int64_t K, int64_t ldx,
+                                                            int8_t* q, int64_t ldq, float* s_act,
+                                                            int32_t* z) {
+  __shared__ float red[2][kQuantBlock / 64];
+  const int64_t m = blockIdx.x;
+  const float* r = x + m * ldx;
+  float lo = 0.0f, hi = 0.0f;
+  for (int64_t j = threadIdx.x; j < K; j += kQuantBlock) {
+    const float v = load_g(r + j);
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[0][w] = lo, red[1][w] = hi;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kQuantBlock / 64; ++i) lo = fminf(lo, red[0][i]), hi = fmaxf(hi, red[1][i]);
+  float s = __fdiv_rn(hi - lo, 255.0f);
+  if (s == 0.0f) s = 1.0f;
+  const int32_t zm = -128 - (int32_t)__builtin_rintf(__fdiv_rn(lo, s));
+  int8_t* out = q + m * ldq;
+  for (int64_t j = threadIdx.x; j < K; j += kQuantBlock) {
+    int32_t v = (int32_t)__builtin_rintf(__fdiv_rn(load_g(r + j), s)) + zm;
+    v = min(127, max(-128, v));
+    out[j] = (int8_t)v;
+  }
+  if (threadIdx.x == 0) {
+    s_act[m] = s;
+    z[m] = zm;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                               int64_t ldq, float* s_act, int32_t* z, hipStream_t s) {
+  hipLaunchKernelGGL(quant_kernel, dim3((unsigned)M), dim3(kQuantBlock), 0, s, x, K, ldx, q, ldq,
+                     s_act, z);
+  return hipGetLastError();
+}
+
+}  // namespace tern

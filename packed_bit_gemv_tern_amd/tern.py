@@ -31,7 +31,7 @@ TERN_HEAD_MAX_K = 43803
 EXPORTS = (
     "tern_row_bytes", "tern_pack", "tern_unpack", "tern_validate", "tern_gemv",
     "tern_gemm_smallM", "tern_linear_stack_workspace_bytes", "tern_linear_stack_prepare",
-    "tern_linear_stack", "tern_head_rowsum", "tern_head_gemv", "tern_read_probe",
+    "tern_linear_stack", "tern_quantize_act", "tern_head_rowsum", "tern_head_gemv", "tern_read_probe",
     "tern_status_string", "tern_last_hip_error",
 )
 
@@ -95,6 +95,7 @@ def _declare(lib):
         "tern_linear_stack_prepare": (i32, [ctypes.POINTER(tern_linear_desc), i64, i64, i32,
                                             vp, i64, ctypes.POINTER(tern_stack_plan), vp]),
         "tern_linear_stack": (i32, [ctypes.POINTER(tern_stack_plan), vp]),
+        "tern_quantize_act": (i32, [vp, i64, i64, i64, vp, i64, vp, vp, vp]),
         "tern_head_rowsum": (i32, [vp, i64, i64, i64, vp, vp]),
         "tern_head_gemv": (i32, [vp, vp, vp, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, vp]),
         "tern_read_probe": (i32, [vp, i64, vp, i32, i32, i32, vp]),
@@ -164,6 +165,11 @@ def tern_gemm_smallM(packed, s_row, rowsum, N, K, M, q, ldq, s_act, z, y, ldy, a
     _check(_lib().tern_gemm_smallM(_ptr(packed), _ptr(s_row), _ptr(rowsum), N, K, M, _ptr(q), ldq,
                                    _ptr(s_act), _ptr(z), _ptr(y), ldy, _ptr(acc), int(path),
                                    _stream(stream)), "tern_gemm_smallM")
+
+
+def tern_quantize_act(x, M, K, ldx, q, ldq, s_act, z, stream=None):
+    _check(_lib().tern_quantize_act(_ptr(x), M, K, ldx, _ptr(q), ldq, _ptr(s_act), _ptr(z),
+                                    _stream(stream)), "tern_quantize_act")
 
 
 def tern_head_rowsum(W, N, K, ldw, rowsum, stream=None):
