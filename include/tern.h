@@ -210,6 +210,41 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
 int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream);
 
 /*
+ * Block-wise scales along K.  The article ("What's actually ternary")
+ * groups each row's weights into fixed-size blocks along the input
+ * dimension, each block with its own higher-precision scale; one scale per
+ * row (the calls above) is the coarsest case.  With block size B, block b of
+ * a row holds columns [b*B, min((b+1)*B, K)), nb = ceil(K / B), and for one
+ * token
+ *     acc_b = sum_{j in b} w_ij q_j - z * rowsum_b[i][b]          (int32, exact)
+ *     y_i   = (sum_b s_b[i][b] * acc_b) * s_act                    (fp32)
+ * The fp32 sum over blocks is taken in the kernel's own order: it differs
+ * from any other order by rounding only, within
+ * (nb + 1) * 2^-24 * |s_act| * sum_b |s_b[i][b] * acc_b|.
+ * Weights use the packed layout above; B is a power of two in [64, 4096]
+ * and K <= TERN_BLOCK_MAX_K.  Metadata rows have stride nb.
+ */
+#define TERN_BLOCK_MAX_K 16384
+
+/*
+ * tern_block_rowsum -- load-time block row sums from packed weights.
+ *   rowsum_b  device, N x nb int32 (written).
+ */
+int tern_block_rowsum(const uint8_t* packed, int64_t N, int64_t K, int64_t B, int32_t* rowsum_b,
+                      hipStream_t stream);
+
+/*
+ * tern_gemv_blocked -- one token against block-scaled packed weights.
+ *   packed    device, N rows of tern_row_bytes(K) bytes, 16-byte aligned;
+ *   s_b       device, N x nb floats;  rowsum_b  device, N x nb int32;
+ *   q         device, K int8 (16-byte aligned);  s_act, z  device, one each;
+ *   y         device, N floats (written).
+ */
+int tern_gemv_blocked(const uint8_t* packed, const float* s_b, const int32_t* rowsum_b, int64_t N,
+                      int64_t K, int64_t B, const int8_t* q, const float* s_act, const int32_t* z,
+                      float* y, hipStream_t stream);
+
+/*
  * tern_quantize_act -- per-token asymmetric int8 activations for the calls
  * above (they take x_j = s_act * (q_j - z)).  The pages do not describe the
  * activation quantiser; this is the plainest reading, the token's range

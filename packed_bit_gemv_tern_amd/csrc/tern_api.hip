@@ -195,6 +195,39 @@ int tern_gemv(const uint8_t* packed, const float* s_row, const int32_t* rowsum, 
                           TERN_PATH_AUTO, stream);
 }
 
+static bool block_size_ok(int64_t B) {
+  return B >= 64 && B <= 4096 && (B & (B - 1)) == 0;
+}
+
+int tern_block_rowsum(const uint8_t* packed, int64_t N, int64_t K, int64_t B, int32_t* rowsum_b,
+                      hipStream_t stream) {
+  if (N < 0 || K < 1 || !block_size_ok(B)) return TERN_ERR_INVALID_ARG;
+  if (K > TERN_BLOCK_MAX_K || N > kI32Max) return TERN_ERR_RANGE;
+  if (N == 0) return TERN_OK;
+  if (!packed || !rowsum_b) return TERN_ERR_INVALID_ARG;
+  if (!aligned(packed, 16) || !aligned(rowsum_b, 4)) return TERN_ERR_ALIGNMENT;
+  const hipError_t e = launch_block_rowsum(packed, N, K, B, rowsum_b, stream);
+  return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
+int tern_gemv_blocked(const uint8_t* packed, const float* s_b, const int32_t* rowsum_b, int64_t N,
+                      int64_t K, int64_t B, const int8_t* q, const float* s_act, const int32_t* z,
+                      float* y, hipStream_t stream) {
+  if (N < 0 || K < 1 || !block_size_ok(B)) return TERN_ERR_INVALID_ARG;
+  if (K > TERN_BLOCK_MAX_K || N > kI32Max) return TERN_ERR_RANGE;
+  if (N == 0) return TERN_OK;
+  if (!packed || !s_b || !rowsum_b || !q || !s_act || !z || !y) return TERN_ERR_INVALID_ARG;
+  if (!aligned(packed, 16) || !aligned(q, 16)) return TERN_ERR_ALIGNMENT;
+  if (!aligned(s_b, 4) || !aligned(rowsum_b, 4) || !aligned(s_act, 4) || !aligned(z, 4) || !aligned(y, 4))
+    return TERN_ERR_ALIGNMENT;
+  const int cus = device_cus();
+  if (cus <= 0) return hip_fail(hipErrorNoDevice);
+  const int64_t waves = (N + blocked_rows_per_wave(K) - 1) / blocked_rows_per_wave(K);
+  const int64_t blocks = std::min<int64_t>((waves + 3) / 4, 4 * (int64_t)cus);
+  const hipError_t e = launch_blocked_gemv(packed, s_b, rowsum_b, N, K, B, q, s_act, z, y, (int)blocks, stream);
+  return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
 int tern_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
                       float* s_act, int32_t* z, hipStream_t stream) {
   if (M < 0 || K < 1 || ldx < K || ldq < K) return TERN_ERR_INVALID_ARG;

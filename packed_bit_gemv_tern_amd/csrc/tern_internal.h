@@ -127,6 +127,13 @@ hipError_t launch_head(const int8_t* W, const float* s_row, const int32_t* rowsu
                        hipStream_t s);
 hipError_t launch_head_rowsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw, int32_t* rowsum,
                               hipStream_t s);
+// one token against block-scaled ternary weights (tern_block.hip)
+int blocked_rows_per_wave(int64_t K);
+hipError_t launch_blocked_gemv(const uint8_t* packed, const float* s_b, const int32_t* rowsum_b, int64_t N,
+                               int64_t K, int64_t B, const int8_t* q, const float* s_act, const int32_t* z,
+                               float* y, int grid_blocks, hipStream_t s);
+hipError_t launch_block_rowsum(const uint8_t* packed, int64_t N, int64_t K, int64_t B, int32_t* rowsum_b,
+                               hipStream_t s);
 // per-token asymmetric int8 quantisation of activations (tern_quant.hip)
 hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                int64_t ldq, float* s_act, int32_t* z, hipStream_t s);

@@ -24,6 +24,7 @@ TERN_ERR_HIP = 6
 TERN_PATH_AUTO, TERN_PATH_VALU, TERN_PATH_MFMA = 0, 1, 2
 TERN_MAX_K = 5600000
 TERN_VALU_MAX_M = 8
+TERN_BLOCK_MAX_K = 16384
 TERN_HEAD_MAX_M = 8
 TERN_HEAD_MAX_K = 43803
 
@@ -31,7 +32,8 @@ TERN_HEAD_MAX_K = 43803
 EXPORTS = (
     "tern_row_bytes", "tern_pack", "tern_unpack", "tern_validate", "tern_gemv",
     "tern_gemm_smallM", "tern_linear_stack_workspace_bytes", "tern_linear_stack_prepare",
-    "tern_linear_stack", "tern_quantize_act", "tern_head_rowsum", "tern_head_gemv", "tern_read_probe",
+    "tern_linear_stack", "tern_block_rowsum", "tern_gemv_blocked", "tern_quantize_act",
+    "tern_head_rowsum", "tern_head_gemv", "tern_read_probe",
     "tern_status_string", "tern_last_hip_error",
 )
 
@@ -95,6 +97,8 @@ def _declare(lib):
         "tern_linear_stack_prepare": (i32, [ctypes.POINTER(tern_linear_desc), i64, i64, i32,
                                             vp, i64, ctypes.POINTER(tern_stack_plan), vp]),
         "tern_linear_stack": (i32, [ctypes.POINTER(tern_stack_plan), vp]),
+        "tern_block_rowsum": (i32, [vp, i64, i64, i64, vp, vp]),
+        "tern_gemv_blocked": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp]),
         "tern_quantize_act": (i32, [vp, i64, i64, i64, vp, i64, vp, vp, vp]),
         "tern_head_rowsum": (i32, [vp, i64, i64, i64, vp, vp]),
         "tern_head_gemv": (i32, [vp, vp, vp, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, vp]),
@@ -165,6 +169,16 @@ def tern_gemm_smallM(packed, s_row, rowsum, N, K, M, q, ldq, s_act, z, y, ldy, a
     _check(_lib().tern_gemm_smallM(_ptr(packed), _ptr(s_row), _ptr(rowsum), N, K, M, _ptr(q), ldq,
                                    _ptr(s_act), _ptr(z), _ptr(y), ldy, _ptr(acc), int(path),
                                    _stream(stream)), "tern_gemm_smallM")
+
+
+def tern_block_rowsum(packed, N, K, B, rowsum_b, stream=None):
+    _check(_lib().tern_block_rowsum(_ptr(packed), N, K, B, _ptr(rowsum_b), _stream(stream)),
+           "tern_block_rowsum")
+
+
+def tern_gemv_blocked(packed, s_b, rowsum_b, N, K, B, q, s_act, z, y, stream=None):
+    _check(_lib().tern_gemv_blocked(_ptr(packed), _ptr(s_b), _ptr(rowsum_b), N, K, B, _ptr(q),
+                                    _ptr(s_act), _ptr(z), _ptr(y), _stream(stream)), "tern_gemv_blocked")
 
 
 def tern_quantize_act(x, M, K, ldx, q, ldq, s_act, z, stream=None):
