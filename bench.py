@@ -19,8 +19,10 @@ kernels run on; ``cpu_baseline`` is the CPU oracle on a bounded sample.
 each: the single 256 x 512 GEMV; one 8B layer at M = 1 per linear and per
 layer (eight rotating copies, 390 MB, more than the 256 MB Infinity Cache);
 the 0.6B stack as seven M = 1 passes per step (three rotating copies, and
-warm); and the prefill sweep M = 1 .. 512 on one 8B layer (eight copies).
-Each line carries the oracle timed on a bounded sample of the same workload.
+warm); the prefill sweep M = 1 .. 512 on one 8B layer (eight copies); the
+int8 output head (151,936 x 4,096) at M = 1 and 8; block-wise scales on the
+8B's stacked gate projections; and the activation quantiser.  Each line
+carries the oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -328,6 +330,96 @@ def suite(args):
                   "fraction is claimed for them",
           "cpu_oracle": {"GBps": round(ogb, 4), "us_per_pass": round(ous, 1), "cores": cores,
                          "reps": oreps}})
+    del b06, st06
+    torch.cuda.empty_cache()
+
+    def oracle_time(fn, seconds):
+        t, reps = 0.0, 0
+        while t < seconds:
+            t0 = time.perf_counter()
+            fn()
+            t += time.perf_counter() - t0
+            reps += 1
+        return t / reps, reps
+
+    # --- the int8 output head (151,936 x 4,096), M = 1 and 8
+    W, s_row_h = synth.make_head(0)
+    N, K = W.shape
+    Wd = torch.from_numpy(W).to(dev)
+    srh = torch.from_numpy(s_row_h).to(dev)
+    rsh = torch.empty(N, dtype=torch.int32, device=dev)
+    tern.tern_head_rowsum(Wd, N, K, K, rsh)
+    rows = np.arange(0, N, N // 256)[:256]
+    Ws = np.ascontiguousarray(W[rows])
+    ors = oracle.head_rowsum(Ws, lib=olib)
+    for M in (1, 8):
+        qq, sa, zz = synth.make_activations(0, 36, 7, K, M)
+        qd, sad, zd = (torch.from_numpy(a).to(dev) for a in (qq, sa, zz))
+        yd = torch.empty((M, N), dtype=torch.float32, device=dev)
+        us = _event_times(lambda i: tern.tern_head_gemv(Wd, srh, rsh, N, K, K, M, qd, K, sad, zd, yd, N), 48)
+        hb = N * K + 8 * N + M * K + 8 * M + 4 * M * N
+        ot, oreps = oracle_time(lambda: oracle.head(Ws, s_row_h[rows], ors, qq, sa, zz, lib=olib), 2.0)
+        sb = len(rows) * K + 8 * len(rows) + M * K + 8 * M + 4 * M * len(rows)
+        emit({"suite": "head8b", "workload": "int8 output head 151,936 x 4,096 (one scale per row), "
+              "M = %d" % M, "M": M, "kernel": "head_kernel<%d>" % (1 if M == 1 else 8),
+              **_stats(us, hb),
+              "cpu_oracle": {"GBps": round(sb / ot / 1e9, 4), "cores": cores, "reps": oreps,
+                             "sample": "256 rows"}})
+    del Wd, srh, rsh, W
+    torch.cuda.empty_cache()
+
+    # --- block-wise scales: the 8B's 36 gate projections stacked (442,368 x 4,096)
+    specs8 = [s_ for s_ in synth.stack_specs("8b") if s_[2] == "gate"]
+    K = specs8[0][4]
+    N = sum(s_[3] for s_ in specs8)
+    ld = tern.tern_row_bytes(K)
+    packed = torch.empty((N, ld), dtype=torch.uint8, device=dev)
+    r0 = 0
+    for (layer, idx, name, n_, k_, p0) in specs8:
+        w, _ = synth.make_weights(0, layer, idx, n_, k_, p0)
+        rs_ = torch.empty(n_, dtype=torch.int32, device=dev)
+        tern.tern_pack(torch.from_numpy(w).to(dev), n_, k_, k_, packed[r0:r0 + n_], rs_)
+        r0 += n_
+    qq, sa, zz = synth.make_activations(0, 0, 4, K, 1)
+    qd, sad, zd = (torch.from_numpy(a).to(dev) for a in (qq.reshape(-1), sa, zz))
+    yd = torch.empty(N, dtype=torch.float32, device=dev)
+    w0, _ = synth.make_weights(0, 0, 4, 256, K, specs8[0][5])
+    opk, _, _ = oracle.pack(w0, lib=olib)
+    for B in (128, 1024):
+        nb = K // B
+        sbd = torch.from_numpy(np.random.default_rng([B, 1]).uniform(0.01, 0.1, (N, nb))
+                               .astype(np.float32)).to(dev)
+        rbd = torch.empty((N, nb), dtype=torch.int32, device=dev)
+        tern.tern_block_rowsum(packed, N, K, B, rbd)
+        us = _event_times(lambda i: tern.tern_gemv_blocked(packed, sbd, rbd, N, K, B, qd, sad, zd, yd), 48)
+        bb = N * ld + 8 * N * nb + K + 8 + 4 * N
+        s_o = sbd[:256].cpu().numpy()
+        r_o = oracle.block_rowsum(w0, B, lib=olib)
+        ot, oreps = oracle_time(lambda: oracle.linear_blocked(opk, s_o, r_o, K, B, qq, sa, zz, lib=olib), 2.0)
+        emit({"suite": "blocked", "workload": "8B gate projections stacked (442,368 x 4,096), "
+              "block scales every %d columns, M = 1" % B, "B": B, "kernel": "blocked_gemv_kernel<1>",
+              **_stats(us, bb),
+              "cpu_oracle": {"GBps": round((256 * ld + 8 * 256 * nb + K + 4 * 256) / ot / 1e9, 4),
+                             "cores": cores, "reps": oreps, "sample": "256 rows of layer 0's gate"}})
+        del sbd, rbd
+    del packed
+    torch.cuda.empty_cache()
+
+    # --- activation quantiser (launch-bound at decode sizes)
+    for M in (1, 8, 512):
+        x = np.random.default_rng([M, 5]).normal(0, 1, (M, 4096)).astype(np.float32)
+        xd = torch.from_numpy(x).to(dev)
+        qd = torch.empty((M, 4096), dtype=torch.int8, device=dev)
+        sd = torch.empty(M, dtype=torch.float32, device=dev)
+        zd = torch.empty(M, dtype=torch.int32, device=dev)
+        us = _event_times(lambda i: tern.tern_quantize_act(xd, M, 4096, 4096, qd, 4096, sd, zd), 100)
+        ot, oreps = oracle_time(lambda: oracle.quantize_act(x, lib=olib), 1.0)
+        st_ = _stats(us, 5 * M * 4096 + 8 * M)
+        if M < 512:
+            st_.pop("frac_of_peak")
+        emit({"suite": "quantize", "workload": "per-token int8 quantisation of M x 4,096 fp32 "
+              "activations, M = %d" % M, "M": M, "kernel": "quant_kernel", **st_,
+              "cpu_oracle": {"us": round(ot * 1e6, 2), "cores": cores, "reps": oreps}})
 
 
 def main():
@@ -342,8 +434,9 @@ def main():
     ap.add_argument("--only", choices=["m1", "m8"], default=None,
                     help="launch a single pass per step (for profiling)")
     ap.add_argument("--suite", action="store_true",
-                    help="measure the single GEMV, one 8B layer, the prefill sweep and the "
-                         "0.6B stack instead (one JSON line each)")
+                    help="measure the single GEMV, one 8B layer, the prefill sweep, the 0.6B "
+                         "stack, the int8 head, block scales and the quantiser instead (one JSON "
+                         "line each)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times "
                          "(reference for the HBM byte counters) and exit")
