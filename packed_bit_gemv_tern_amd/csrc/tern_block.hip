@@ -24,6 +24,8 @@
 // through range-checked buffer loads, as in the per-row M = 1 kernel.
 #include "tern_device.h"
 
+#include <type_traits>
+
 namespace tern {
 
 namespace {
@@ -38,7 +40,10 @@ __device__ __forceinline__ uint32_t udot4(uint32_t a, uint32_t b, uint32_t c) {
   return __builtin_amdgcn_udot4(a, b, c, false);
 }
 
-// value of the lane at distance D (same exchange as pair_sum)
+// Value of lane l ^ D.  The transposed steps below need exactly that lane:
+// the partner must agree with l in every other bit, so the half-mirror
+// exchange dpp_partner<4> (lane 7 - (l & 7)) is composed with a quad
+// reversal (l ^ 3) to give l ^ 4.
 template <int D>
 __device__ __forceinline__ uint32_t partner(uint32_t v) {
   if constexpr (D == 32) {
@@ -47,8 +52,11 @@ __device__ __forceinline__ uint32_t partner(uint32_t v) {
   } else if constexpr (D == 16) {
     auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
     return p[0] ^ p[1] ^ v;
+  } else if constexpr (D == 4) {
+    const uint32_t m = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x1B, 0xF, 0xF, false);
   } else {
-    return dpp_partner<D>(v);
+    return dpp_partner<D>(v);  // l ^ 8 (row_ror:8), l ^ 2, l ^ 1 (quad_perm)
   }
 }
 
@@ -63,16 +71,52 @@ __device__ __forceinline__ uint32_t group_sum_int(uint32_t v, int g) {
   return v;
 }
 
-// sum of one value per group over the 64 / g groups (every lane of a group
-// holds the same value)
-__device__ __forceinline__ float across_groups(float v, int g) {
-  if (g <= 1) v += __uint_as_float(partner<1>(__float_as_uint(v)));
-  if (g <= 2) v += __uint_as_float(partner<2>(__float_as_uint(v)));
-  if (g <= 4) v += __uint_as_float(partner<4>(__float_as_uint(v)));
-  if (g <= 8) v += __uint_as_float(partner<8>(__float_as_uint(v)));
-  if (g <= 16) v += __uint_as_float(partner<16>(__float_as_uint(v)));
-  if (g <= 32) v += __uint_as_float(partner<32>(__float_as_uint(v)));
-  return v;
+template <int D>
+__device__ __forceinline__ float fpartner(float v) {
+  return __uint_as_float(partner<D>(__float_as_uint(v)));
+}
+
+// Transposed butterfly step on floats: lanes with bit D clear keep
+// a + partner's a, lanes with bit D set keep b + partner's b.
+template <int D>
+__device__ __forceinline__ float fsplit(float a, float b, int lane) {
+  if constexpr (D == 32) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  } else if constexpr (D == 16) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  } else {
+    const bool hi = (lane & D) != 0;
+    return (hi ? b : a) + fpartner<D>(hi ? a : b);
+  }
+}
+
+// Sum over the 64 / G groups of U values per lane (each group of G lanes
+// holds the same U values), U * G <= 64: the first log2(U) levels split the
+// values (transposed), so lane l ends with the total of value
+// (l >> log2(G)) & (U - 1) and the wave does about one level per value
+// instead of six.
+template <int LG, int U>
+__device__ __forceinline__ float reduce_groups(float (&v)[U], int lane) {
+  constexpr int G = 1 << LG;
+  static_assert(U * G <= 64, "groups");
+  if constexpr (U == 4) {
+    v[0] = fsplit<G>(v[0], v[1], lane);
+    v[1] = fsplit<G>(v[2], v[3], lane);
+    v[0] = fsplit<2 * G>(v[0], v[1], lane);
+  } else if constexpr (U == 2) {
+    v[0] = fsplit<G>(v[0], v[1], lane);
+  }
+  constexpr int D0 = G * U;  // first plain level
+  float x = v[0];
+  if constexpr (D0 <= 1) x += fpartner<1>(x);
+  if constexpr (D0 <= 2) x += fpartner<2>(x);
+  if constexpr (D0 <= 4) x += fpartner<4>(x);
+  if constexpr (D0 <= 8) x += fpartner<8>(x);
+  if constexpr (D0 <= 16) x += fpartner<16>(x);
+  if constexpr (D0 <= 32) x += fpartner<32>(x);
+  return x;
 }
 
 struct BlkArgs {
@@ -91,13 +135,13 @@ struct BlkU {
   static constexpr int U = CPL == 1 ? 4 : CPL == 2 ? 2 : 1;
 };
 
-template <int CPL>
+template <int CPL, int LG>
 __global__ __launch_bounds__(kBlkBlock) void blocked_gemv_kernel(BlkArgs a) {
   constexpr int U = BlkU<CPL>::U;
+  constexpr int g = 1 << LG;
   const int lane = threadIdx.x & 63;
   const int gw = (int)blockIdx.x * kBlkWaves + (int)(threadIdx.x >> 6);
   const int nw = (int)gridDim.x * kBlkWaves;
-  const int g = a.g;
 
   // biased activations of the lane's chunks (zero past K) and each chunk's
   // block activation sum
@@ -157,10 +201,10 @@ __global__ __launch_bounds__(kBlkBlock) void blocked_gemv_kernel(BlkArgs a) {
       }
   };
   auto finish = [&](const Unit& c, int base) {
-    float yv[U];
+    float f[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float f = 0.0f;
+      f[u] = 0.0f;
 #pragma unroll
       for (int t = 0; t < CPL; ++t) {
         uint32_t p[4] = {0, 0, 0, 0};
@@ -172,19 +216,28 @@ __global__ __launch_bounds__(kBlkBlock) void blocked_gemv_kernel(BlkArgs a) {
           p[2] = udot4(x & kPlane2, qc[t][4 * d + 2], p[2]);
           p[3] = udot4(x & kPlane3, qc[t][4 * d + 3], p[3]);
         }
-        // sum c * qb of the chunk (plane k is 4^k-scaled)
+        // sum c * qb of the chunk (plane k is 4^k-scaled), then of the block
         const uint32_t sc = p[0] + (p[1] >> 2) + (p[2] >> 4) + (p[3] >> 6);
         const uint32_t sb = group_sum_int(sc, g);
         const int32_t accb = (int32_t)(sb - qbb[t] - zb * (uint32_t)c.r[u][t]);
-        f += __fmul_rn(c.s[u][t], (float)accb);  // zero for chunks past the row
+        f[u] += __fmul_rn(c.s[u][t], (float)accb);  // zero for chunks past the row
       }
-      yv[u] = across_groups(f, g);
     }
     const uint32_t rows = (uint32_t)min(U, a.N - base) * 4u;
     const auto ry = buffer_rsrc(a.y + base, rows);
+    if constexpr (U * g <= 64) {
+      // lane l holds row (l >> LG) & (U - 1); one lane per row stores
+      const float tot = reduce_groups<LG, U>(f, lane);
+      const bool writer = lane < U * g && (lane & (g - 1)) == 0;
+      buffer_store_u32(__float_as_uint(__fmul_rn(tot, sa)), ry, writer ? 4u * (uint32_t)(lane >> LG) : kDropOffset);
+    } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      buffer_store_u32(__float_as_uint(__fmul_rn(yv[u], sa)), ry, lane == 0 ? 4u * (uint32_t)u : kDropOffset);
+      for (int u = 0; u < U; ++u) {
+        float one[1] = {f[u]};
+        const float tot = reduce_groups<LG, 1>(one, lane);
+        buffer_store_u32(__float_as_uint(__fmul_rn(tot, sa)), ry, lane == 0 ? 4u * (uint32_t)u : kDropOffset);
+      }
+    }
   };
 
   const int step = nw * U;
@@ -245,12 +298,26 @@ hipError_t launch_blocked_gemv(const uint8_t* packed, const float* s_b, const in
   a.nb = (int32_t)((K + B - 1) / B);
   a.g = (int32_t)(B / 64);
   const int cpl = (a.nch + 63) / 64;
+  int lg = 0;
+  while ((1 << lg) < a.g) ++lg;
   const dim3 grid((unsigned)grid_blocks), block(kBlkBlock);
+  auto go = [&](auto cpl_c) {
+    constexpr int C = decltype(cpl_c)::value;
+    switch (lg) {
+      case 0: hipLaunchKernelGGL((blocked_gemv_kernel<C, 0>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((blocked_gemv_kernel<C, 1>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((blocked_gemv_kernel<C, 2>), grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((blocked_gemv_kernel<C, 3>), grid, block, 0, s, a); break;
+      case 4: hipLaunchKernelGGL((blocked_gemv_kernel<C, 4>), grid, block, 0, s, a); break;
+      case 5: hipLaunchKernelGGL((blocked_gemv_kernel<C, 5>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((blocked_gemv_kernel<C, 6>), grid, block, 0, s, a); break;
+    }
+  };
   switch (cpl) {
-    case 1: hipLaunchKernelGGL(blocked_gemv_kernel<1>, grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL(blocked_gemv_kernel<2>, grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL(blocked_gemv_kernel<3>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(blocked_gemv_kernel<4>, grid, block, 0, s, a); break;
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    default: go(std::integral_constant<int, 4>{}); break;
   }
   return hipGetLastError();
 }
