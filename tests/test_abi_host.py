@@ -158,3 +158,57 @@ def test_read_probe_argument_errors(lib):
     assert lib.tern_read_probe(A16, 1024, sink, 9, 8, 1, S) == tern.TERN_ERR_INVALID_ARG
     assert lib.tern_read_probe(A16, 1024, sink, 4, 5, 1, S) == tern.TERN_ERR_UNSUPPORTED
     assert lib.tern_read_probe(ODD, 1024, sink, 4, 8, 1, S) == tern.TERN_ERR_ALIGNMENT
+
+
+def head(lib, W=A16, s_row=A16, rowsum=A16, N=16, K=64, ldw=64, M=2, q=A16, ldq=64, s_act=A16,
+         z=A16, y=A16, ldy=16, acc=None):
+    return lib.tern_head_gemv(W, s_row, rowsum, N, K, ldw, M, q, ldq, s_act, z, y, ldy, acc, S)
+
+
+def test_head_argument_errors(lib):
+    assert head(lib, N=0) == tern.TERN_OK and head(lib, M=0) == tern.TERN_OK  # empty problems
+    assert head(lib, K=0) == tern.TERN_ERR_INVALID_ARG
+    assert head(lib, ldw=48) == tern.TERN_ERR_INVALID_ARG
+    assert head(lib, M=tern.TERN_HEAD_MAX_M + 1) == tern.TERN_ERR_UNSUPPORTED
+    assert head(lib, K=tern.TERN_HEAD_MAX_K + 1, ldw=tern.TERN_HEAD_MAX_K + 16) == tern.TERN_ERR_RANGE
+    assert head(lib, ldw=(1 << 28) + 16) == tern.TERN_ERR_RANGE
+    for field in ("W", "s_row", "rowsum", "q", "s_act", "z", "y"):
+        assert head(lib, **{field: None}) == tern.TERN_ERR_INVALID_ARG, field
+    assert head(lib, ldq=40) == tern.TERN_ERR_INVALID_ARG
+    assert head(lib, ldy=8) == tern.TERN_ERR_INVALID_ARG
+    assert head(lib, W=ODD) == tern.TERN_ERR_ALIGNMENT
+    assert head(lib, ldw=72) == tern.TERN_ERR_ALIGNMENT
+    assert head(lib, ldq=72) == tern.TERN_ERR_ALIGNMENT
+    assert head(lib, acc=A16 + 2) == tern.TERN_ERR_ALIGNMENT
+    assert lib.tern_head_rowsum(A16, 4, 64, 32, A16, S) == tern.TERN_ERR_INVALID_ARG   # ldw < K
+    assert lib.tern_head_rowsum(None, 4, 64, 64, A16, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_head_rowsum(A16, 0, 64, 64, None, S) == tern.TERN_OK
+
+
+def test_blocked_argument_errors(lib):
+    def blk(packed=A16, s_b=A16, rb=A16, N=4, K=256, B=128, q=A16, s_act=A16, z=A16, y=A16):
+        return lib.tern_gemv_blocked(packed, s_b, rb, N, K, B, q, s_act, z, y, S)
+    assert blk(N=0) == tern.TERN_OK
+    for B in (0, 32, 96, 192, 8192):
+        assert blk(B=B) == tern.TERN_ERR_INVALID_ARG, B
+    assert blk(K=tern.TERN_BLOCK_MAX_K + 1) == tern.TERN_ERR_RANGE
+    for field in ("packed", "s_b", "rb", "q", "s_act", "z", "y"):
+        assert blk(**{field: None}) == tern.TERN_ERR_INVALID_ARG, field
+    assert blk(packed=ODD) == tern.TERN_ERR_ALIGNMENT
+    assert blk(q=ODD) == tern.TERN_ERR_ALIGNMENT
+    assert blk(s_b=A16 + 2) == tern.TERN_ERR_ALIGNMENT
+    assert lib.tern_block_rowsum(A16, 4, 256, 100, A16, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_block_rowsum(A16, 4, tern.TERN_BLOCK_MAX_K + 1, 128, A16, S) == tern.TERN_ERR_RANGE
+
+
+def test_quantize_argument_errors(lib):
+    def qa(x=A16, M=2, K=64, ldx=64, q=A16, ldq=64, s=A16, z=A16):
+        return lib.tern_quantize_act(x, M, K, ldx, q, ldq, s, z, S)
+    assert qa(M=0) == tern.TERN_OK
+    assert qa(K=0) == tern.TERN_ERR_INVALID_ARG
+    assert qa(ldx=63) == tern.TERN_ERR_INVALID_ARG
+    assert qa(ldq=63) == tern.TERN_ERR_INVALID_ARG
+    for field in ("x", "q", "s", "z"):
+        assert qa(**{field: None}) == tern.TERN_ERR_INVALID_ARG, field
+    assert qa(x=A16 + 2) == tern.TERN_ERR_ALIGNMENT
+    assert qa(s=A16 + 1) == tern.TERN_ERR_ALIGNMENT
