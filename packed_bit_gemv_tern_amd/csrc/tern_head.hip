@@ -34,7 +34,7 @@ constexpr int kHeadWaves = kHeadBlock / 64;
 // rows per unit for MT tokens: U * MT values go through one 64-lane reduction
 template <int MT>
 struct HeadU {
-  static constexpr int U = MT == 1 ? 8 : MT == 2 ? 4 : MT == 4 ? 4 : 2;
+  static constexpr int U = MT == 1 ? 8 : 4;
 };
 
 struct HeadArgs {
