@@ -99,6 +99,18 @@ def _declare(lib):
         _p(ctypes.c_uint8), _p(ctypes.c_float), _p(i32), i64, i64, i64, i64,
         _p(ctypes.c_int8), i64, _p(ctypes.c_float), _p(i32),
         _p(ctypes.c_float), _p(ctypes.c_double), _p(ctypes.c_double), i64]
+    lib.oracle_row_bytes5.restype = i64
+    lib.oracle_row_bytes5.argtypes = [i64]
+    lib.oracle_pack5.restype = i64
+    lib.oracle_pack5.argtypes = [_p(ctypes.c_int8), i64, i64, i64,
+                                 _p(ctypes.c_uint8), _p(i32)]
+    lib.oracle_unpack5.restype = None
+    lib.oracle_unpack5.argtypes = [_p(ctypes.c_uint8), i64, i64, _p(ctypes.c_int8), i64]
+    lib.oracle_linear5.restype = ctypes.c_int
+    lib.oracle_linear5.argtypes = [
+        _p(ctypes.c_uint8), _p(ctypes.c_float), _p(i32), i64, i64, i64,
+        _p(ctypes.c_int8), i64, _p(ctypes.c_float), _p(i32),
+        _p(i32), _p(ctypes.c_float), _p(ctypes.c_double), i64]
     return lib
 
 
@@ -288,3 +300,53 @@ def linear_blocked(packed, s_b, rowsum_b, K, B, q, s_act, z, lib=None, check=Tru
     if check and st != OK:
         raise ValueError("oracle_linear_blocked status %d" % st)
     return y32, y64, yabs
+
+
+# ---- 1.6-bit rows (five weights per byte) ----
+
+def row_bytes5(K: int, lib=None) -> int:
+    return int((lib or load()).oracle_row_bytes5(int(K)))
+
+
+def pack5(w, lib=None):
+    """int8 (N, K) ternary matrix -> (1.6-bit rows uint8 (N, row_bytes5), rowsum int32 (N,), bad)."""
+    lib = lib or load()
+    w = _c(np.atleast_2d(w), np.int8)
+    N, K = w.shape
+    packed = np.empty((N, row_bytes5(K, lib)), np.uint8)
+    rowsum = np.empty(N, np.int32)
+    bad = lib.oracle_pack5(_ptr(w, ctypes.c_int8), N, K, K,
+                           _ptr(packed, ctypes.c_uint8), _ptr(rowsum, ctypes.c_int32))
+    return packed, rowsum, int(bad)
+
+
+def unpack5(packed, N: int, K: int, lib=None):
+    """1.6-bit rows -> int8 (N, K) weights (every byte decodes)."""
+    lib = lib or load()
+    packed = _c(packed, np.uint8)
+    assert packed.size == N * row_bytes5(K, lib)
+    w = np.empty((N, K), np.int8)
+    lib.oracle_unpack5(_ptr(packed, ctypes.c_uint8), N, K, _ptr(w, ctypes.c_int8), K)
+    return w
+
+
+def linear5(packed, s_row, rowsum, K, q, s_act, z, lib=None, check=True):
+    """The linear layer on 1.6-bit rows: acc (int32), y32, y64, each (M, N)."""
+    lib = lib or load()
+    q, s_act, z, M = _tokens(q, s_act, z, K)
+    packed = _c(packed, np.uint8)
+    s_row = _c(s_row, np.float32).reshape(-1)
+    rowsum = _c(rowsum, np.int32).reshape(-1)
+    N = s_row.shape[0]
+    assert rowsum.shape[0] == N and packed.size == N * row_bytes5(K, lib)
+    acc = np.empty((M, N), np.int32)
+    y32 = np.empty((M, N), np.float32)
+    y64 = np.empty((M, N), np.float64)
+    st = lib.oracle_linear5(_ptr(packed, ctypes.c_uint8), _ptr(s_row, ctypes.c_float),
+                            _ptr(rowsum, ctypes.c_int32), N, K, M, _ptr(q, ctypes.c_int8), K,
+                            _ptr(s_act, ctypes.c_float), _ptr(z, ctypes.c_int32),
+                            _ptr(acc, ctypes.c_int32), _ptr(y32, ctypes.c_float),
+                            _ptr(y64, ctypes.c_double), N)
+    if check and st != OK:
+        raise ValueError("oracle_linear5 status %d" % st)
+    return acc, y32, y64

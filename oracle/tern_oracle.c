@@ -399,3 +399,119 @@ int oracle_linear_blocked(const uint8_t* packed, const float* s_b,
   }
   return status;
 }
+
+/* ====================== 1.6-bit rows: five weights per byte ======================
+ *
+ * Three states hold log2(3), about 1.58 bits, per weight (article
+ * "Neutrino-1: quantization is a training decision, not a deployment one",
+ * "Where the bytes go"), so 2-bit fields leave a fifth of every row unused.
+ * This second layout (this project's own, like the 2-bit one) stores five
+ * weights per byte:
+ *  - a byte's five weights, as digits d = w + 1 in {0, 1, 2}, form the
+ *    base-3 number v = 81 d0 + 27 d1 + 9 d2 + 3 d3 + d4  (0 <= v <= 242);
+ *  - the byte stored is b = ceil(256 v / 243); it is read back as
+ *    v = floor(243 b / 256), which every byte value decodes to, so no byte
+ *    is invalid (13 values are simply never written);
+ *  - a row takes row_bytes5(K) = 16 * ceil(K / 80) bytes (80 weights per
+ *    16-byte chunk), so rows start 16-byte aligned;
+ *  - weight j of a row is digit (j % 20) / 4 of byte 4 * (j / 20) + j % 4:
+ *    a 4-byte word holds 20 weights, its digit i of bytes 0..3 being
+ *    weights 4i..4i+3 of the word;
+ *  - columns j >= K are padding and hold weight 0, so a byte made only of
+ *    padding holds v = 121 and reads 0x80.
+ * The layer itself is the one above: the same acc, y32 and y64.
+ */
+int64_t oracle_row_bytes5(int64_t K) { return 16 * ((K + 79) / 80); }
+
+static const unsigned kPlace5[5] = {81u, 27u, 9u, 3u, 1u}; /* value of digit i */
+
+static int64_t byte5_of(int64_t j) { return 4 * (j / 20) + j % 4; }
+static int digit5_of(int64_t j) { return (int)((j % 20) / 4); }
+
+/* The weight in column j of a 1.6-bit row. */
+static int read_weight5(const uint8_t* row, int64_t j) {
+  unsigned v = (243u * row[byte5_of(j)]) / 256u;
+  return (int)((v / kPlace5[digit5_of(j)]) % 3u) - 1;
+}
+
+/*
+ * Pack an N x K int8 matrix (row stride ldw elements) with entries in
+ * {-1, 0, +1} into 1.6-bit rows; rowsum[i] = sum_j w_ij.  Entries outside
+ * {-1, 0, +1} are counted (the return value), stored as 0 and left out of
+ * the row sum.
+ */
+int64_t oracle_pack5(const int8_t* w, int64_t N, int64_t K, int64_t ldw,
+                     uint8_t* packed, int32_t* rowsum) {
+  const int64_t ld = oracle_row_bytes5(K);
+  int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+  for (int64_t i = 0; i < N; ++i) {
+    uint8_t* row = packed + i * ld;
+    int64_t sum = 0;
+    for (int64_t p = 0; p < ld; ++p) {
+      unsigned v = 0;
+      for (int d = 0; d < 5; ++d) {
+        /* the column whose weight is digit d of byte p */
+        int64_t j = 20 * (p / 4) + 4 * d + p % 4;
+        int wv = 0;
+        if (j < K) {
+          wv = w[i * ldw + j];
+          if (wv < -1 || wv > 1) {
+            ++bad;
+            wv = 0;
+          }
+          sum += wv;
+        }
+        v += (unsigned)(wv + 1) * kPlace5[d];
+      }
+      row[p] = (uint8_t)((256u * v + 242u) / 243u); /* ceil(256 v / 243) */
+    }
+    rowsum[i] = (int32_t)sum;
+  }
+  return bad;
+}
+
+/* 1.6-bit rows back to int8 weights (row stride ldw elements). */
+void oracle_unpack5(const uint8_t* packed, int64_t N, int64_t K, int8_t* w,
+                    int64_t ldw) {
+  const int64_t ld = oracle_row_bytes5(K);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < N; ++i)
+    for (int64_t j = 0; j < K; ++j) w[i * ldw + j] = (int8_t)read_weight5(packed + i * ld, j);
+}
+
+/*
+ * The linear layer on 1.6-bit rows: the same outputs, status and rounding
+ * as oracle_linear (acc exact in int64 and within +-2^24; y32 two rounded
+ * products (s_row * acc) * s_act).
+ */
+int oracle_linear5(const uint8_t* packed, const float* s_row,
+                   const int32_t* rowsum, int64_t N, int64_t K, int64_t M,
+                   const int8_t* q, int64_t ldq, const float* s_act,
+                   const int32_t* z, int32_t* acc, float* y32, double* y64,
+                   int64_t ldy) {
+  const int64_t ld = oracle_row_bytes5(K);
+  const int64_t limit = (int64_t)1 << 24;
+  int status = ORACLE_OK;
+#pragma omp parallel for schedule(static) collapse(2)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t i = 0; i < N; ++i) {
+      const uint8_t* row = packed + i * ld;
+      int64_t dot = 0;
+      for (int64_t j = 0; j < K; ++j)
+        dot += (int64_t)read_weight5(row, j) * (int64_t)q[m * ldq + j];
+      const int64_t a = dot - (int64_t)rowsum[i] * (int64_t)z[m];
+      if (a >= limit || a <= -limit) {
+#pragma omp critical
+        if (status == ORACLE_OK) status = ORACLE_OVERFLOW;
+      }
+      if (acc) acc[m * ldy + i] = (int32_t)a;
+      if (y64) y64[m * ldy + i] = (double)s_row[i] * (double)a * (double)s_act[m];
+      if (y32) {
+        float prod = s_row[i] * (float)a; /* exact conversion, then round */
+        y32[m * ldy + i] = prod * s_act[m];
+      }
+    }
+  }
+  return status;
+}

@@ -126,3 +126,55 @@ def test_neighbour_pins_catch_mutant(name, tmp_path, monkeypatch):
         except BaseException:
             caught += 1
     assert caught, "no pin caught mutant %s" % name
+
+
+# ---- the 1.6-bit layout (five weights per byte) ----
+
+from test_oracle_packed5 import PACK5_CHECKS  # noqa: E402
+
+PACK5_MUTANTS = {
+    "pack5_digit_order_reversed": ("v += (unsigned)(wv + 1) * kPlace5[d];",
+                                   "v += (unsigned)(wv + 1) * kPlace5[4 - d];"),
+    "pack5_rounds_down": ("row[p] = (uint8_t)((256u * v + 242u) / 243u);",
+                          "row[p] = (uint8_t)((256u * v) / 243u);"),
+    "pack5_padding_minus_one": ("        int wv = 0;\n        if (j < K) {",
+                                "        int wv = -1;\n        if (j < K) {"),
+    "pack5_rowsum_skips_minus": ("          sum += wv;\n", "          sum += (wv > 0) ? wv : 0;\n"),
+    "decode5_rounds_up": ("unsigned v = (243u * row[byte5_of(j)]) / 256u;",
+                          "unsigned v = (243u * row[byte5_of(j)] + 255u) / 256u;"),
+    "layout5_bytes_swapped": ("static int64_t byte5_of(int64_t j) { return 4 * (j / 20) + j % 4; }",
+                              "static int64_t byte5_of(int64_t j) { return 4 * (j / 20) + 3 - j % 4; }"),
+    "pack5_column_map_transposed": ("int64_t j = 20 * (p / 4) + 4 * d + p % 4;",
+                                    "int64_t j = 20 * (p / 4) + 5 * (p % 4) + d;"),
+    "linear5_zero_point_dropped": ("const int64_t a = dot - (int64_t)rowsum[i] * (int64_t)z[m];",
+                                   "const int64_t a = dot;"),
+    "linear5_epilogue_order": ("float prod = s_row[i] * (float)a; /* exact conversion, then round */\n"
+                               "        y32[m * ldy + i] = prod * s_act[m];",
+                               "float prod = (float)a * s_act[m];\n"
+                               "        y32[m * ldy + i] = prod * s_row[i];"),
+    "linear5_overflow_unchecked": ("      if (a >= limit || a <= -limit) {\n#pragma omp critical\n"
+                                   "        if (status == ORACLE_OK) status = ORACLE_OVERFLOW;",
+                                   "      if (0) {\n#pragma omp critical\n"
+                                   "        if (status == ORACLE_OK) status = ORACLE_OVERFLOW;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PACK5_MUTANTS))
+def test_packed5_pins_catch_mutant(name, tmp_path):
+    old, new = PACK5_MUTANTS[name]
+    with open(oracle._SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, "mutation anchor not found once: %s" % name
+    path = os.path.join(str(tmp_path), "mutant.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.load(oracle.build(force=True, src=path, out=os.path.join(str(tmp_path), "libmut.so")))
+    caught = []
+    for check in PACK5_CHECKS:
+        try:
+            check(lib)
+        except (KeyboardInterrupt, SystemExit):
+            raise
+        except BaseException:
+            caught.append(check.__name__)
+    assert caught, "no pin caught mutant %s" % name
