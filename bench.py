@@ -35,6 +35,10 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+# vector ALU lane-operations per second: 256 CUs x 64 lanes per clock (four
+# SIMD16 units) x 2.4 GHz; the fp32 vector peak of 157.3 TFLOP/s is this
+# times 2 (FMA) times 2 (packed fp32)
+VALU_LANE_OPS_PER_S = 256 * 64 * 2.4e9
 
 
 def log(*a):
@@ -403,6 +407,52 @@ def suite(args):
                              "cores": cores, "reps": oreps, "sample": "256 rows of layer 0's gate"}})
         del sbd, rbd
     del packed
+    torch.cuda.empty_cache()
+
+    # --- 1.6-bit rows against 2-bit rows: the same 36 stacked 8B gate
+    # projections (442,368 x 4,096), one M = 1 call each
+    N5 = sum(s_[3] for s_ in specs8)
+    ld2, ld5 = tern.tern_row_bytes(K), tern.tern_row_bytes5(K)
+    p2 = torch.empty((N5, ld2), dtype=torch.uint8, device=dev)
+    p5 = torch.empty((N5, ld5), dtype=torch.uint8, device=dev)
+    rs5 = torch.empty(N5, dtype=torch.int32, device=dev)
+    sr5 = torch.empty(N5, dtype=torch.float32, device=dev)
+    r0 = 0
+    for (layer, idx, name, n_, k_, p0) in specs8:
+        w, sr_ = synth.make_weights(0, layer, idx, n_, k_, p0)
+        wd = torch.from_numpy(w).to(dev)
+        tern.tern_pack(wd, n_, k_, k_, p2[r0:r0 + n_], rs5[r0:r0 + n_])
+        tern.tern_pack5(wd, n_, k_, k_, p5[r0:r0 + n_], rs5[r0:r0 + n_])
+        sr5[r0:r0 + n_] = torch.from_numpy(sr_).to(dev)
+        r0 += n_
+    qq, sa, zz = synth.make_activations(0, 0, 4, K, 1)
+    qd, sad, zd = (torch.from_numpy(a).to(dev) for a in (qq.reshape(-1), sa, zz))
+    yd = torch.empty(N5, dtype=torch.float32, device=dev)
+    w0, s0 = synth.make_weights(0, 0, 4, 256, K, specs8[0][5])
+    weights = N5 * K
+    for label, ld_, fn, kern, ops in (
+            ("2-bit", ld2, lambda i: tern.tern_gemv(p2, sr5, rs5, N5, K, qd, sad, zd, yd),
+             "valu_linear_kernel", 0.5),
+            ("1.6-bit", ld5, lambda i: tern.tern_gemv5(p5, sr5, rs5, N5, K, qd, sad, zd, yd),
+             "gemv5_kernel<8, 2>", 26 / 20)):
+        us = _event_times(fn, 48)
+        st_ = _stats(us, N5 * ld_ + 8 * N5 + K + 8 + 4 * N5)
+        wps = weights / (st_["median_us"] * 1e-6)
+        if label == "2-bit":
+            o_pk, o_rs, _ = oracle.pack(w0, lib=olib)
+            ofn = lambda: oracle.linear(o_pk, s0, o_rs, K, qq, sa, zz, lib=olib)
+        else:
+            o_pk, o_rs, _ = oracle.pack5(w0, lib=olib)
+            ofn = lambda: oracle.linear5(o_pk, s0, o_rs, K, qq, sa, zz, lib=olib)
+        ot, oreps = oracle_time(ofn, 2.0)
+        emit({"suite": "packed5", "workload": "8B gate projections stacked (442,368 x 4,096) in "
+              "%s rows, M = 1" % label, "layout": label, "kernel": kern, **st_,
+              "weights_per_s": float("%.4g" % wps),
+              "valu_ops_per_weight": ops,
+              "frac_of_valu_peak": round(ops * wps / VALU_LANE_OPS_PER_S, 4),
+              "cpu_oracle": {"weights_per_s": float("%.4g" % (256 * K / ot)), "cores": cores,
+                             "reps": oreps, "sample": "256 rows of layer 0's gate"}})
+    del p2, p5, rs5, sr5, yd
     torch.cuda.empty_cache()
 
     # --- activation quantiser (launch-bound at decode sizes)

@@ -307,6 +307,47 @@ int tern_head_gemv(const int8_t* W, const float* s_row, const int32_t* rowsum, i
                    const int32_t* z, float* y, int64_t ldy, int32_t* acc, hipStream_t stream);
 
 /*
+ * The 1.6-bit layout.  Three states carry about 1.58 bits per weight
+ * (article "Neutrino-1: quantization is a training decision, not a
+ * deployment one", "Where the bytes go"), so this second layout (also the
+ * library's own) packs five weights per byte, 20 % fewer bytes per row:
+ *   - a byte's five weights, as digits d = w + 1 (most significant first),
+ *     form v = 81 d0 + 27 d1 + 9 d2 + 3 d3 + d4, stored as
+ *     b = ceil(256 v / 243) (read back as v = floor(243 b / 256); every byte
+ *     value decodes, 13 of them are never written);
+ *   - row i starts at packed5 + i * tern_row_bytes5(K); a row is
+ *     16 * ceil(K / 80) bytes (80 weights per 16-byte chunk);
+ *   - weight j is digit (j % 20) / 4 of byte 4 * (j / 20) + j % 4 of its row;
+ *   - columns j >= K are padding with weight 0 (a padding-only byte is 0x80);
+ *   - metadata as for the 2-bit layout: float s_row[N], int32 rowsum[N].
+ * The layer computed is the one at the top of this file.  Decoding costs
+ * about 1.3 VALU operations per weight here against 0.5 for 2-bit rows.
+ */
+#define TERN5_MAX_K 65520
+
+/* Bytes of one 1.6-bit row: 16 * ceil(K / 80); 0 for K < 1. */
+int64_t tern_row_bytes5(int64_t K);
+
+/*
+ * tern_pack5 -- load-time packing of an int8 ternary matrix into 1.6-bit
+ * rows; arguments as tern_pack, with rows of tern_row_bytes5(K) bytes and
+ * K <= TERN5_MAX_K.
+ */
+int tern_pack5(const int8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed5,
+               int32_t* rowsum, int32_t* bad_count, hipStream_t stream);
+
+/*
+ * tern_gemv5 -- one token (M = 1) against 1.6-bit rows; arguments as
+ * tern_gemv, with packed5 (16-byte aligned) holding N rows of
+ * tern_row_bytes5(K) bytes and 1 <= K <= TERN5_MAX_K.  rowsum must be the
+ * row sums of the packed weights (tern_pack5 writes them): the kernel takes
+ * the zero-point and bias terms from it.
+ */
+int tern_gemv5(const uint8_t* packed5, const float* s_row, const int32_t* rowsum, int64_t N,
+               int64_t K, const int8_t* q, const float* s_act, const int32_t* z, float* y,
+               int32_t* acc, hipStream_t stream);
+
+/*
  * tern_read_probe -- a measurement aid, not part of the method: reads `bytes`
  * bytes of `buf` (device, 16-byte aligned, bytes a multiple of 16) with the
  * same 16-byte loads and workgroup shape as the GEMV kernels and does nothing

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtern.so")
 SOURCES = ["tern_api.hip", "tern_pack.hip", "tern_valu.hip", "tern_mfma.hip", "tern_gemm.hip",
-           "tern_head.hip", "tern_quant.hip", "tern_block.hip", "tern_probe.hip"]
+           "tern_head.hip", "tern_quant.hip", "tern_block.hip", "tern_packed5.hip", "tern_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

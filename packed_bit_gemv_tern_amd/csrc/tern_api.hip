@@ -239,6 +239,34 @@ int tern_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t*
   return e == hipSuccess ? TERN_OK : hip_fail(e);
 }
 
+int64_t tern_row_bytes5(int64_t K) { return K < 1 ? 0 : 16 * ((K + 79) / 80); }
+
+int tern_pack5(const int8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed5,
+               int32_t* rowsum, int32_t* bad_count, hipStream_t stream) {
+  if (N < 0 || K < 1 || ldw < K) return TERN_ERR_INVALID_ARG;
+  if (K > TERN5_MAX_K || N > kI32Max) return TERN_ERR_RANGE;
+  if (bad_count && !aligned(bad_count, 4)) return TERN_ERR_ALIGNMENT;
+  if (bad_count) {
+    hipError_t e = launch_zero_i32(bad_count, 1, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (N == 0) return TERN_OK;
+  if (!w || !packed5 || !rowsum) return TERN_ERR_INVALID_ARG;
+  if (!aligned(packed5, 16) || !aligned(rowsum, 4)) return TERN_ERR_ALIGNMENT;
+  const hipError_t e = launch_pack5(w, N, K, ldw, packed5, rowsum, bad_count, stream);
+  return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
+int tern_gemv5(const uint8_t* packed5, const float* s_row, const int32_t* rowsum, int64_t N,
+               int64_t K, const int8_t* q, const float* s_act, const int32_t* z, float* y,
+               int32_t* acc, hipStream_t stream) {
+  if (K > TERN5_MAX_K) return TERN_ERR_RANGE;
+  const int st = check_linear(packed5, s_row, rowsum, N, K, 1, q, K, s_act, z, y, N, acc);
+  if (st != TERN_OK || N == 0) return st;
+  const hipError_t e = launch_gemv5(packed5, s_row, rowsum, N, K, q, s_act, z, y, acc, stream);
+  return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
 int tern_head_rowsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw, int32_t* rowsum,
                      hipStream_t stream) {
   if (N < 0 || K < 1 || ldw < K) return TERN_ERR_INVALID_ARG;

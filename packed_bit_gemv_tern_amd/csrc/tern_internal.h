@@ -135,6 +135,12 @@ hipError_t launch_blocked_gemv(const uint8_t* packed, const float* s_b, const in
 hipError_t launch_block_rowsum(const uint8_t* packed, int64_t N, int64_t K, int64_t B, int32_t* rowsum_b,
                                hipStream_t s);
 // per-token asymmetric int8 quantisation of activations (tern_quant.hip)
+int packed5_lanes_per_row(int64_t K);
+hipError_t launch_pack5(const int8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed,
+                        int32_t* rowsum, int32_t* bad, hipStream_t s);
+hipError_t launch_gemv5(const uint8_t* packed, const float* s_row, const int32_t* rowsum, int64_t N,
+                        int64_t K, const int8_t* q, const float* s_act, const int32_t* z, float* y,
+                        int32_t* acc, hipStream_t s);
 hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                int64_t ldq, float* s_act, int32_t* z, hipStream_t s);
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int grid, int unroll,

@@ -27,13 +27,15 @@ TERN_VALU_MAX_M = 8
 TERN_BLOCK_MAX_K = 16384
 TERN_HEAD_MAX_M = 8
 TERN_HEAD_MAX_K = 43803
+TERN5_MAX_K = 65520
 
 # Every function include/tern.h declares.
 EXPORTS = (
     "tern_row_bytes", "tern_pack", "tern_unpack", "tern_validate", "tern_gemv",
     "tern_gemm_smallM", "tern_linear_stack_workspace_bytes", "tern_linear_stack_prepare",
     "tern_linear_stack", "tern_block_rowsum", "tern_gemv_blocked", "tern_quantize_act",
-    "tern_head_rowsum", "tern_head_gemv", "tern_read_probe",
+    "tern_head_rowsum", "tern_head_gemv", "tern_row_bytes5", "tern_pack5", "tern_gemv5",
+    "tern_read_probe",
     "tern_status_string", "tern_last_hip_error",
 )
 
@@ -102,6 +104,9 @@ def _declare(lib):
         "tern_quantize_act": (i32, [vp, i64, i64, i64, vp, i64, vp, vp, vp]),
         "tern_head_rowsum": (i32, [vp, i64, i64, i64, vp, vp]),
         "tern_head_gemv": (i32, [vp, vp, vp, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, vp]),
+        "tern_row_bytes5": (i64, [i64]),
+        "tern_pack5": (i32, [vp, i64, i64, i64, vp, vp, vp, vp]),
+        "tern_gemv5": (i32, [vp, vp, vp, i64, i64, vp, vp, vp, vp, vp, vp]),
         "tern_read_probe": (i32, [vp, i64, vp, i32, i32, i32, vp]),
         "tern_status_string": (ctypes.c_char_p, [i32]),
         "tern_last_hip_error": (i32, []),
@@ -195,6 +200,20 @@ def tern_head_gemv(W, s_row, rowsum, N, K, ldw, M, q, ldq, s_act, z, y, ldy, acc
     _check(_lib().tern_head_gemv(_ptr(W), _ptr(s_row), _ptr(rowsum), N, K, ldw, M, _ptr(q), ldq,
                                  _ptr(s_act), _ptr(z), _ptr(y), ldy, _ptr(acc), _stream(stream)),
            "tern_head_gemv")
+
+
+def tern_row_bytes5(K: int) -> int:
+    return int(_lib().tern_row_bytes5(int(K)))
+
+
+def tern_pack5(w, N, K, ldw, packed5, rowsum, bad_count=None, stream=None):
+    _check(_lib().tern_pack5(_ptr(w), N, K, ldw, _ptr(packed5), _ptr(rowsum), _ptr(bad_count),
+                             _stream(stream)), "tern_pack5")
+
+
+def tern_gemv5(packed5, s_row, rowsum, N, K, q, s_act, z, y, acc=None, stream=None):
+    _check(_lib().tern_gemv5(_ptr(packed5), _ptr(s_row), _ptr(rowsum), N, K, _ptr(q), _ptr(s_act),
+                             _ptr(z), _ptr(y), _ptr(acc), _stream(stream)), "tern_gemv5")
 
 
 def tern_linear_stack_workspace_bytes(L: int, M: int) -> int:

@@ -212,3 +212,30 @@ def test_quantize_argument_errors(lib):
         assert qa(**{field: None}) == tern.TERN_ERR_INVALID_ARG, field
     assert qa(x=A16 + 2) == tern.TERN_ERR_ALIGNMENT
     assert qa(s=A16 + 1) == tern.TERN_ERR_ALIGNMENT
+
+
+def test_packed5_row_bytes_and_argument_errors(lib):
+    for K, ld in [(0, 0), (-1, 0), (1, 16), (80, 16), (81, 32), (4096, 832), (12288, 2464)]:
+        assert tern.tern_row_bytes5(K) == ld, K
+    assert lib.tern_pack5(A16, 4, 64, 63, A16, A16, None, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_pack5(A16, 4, 0, 64, A16, A16, None, S) == tern.TERN_ERR_INVALID_ARG
+    K5 = tern.TERN5_MAX_K + 1
+    assert lib.tern_pack5(A16, 4, K5, K5, A16, A16, None, S) == tern.TERN_ERR_RANGE
+    assert lib.tern_pack5(A16, 4, 64, 64, ODD, A16, None, S) == tern.TERN_ERR_ALIGNMENT
+    assert lib.tern_pack5(A16, 4, 64, 64, A16, A16 + 2, None, S) == tern.TERN_ERR_ALIGNMENT
+    assert lib.tern_pack5(A16, 4, 64, 64, A16, A16, A16 + 1, S) == tern.TERN_ERR_ALIGNMENT
+    assert lib.tern_pack5(None, 4, 64, 64, A16, A16, None, S) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_pack5(None, 0, 64, 64, None, None, None, S) == tern.TERN_OK
+
+    def g5(packed=A16, s_row=A16, rs=A16, N=8, K=100, q=A16, s_act=A16, z=A16, y=A16, acc=None):
+        return lib.tern_gemv5(packed, s_row, rs, N, K, q, s_act, z, y, acc, S)
+    assert g5(N=0) == tern.TERN_OK
+    assert g5(K=0) == tern.TERN_ERR_INVALID_ARG
+    assert g5(N=-1) == tern.TERN_ERR_INVALID_ARG
+    assert g5(K=tern.TERN5_MAX_K + 1) == tern.TERN_ERR_RANGE
+    for field in ("packed", "s_row", "rs", "q", "s_act", "z", "y"):
+        assert g5(**{field: None}) == tern.TERN_ERR_INVALID_ARG, field
+    assert g5(packed=ODD) == tern.TERN_ERR_ALIGNMENT
+    assert g5(q=ODD) == tern.TERN_ERR_ALIGNMENT
+    assert g5(y=A16 + 2) == tern.TERN_ERR_ALIGNMENT
+    assert g5(acc=A16 + 1) == tern.TERN_ERR_ALIGNMENT
