@@ -154,7 +154,8 @@ int tern_gemm_smallM(const uint8_t* packed, const float* s_row, const int32_t* r
                      int32_t* acc, int path, hipStream_t stream);
 
 /*
- * A stack of L independent linears evaluated by one persistent launch (the
+ * A stack of L independent linears evaluated by one kernel launch over a
+ * schedule made once by tern_linear_stack_prepare (the
  * 8B carries 252 such linears, seven per decoder layer, and the 0.6B 196:
  * article "What's actually ternary"; models page "The family").  Every linear
  * sees the same token count M; each has its own shapes and buffers (all
@@ -206,7 +207,7 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
                               void* workspace, int64_t workspace_bytes,
                               tern_stack_plan* plan, hipStream_t stream);
 
-/* tern_linear_stack -- one persistent launch over the prepared stack. */
+/* tern_linear_stack -- one launch over the prepared stack. */
 int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream);
 
 /*

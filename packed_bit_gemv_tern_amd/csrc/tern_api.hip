@@ -90,6 +90,13 @@ int device_cus() {
 constexpr int kStackBlock = 256;
 constexpr int kWavesPerBlock = kStackBlock / 64;
 constexpr int kMaxWavesPerCu = 32;  // 8 waves per SIMD x 4 SIMDs
+// The VALU stack kernels launch this many times the workgroups that fit on
+// the chip at once, each with 1/16 of a resident workgroup's share: the
+// dispatcher then starts a new workgroup wherever one finishes, which evens
+// out compute units and dispatch ranks that stream at different speeds (8B
+// stack at M = 1: 280 us with one workgroup per slot, 267 at 8x, 261 at
+// 16x, 270 at 32x).  The MFMA window kernel gained nothing from it.
+constexpr int kValuOversubscribe = 16;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -309,7 +316,7 @@ int64_t tern_linear_stack_workspace_bytes(int64_t L, int64_t M) {
   if (L < 0 || M < 0 || L > kI32Max) return 0;
   int cus = device_cus();
   if (cus <= 0) cus = 256;
-  const int64_t workers = (int64_t)cus * kMaxWavesPerCu;
+  const int64_t workers = (int64_t)cus * kMaxWavesPerCu * kValuOversubscribe;
   return layout_for(L, workers, workers + L).total;
 }
 
@@ -360,7 +367,7 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   int per_cu = p == TERN_PATH_VALU ? valu_stack_blocks_per_cu(kernel)
                                    : mfma_stack_blocks_per_cu(kernel - SK_MFMA);
   per_cu = std::min(per_cu, kMaxWavesPerCu / kWavesPerBlock);
-  int grid = cus * per_cu;
+  int grid = cus * per_cu * (p == TERN_PATH_VALU ? kValuOversubscribe : 1);
   grid = std::max(8, grid / 8 * 8);  // a multiple of 8 for the XCD-aware numbering
   // schedule entries belong to waves, or to whole workgroups for the
   // lockstep MFMA kernel
