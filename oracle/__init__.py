@@ -99,6 +99,9 @@ def _declare(lib):
         _p(ctypes.c_uint8), _p(ctypes.c_float), _p(i32), i64, i64, i64, i64,
         _p(ctypes.c_int8), i64, _p(ctypes.c_float), _p(i32),
         _p(ctypes.c_float), _p(ctypes.c_double), _p(ctypes.c_double), i64]
+    lib.oracle_quantize_weights.restype = None
+    lib.oracle_quantize_weights.argtypes = [_p(ctypes.c_float), i64, i64, i64, i64,
+                                            _p(ctypes.c_int8), i64, _p(ctypes.c_float)]
     lib.oracle_row_bytes5.restype = i64
     lib.oracle_row_bytes5.argtypes = [i64]
     lib.oracle_pack5.restype = i64
@@ -300,6 +303,19 @@ def linear_blocked(packed, s_b, rowsum_b, K, B, q, s_act, z, lib=None, check=Tru
     if check and st != OK:
         raise ValueError("oracle_linear_blocked status %d" % st)
     return y32, y64, yabs
+
+
+def quantize_weights(W, B, lib=None):
+    """fp32 (N, K) weights -> (states int8 (N, K), block scales fp32 (N, ceil(K / B)))."""
+    lib = lib or load()
+    W = _c(np.atleast_2d(W), np.float32)
+    N, K = W.shape
+    nb = (K + B - 1) // B
+    t = np.empty((N, K), np.int8)
+    s_b = np.empty((N, nb), np.float32)
+    lib.oracle_quantize_weights(_ptr(W, ctypes.c_float), N, K, K, int(B), _ptr(t, ctypes.c_int8), K,
+                                _ptr(s_b, ctypes.c_float))
+    return t, s_b
 
 
 # ---- 1.6-bit rows (five weights per byte) ----

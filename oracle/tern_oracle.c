@@ -515,3 +515,48 @@ int oracle_linear5(const uint8_t* packed, const float* s_row,
   }
   return status;
 }
+
+/* ====================== weight quantiser ======================
+ *
+ * The article ("What's actually ternary") states how a weight becomes a
+ * state: weights are grouped into fixed-size blocks along the input
+ * dimension, the block's scale is the mean absolute value of its weights,
+ * and each weight's state is the rounded, clamped ratio w / scale; one block
+ * for the whole row is the coarsest case.  The pages fix no precision or
+ * order for the mean, so it is defined here:
+ *
+ *     sum  = |w_0| + |w_1| + ... + |w_(n-1)|   in fp64, in column order
+ *     s_b  = fp32(sum / n)                     (n = the block's columns; the
+ *                                               last block may be shorter)
+ *     state_j = rint(clamp(w_j / s_b, -1, 1))  (fp32 division; rint rounds
+ *                                               half to even)
+ *
+ * A block of zeros has s_b = 0 and all states 0.  W holds N rows of K finite
+ * floats (row stride ldw); the states go to t (row stride ldt) and the
+ * scales to s_b (N x nb, nb = ceil(K / B)).
+ */
+void oracle_quantize_weights(const float* W, int64_t N, int64_t K, int64_t ldw, int64_t B,
+                             int8_t* t, int64_t ldt, float* s_b) {
+  const int64_t nb = (K + B - 1) / B;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < N; ++i) {
+    const float* row = W + i * ldw;
+    for (int64_t b = 0; b < nb; ++b) {
+      const int64_t j0 = b * B, j1 = (j0 + B < K) ? j0 + B : K;
+      double total = 0.0;
+      for (int64_t j = j0; j < j1; ++j) total += fabs((double)row[j]);
+      const float scale = (float)(total / (double)(j1 - j0));
+      s_b[i * nb + b] = scale;
+      for (int64_t j = j0; j < j1; ++j) {
+        float state = 0.0f;
+        if (scale > 0.0f) {
+          float ratio = row[j] / scale;
+          if (ratio > 1.0f) ratio = 1.0f;
+          if (ratio < -1.0f) ratio = -1.0f;
+          state = rintf(ratio);
+        }
+        t[i * ldt + j] = (int8_t)state;
+      }
+    }
+  }
+}

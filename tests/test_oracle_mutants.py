@@ -178,3 +178,41 @@ def test_packed5_pins_catch_mutant(name, tmp_path):
         except BaseException:
             caught.append(check.__name__)
     assert caught, "no pin caught mutant %s" % name
+
+
+# ---- the weight quantiser ----
+
+from test_oracle_wquant import WQUANT_CHECKS  # noqa: E402
+
+WQUANT_MUTANTS = {
+    "wquant_full_block_count": ("const float scale = (float)(total / (double)(j1 - j0));",
+                                "const float scale = (float)(total / (double)B);"),
+    "wquant_signed_sum": ("total += fabs((double)row[j]);", "total += (double)row[j];"),
+    "wquant_round_half_away": ("state = rintf(ratio);", "state = roundf(ratio);"),
+    "wquant_no_clamp": ("if (ratio > 1.0f) ratio = 1.0f;", "if (ratio > 9.0f) ratio = 1.0f;"),
+    "wquant_blocks_shifted": ("const int64_t j0 = b * B, j1 = (j0 + B < K) ? j0 + B : K;",
+                              "const int64_t j0 = b * B + (b > 0), j1 = (j0 + B < K) ? j0 + B : K;"),
+    "wquant_fp32_sum": ("double total = 0.0;\n      for (int64_t j = j0; j < j1; ++j) total += fabs((double)row[j]);",
+                        "float total = 0.0f;\n      for (int64_t j = j0; j < j1; ++j) total += fabsf(row[j]);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WQUANT_MUTANTS))
+def test_wquant_pins_catch_mutant(name, tmp_path):
+    old, new = WQUANT_MUTANTS[name]
+    with open(oracle._SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, "mutation anchor not found once: %s" % name
+    path = os.path.join(str(tmp_path), "mutant.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.load(oracle.build(force=True, src=path, out=os.path.join(str(tmp_path), "libmut.so")))
+    caught = []
+    for check in WQUANT_CHECKS:
+        try:
+            check(lib)
+        except (KeyboardInterrupt, SystemExit):
+            raise
+        except BaseException:
+            caught.append(check.__name__)
+    assert caught, "no pin caught mutant %s" % name
