@@ -455,6 +455,22 @@ def suite(args):
     del p2, p5, rs5, sr5, yd
     torch.cuda.empty_cache()
 
+    # --- weight quantiser (load time): one 8B gate projection, fp32 12,288 x 4,096
+    Nw, Kw, Bw = 12288, 4096, 128
+    Wf = (np.random.default_rng([1, 4, 7]).standard_normal((Nw, Kw)) * 0.02).astype(np.float32)
+    Wd = torch.from_numpy(Wf).to(dev)
+    td = torch.empty((Nw, Kw), dtype=torch.int8, device=dev)
+    sd = torch.empty((Nw, Kw // Bw), dtype=torch.float32, device=dev)
+    us = _event_times(lambda i: tern.tern_quantize_weights(Wd, Nw, Kw, Kw, Bw, td, Kw, sd), 20)
+    ot, oreps = oracle_time(lambda: oracle.quantize_weights(Wf[:256], Bw, lib=olib), 1.0)
+    emit({"suite": "quantize_weights", "workload": "ternarise one 8B gate projection (fp32 12,288 x 4,096), "
+          "block scales every %d columns (load time)" % Bw, "B": Bw, "kernel": "wquant_kernel",
+          **_stats(us, 5 * Nw * Kw + 4 * Nw * (Kw // Bw)),
+          "cpu_oracle": {"GBps": round((5 * 256 * Kw + 4 * 256 * (Kw // Bw)) / ot / 1e9, 4), "cores": cores,
+                         "reps": oreps, "sample": "256 rows"}})
+    del Wd, td, sd, Wf
+    torch.cuda.empty_cache()
+
     # --- activation quantiser (launch-bound at decode sizes)
     for M in (1, 8, 512):
         x = np.random.default_rng([M, 5]).normal(0, 1, (M, 4096)).astype(np.float32)

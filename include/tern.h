@@ -263,6 +263,24 @@ int tern_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t*
                       float* s_act, int32_t* z, hipStream_t stream);
 
 /*
+ * tern_quantize_weights -- load-time ternarisation of fp32 weights with one
+ * scale per block of B columns along K (article "What's actually ternary":
+ * the block's scale is its mean absolute weight, the state of a weight its
+ * rounded, clamped ratio to that scale; B >= K gives one scale per row):
+ *     s_b[i][b] = fp32( (sum of |W_ij| over the block, in fp64, in column
+ *                       order) / (the block's column count) )
+ *     w_ij      = rint(clamp(W_ij / s_b[i][b], -1, 1))   (fp32 division,
+ *                                                          half to even)
+ * A block of zeros gets scale 0 and states 0.  The states pack with
+ * tern_pack (and tern_block_rowsum) for tern_gemv_blocked.
+ *   W    device, N x K finite floats, row stride ldw >= K, 4-byte aligned;
+ *   w    device, N x K int8 states, row stride ldt >= K (written);
+ *   s_b  device, N x ceil(K / B) floats, row stride ceil(K / B) (written).
+ */
+int tern_quantize_weights(const float* W, int64_t N, int64_t K, int64_t ldw, int64_t B, int8_t* w,
+                          int64_t ldt, float* s_b, hipStream_t stream);
+
+/*
  * The int8 output head.  The token embedding and the output head are not
  * ternary: they stay int8 with one scale per row (Neutrino-1 8B model card,
  * "Where the bytes live"), because nothing sums their rounding errors away

@@ -141,6 +141,8 @@ hipError_t launch_pack5(const int8_t* w, int64_t N, int64_t K, int64_t ldw, uint
 hipError_t launch_gemv5(const uint8_t* packed, const float* s_row, const int32_t* rowsum, int64_t N,
                         int64_t K, const int8_t* q, const float* s_act, const int32_t* z, float* y,
                         int32_t* acc, hipStream_t s);
+hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, int64_t ldw, int64_t B,
+                                   int8_t* t, int64_t ldt, float* s_b, hipStream_t s);
 hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                int64_t ldq, float* s_act, int32_t* z, hipStream_t s);
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int grid, int unroll,

@@ -67,7 +67,46 @@ __global__ __launch_bounds__(kQuantBlock) void quant_kernel(const float* x, int6
   }
 }
 
+// Weight quantiser (article, "What's actually ternary"): per block of B
+// columns, scale = the mean absolute weight and state = the rounded, clamped
+// ratio w / scale.  The mean is an fp64 sum in column order divided by the
+// block's column count and rounded once to fp32, so it is a function of the
+// inputs alone; a zero block has scale 0 and states 0.  One thread per
+// (row, block); this runs once at load time, so it favours the fixed order
+// over speed.
+__global__ __launch_bounds__(kQuantBlock) void wquant_kernel(const float* W, int64_t N, int64_t K,
+                                                             int64_t ldw, int64_t B, int64_t nb,
+                                                             int8_t* t, int64_t ldt, float* s_b) {
+  const int64_t idx = (int64_t)blockIdx.x * kQuantBlock + threadIdx.x;
+  if (idx >= N * nb) return;
+  const int64_t i = idx / nb, b = idx % nb;
+  const float* row = W + i * ldw;
+  const int64_t j0 = b * B, j1 = min(j0 + B, K);
+  double total = 0.0;
+  for (int64_t j = j0; j < j1; ++j) total += fabs((double)load_g(row + j));
+  const float scale = (float)__ddiv_rn(total, (double)(j1 - j0));
+  s_b[idx] = scale;
+  int8_t* out = t + i * ldt;
+  for (int64_t j = j0; j < j1; ++j) {
+    float state = 0.0f;
+    if (scale > 0.0f) {
+      const float ratio = fminf(1.0f, fmaxf(-1.0f, __fdiv_rn(load_g(row + j), scale)));
+      state = __builtin_rintf(ratio);
+    }
+    out[j] = (int8_t)state;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, int64_t ldw, int64_t B,
+                                   int8_t* t, int64_t ldt, float* s_b, hipStream_t s) {
+  const int64_t nb = (K + B - 1) / B;
+  const int64_t blocks = (N * nb + kQuantBlock - 1) / kQuantBlock;
+  hipLaunchKernelGGL(wquant_kernel, dim3((unsigned)blocks), dim3(kQuantBlock), 0, s, W, N, K, ldw, B,
+                     nb, t, ldt, s_b);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                int64_t ldq, float* s_act, int32_t* z, hipStream_t s) {

@@ -34,7 +34,7 @@ EXPORTS = (
     "tern_row_bytes", "tern_pack", "tern_unpack", "tern_validate", "tern_gemv",
     "tern_gemm_smallM", "tern_linear_stack_workspace_bytes", "tern_linear_stack_prepare",
     "tern_linear_stack", "tern_block_rowsum", "tern_gemv_blocked", "tern_quantize_act",
-    "tern_head_rowsum", "tern_head_gemv", "tern_row_bytes5", "tern_pack5", "tern_gemv5",
+    "tern_quantize_weights", "tern_head_rowsum", "tern_head_gemv", "tern_row_bytes5", "tern_pack5", "tern_gemv5",
     "tern_read_probe",
     "tern_status_string", "tern_last_hip_error",
 )
@@ -102,6 +102,7 @@ def _declare(lib):
         "tern_block_rowsum": (i32, [vp, i64, i64, i64, vp, vp]),
         "tern_gemv_blocked": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp]),
         "tern_quantize_act": (i32, [vp, i64, i64, i64, vp, i64, vp, vp, vp]),
+        "tern_quantize_weights": (i32, [vp, i64, i64, i64, i64, vp, i64, vp, vp]),
         "tern_head_rowsum": (i32, [vp, i64, i64, i64, vp, vp]),
         "tern_head_gemv": (i32, [vp, vp, vp, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, vp]),
         "tern_row_bytes5": (i64, [i64]),
@@ -189,6 +190,11 @@ def tern_gemv_blocked(packed, s_b, rowsum_b, N, K, B, q, s_act, z, y, stream=Non
 def tern_quantize_act(x, M, K, ldx, q, ldq, s_act, z, stream=None):
     _check(_lib().tern_quantize_act(_ptr(x), M, K, ldx, _ptr(q), ldq, _ptr(s_act), _ptr(z),
                                     _stream(stream)), "tern_quantize_act")
+
+
+def tern_quantize_weights(W, N, K, ldw, B, w, ldt, s_b, stream=None):
+    _check(_lib().tern_quantize_weights(_ptr(W), N, K, ldw, B, _ptr(w), ldt, _ptr(s_b), _stream(stream)),
+           "tern_quantize_weights")
 
 
 def tern_head_rowsum(W, N, K, ldw, rowsum, stream=None):

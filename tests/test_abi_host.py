@@ -239,3 +239,17 @@ def test_packed5_row_bytes_and_argument_errors(lib):
     assert g5(q=ODD) == tern.TERN_ERR_ALIGNMENT
     assert g5(y=A16 + 2) == tern.TERN_ERR_ALIGNMENT
     assert g5(acc=A16 + 1) == tern.TERN_ERR_ALIGNMENT
+
+
+def test_weight_quantiser_argument_errors(lib):
+    def wq(W=A16, N=4, K=64, ldw=64, B=16, w=A16, ldt=64, s=A16):
+        return lib.tern_quantize_weights(W, N, K, ldw, B, w, ldt, s, S)
+    assert wq(N=0) == tern.TERN_OK
+    assert wq(K=0) == tern.TERN_ERR_INVALID_ARG
+    assert wq(B=0) == tern.TERN_ERR_INVALID_ARG
+    assert wq(ldw=63) == tern.TERN_ERR_INVALID_ARG
+    assert wq(ldt=63) == tern.TERN_ERR_INVALID_ARG
+    for field in ("W", "w", "s"):
+        assert wq(**{field: None}) == tern.TERN_ERR_INVALID_ARG, field
+    assert wq(W=A16 + 2) == tern.TERN_ERR_ALIGNMENT
+    assert wq(s=A16 + 1) == tern.TERN_ERR_ALIGNMENT
