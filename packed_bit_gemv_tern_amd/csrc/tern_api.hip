@@ -90,13 +90,18 @@ int device_cus() {
 constexpr int kStackBlock = 256;
 constexpr int kWavesPerBlock = kStackBlock / 64;
 constexpr int kMaxWavesPerCu = 32;  // 8 waves per SIMD x 4 SIMDs
-// The VALU stack kernels launch this many times the workgroups that fit on
-// the chip at once, each with 1/16 of a resident workgroup's share: the
-// dispatcher then starts a new workgroup wherever one finishes, which evens
-// out compute units and dispatch ranks that stream at different speeds (8B
-// stack at M = 1: 280 us with one workgroup per slot, 267 at 8x, 261 at
-// 16x, 270 at 32x).  The MFMA window kernel gained nothing from it.
+// The VALU stack kernels launch up to this many times the workgroups that
+// fit on the chip at once, each with a matching fraction of a resident
+// workgroup's share: the dispatcher then starts a new workgroup wherever one
+// finishes, which evens out compute units and dispatch ranks that stream at
+// different speeds (8B stack at M = 1: 280 us with one workgroup per slot,
+// 267 at 8x, 261 at 16x, 270 at 32x).  The factor stops growing where a
+// wave's share would fall below kValuWaveBytes (the 8B stack's share at 16x):
+// small stacks lose more to per-workgroup set-up than they gain (one 8B
+// layer: 14.4 us at 1x, 19.8 at 16x).  The MFMA window kernel gained nothing
+// from it.
 constexpr int kValuOversubscribe = 16;
+constexpr int64_t kValuWaveBytes = 24 << 10;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -378,7 +383,12 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   int per_cu = p == TERN_PATH_VALU ? valu_stack_blocks_per_cu(kernel)
                                    : mfma_stack_blocks_per_cu(kernel - SK_MFMA);
   per_cu = std::min(per_cu, kMaxWavesPerCu / kWavesPerBlock);
-  int grid = cus * per_cu * (p == TERN_PATH_VALU ? kValuOversubscribe : 1);
+  int over = 1;
+  if (p == TERN_PATH_VALU) {
+    const int64_t resident_waves = (int64_t)cus * per_cu * kWavesPerBlock;
+    over = (int)std::min<int64_t>(kValuOversubscribe, std::max<int64_t>(1, bytes / (resident_waves * kValuWaveBytes)));
+  }
+  int grid = cus * per_cu * over;
   grid = std::max(8, grid / 8 * 8);  // a multiple of 8 for the XCD-aware numbering
   // schedule entries belong to waves, or to whole workgroups for the
   // lockstep MFMA kernel

@@ -10,12 +10,12 @@
 //
 //  * Each K-step's operands go HBM/L2 -> LDS by DMA (global_load_lds): the
 //    BM x 64 activation tile and the ROWS x 16-byte packed weight tile, in a
-//    ring of STAGES buffers, so STAGES - 2 steps are in flight while one is
-//    used (the loads take several steps of MFMA work to arrive).
-//    One barrier per step (after each wave's own DMA has landed) publishes a
-//    buffer and frees the one the next DMA overwrites.  It is a bare
-//    s_barrier: the usual workgroup barrier also waits for every load in
-//    flight, which would drain the ring at each step.
+//    ring of STAGES buffers, so that later steps are in flight while the
+//    current ones are used (the loads take several steps of MFMA work to
+//    arrive).  One barrier per SS steps (after each wave's own DMA for them
+//    has landed) publishes those buffers and frees the SS the next DMAs
+//    overwrite.  It is a bare s_barrier: the usual workgroup barrier also
+//    waits for every load in flight, which would drain the ring.
 //  * The tile's row operands (rowsum, s_row) and token operands (z, s_act)
 //    come in with the first step by 4-byte DMA into LDS, so the epilogue has
 //    no dependent global loads.
@@ -60,10 +60,16 @@ struct GemmShape {
   static constexpr int WR = ROWS / RGROUPS / 16;     // row blocks of 16 per wave
   static constexpr int QLD = BM / 16 / WAVES;        // activation DMA instructions per wave
   static constexpr int PER = QLD + 1;                // DMA instructions per wave per step
-  static constexpr int STAGES = 6;                   // LDS ring depth (K-steps)
+  // LDS ring depth and K-steps per barrier.  The 64-token tile waits and
+  // synchronises once per 6 steps (a barrier per step kept its four waves in
+  // the same phase, LDS reads and MFMAs never overlapping: 133 -> 84 us per
+  // four 8B layers at M = 64); the eight-wave 128-token tile, which is bound
+  // by LDS bandwidth, was slower that way and keeps one barrier per step.
+  static constexpr int STAGES = BM == 128 ? 6 : 12;
+  static constexpr int SS = BM == 128 ? 1 : 6;
   static constexpr int META = (2 * ROWS + 2 * BM) / 64;  // operand DMA instructions per tile
   static_assert(WAVES * 32 == ROWS && QLD * WAVES * 16 == BM, "tile shape");
-  static_assert(PER * (STAGES - 2) < 16, "vmcnt field");
+  static_assert(PER * (STAGES - 2 * SS) < 64 && STAGES % SS == 0, "vmcnt field");
 };
 
 template <int BM>
@@ -88,8 +94,8 @@ __device__ __forceinline__ i32x4 gemm_decode(uint32_t x) {
 
 template <int N>
 __device__ __forceinline__ void gemm_wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Workgroup barrier without the memory fence of __syncthreads (which waits
@@ -217,20 +223,30 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
   };
   issue_meta();  // older than every step's loads, so step 0's wait covers it
 #pragma unroll
-  for (int s = 0; s < S::STAGES - 1; ++s)
+  for (int s = 0; s < S::STAGES - S::SS; ++s)
     if (s < nks) issue(s);
   // step k: my loads landed (later steps may still fly), then everybody's;
   // the barrier also frees the buffer the next issue reuses
-  for (int k = 0; k < nks; ++k) {
-    if (k + S::STAGES - 2 < nks)
-      gemm_wait_vm<S::PER * (S::STAGES - 2)>();
+  // steps k0 .. k0 + SS - 1 landed (mine, then everybody's); the barrier
+  // also frees the SS buffers the next issues reuse, read in the previous
+  // round
+  for (int k0 = 0; k0 < nks; k0 += S::SS) {
+    if (nks - k0 - S::SS >= S::STAGES - 2 * S::SS)
+      gemm_wait_vm<S::PER * (S::STAGES - 2 * S::SS)>();
     else
       gemm_wait_vm<0>();
     gemm_barrier();
-    if (k + S::STAGES - 1 < nks) issue(k + S::STAGES - 1);
-    Ops o;
-    load_ops(k, o);
-    compute(o);
+#pragma unroll
+    for (int i = 0; i < S::SS; ++i)
+      if (k0 + S::STAGES - S::SS + i < nks) issue(k0 + S::STAGES - S::SS + i);
+#pragma unroll
+    for (int i = 0; i < S::SS; ++i) {
+      if (k0 + i < nks) {
+        Ops o;
+        load_ops(k0 + i, o);
+        compute(o);
+      }
+    }
   }
 
   // epilogue: lane holds tokens tok0 + tbase + 16t + 4g + v of row row0 + rbase + 16b + r
