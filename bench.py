@@ -471,6 +471,41 @@ def suite(args):
     del Wd, td, sd, Wf
     torch.cuda.empty_cache()
 
+    # --- one decode step's linears, eager and replayed from a HIP graph:
+    # quantise the token (fp32 4,096), the 252-linear 8B stack, the int8 head
+    st = DeviceStack("8b", seed=5, threads=16)
+    Wh, srh_ = synth.make_head(0)
+    Nh, Kh = Wh.shape
+    Whd, srhd = torch.from_numpy(Wh).to(dev), torch.from_numpy(srh_).to(dev)
+    del Wh
+    rshd = torch.empty(Nh, dtype=torch.int32, device=dev)
+    tern.tern_head_rowsum(Whd, Nh, Kh, Kh, rshd)
+    for M in (1, 8):
+        b = st.bind(M)
+        ldq = b.q[0].shape[1]
+        xd = torch.from_numpy(np.random.default_rng([M, 6]).normal(0, 1, (M, Kh)).astype(np.float32)).to(dev)
+        logits = torch.empty((M, Nh), dtype=torch.float32, device=dev)
+
+        def dstep(i=0, b=b, xd=xd, logits=logits, M=M, ldq=ldq):
+            tern.tern_quantize_act(xd, M, Kh, Kh, b.q[0], ldq, b.s_act[0], b.z[0])
+            b.run()
+            tern.tern_head_gemv(Whd, srhd, rshd, Nh, Kh, Kh, M, b.q[0], ldq, b.s_act[0], b.z[0], logits, Nh)
+        eager = _event_times(dstep, 20)
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            dstep()
+        torch.cuda.synchronize()
+        replay = _event_times(lambda i: g.replay(), 20)
+        db = b.bytes + Nh * Kh + 8 * Nh + M * Kh + 8 * M + 4 * M * Nh + 5 * M * Kh
+        emit({"suite": "decode_step", "workload": "one decode step's linears at M = %d: quantise the "
+              "token(s), the 252-linear 8B stack (one launch), the int8 head 151,936 x 4,096" % M,
+              "M": M, "eager": _stats(eager, db), "graph_replay": _stats(replay, db),
+              "note": "three kernel launches; the stack's linears take independent synthetic activations"})
+        del b, g, xd, logits
+    del st, Whd, srhd, rshd
+    torch.cuda.empty_cache()
+
     # --- activation quantiser (launch-bound at decode sizes)
     for M in (1, 8, 512):
         x = np.random.default_rng([M, 5]).normal(0, 1, (M, 4096)).astype(np.float32)
