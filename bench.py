@@ -1,7 +1,7 @@
 """Benchmark: the 8B-shaped ternary linear stack on one MI355X.
 
 A step is one decode-and-verify pair over the whole stack of 252 ternary
-linears (36 layers x 7; hidden 4,096, FFN 12,288): one persistent
+linears (36 layers x 7; hidden 4,096, FFN 12,288): one
 ``tern_linear_stack`` launch at M = 1 token and one at M = 8 tokens (seven
 drafted tokens plus the verified one).  Weights are synthetic, seeded, with
 the pages' shapes and zero shares, packed on the device before timing.
@@ -19,10 +19,13 @@ kernels run on; ``cpu_baseline`` is the CPU oracle on a bounded sample.
 each: the single 256 x 512 GEMV; one 8B layer at M = 1 per linear and per
 layer (eight rotating copies, 390 MB, more than the 256 MB Infinity Cache);
 the 0.6B stack as seven M = 1 passes per step (three rotating copies, and
-warm); the prefill sweep M = 1 .. 512 on one 8B layer (eight copies); the
-int8 output head (151,936 x 4,096) at M = 1 and 8; block-wise scales on the
-8B's stacked gate projections; and the activation quantiser.  Each line
-carries the oracle timed on a bounded sample of the same workload.
+warm); the prefill sweep M = 1 .. 512 on one 8B layer (eight copies) and
+M = 16, 64, 512 on four layers; the int8 output head (151,936 x 4,096) at
+M = 1 and 8; block-wise scales on the 8B's stacked gate projections; the
+same gate projections in 2-bit and in 1.6-bit rows; the weight quantiser;
+one decode step (quantiser, stack, head) eager and replayed from a HIP
+graph; and the activation quantiser.  Most lines carry the oracle timed on
+a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -310,6 +313,23 @@ def suite(args):
         del bm
     del copies
 
+    # --- prefill over four 8B layers (28 linears, 195 MB): enough tiles to
+    # fill the chip, so the rate is the kernel's rather than one layer's
+    # longest tile chain (the K = 12,288 down projection)
+    st4 = DeviceStack("8b", layers=4, seed=3, threads=16)
+    specs4 = synth.stack_specs("8b", 4)
+    for M in (16, 64, 512):
+        b4 = st4.bind(M)
+        us = _event_times(lambda i: b4.run(), 24)
+        st = _stats(us, b4.bytes)
+        dense_ops = 2 * M * sum(N * K for (_, _, _, N, K, _) in specs4)
+        st["dense_TOPS"] = round(dense_ops / st["median_us"] / 1e6, 2)
+        st["frac_of_int8_peak"] = round(st["dense_TOPS"] / INT8_DENSE_PEAK_TOPS, 4)
+        emit({"suite": "prefill_4layers", "workload": "four 8B layers (28 linears), M = %d, one stack "
+              "launch" % M, "M": M, "kernel": kernel_name(b4.plan), **st})
+        del b4
+    del st4
+
     # --- 0.6B stack, M = 1, seven passes per step: 3 rotating copies, and warm
     st06 = [DeviceStack("0.6b", seed=c, threads=16) for c in range(3)]
     b06 = [st.bind(1) for st in st06]
@@ -535,9 +555,9 @@ def main():
     ap.add_argument("--only", choices=["m1", "m8"], default=None,
                     help="launch a single pass per step (for profiling)")
     ap.add_argument("--suite", action="store_true",
-                    help="measure the single GEMV, one 8B layer, the prefill sweep, the 0.6B "
-                         "stack, the int8 head, block scales and the quantiser instead (one JSON "
-                         "line each)")
+                    help="measure the single GEMV, one 8B layer, the prefill sweeps, the 0.6B "
+                         "stack, the int8 head, block scales, 1.6-bit rows, the quantisers and a "
+                         "graph-captured decode step instead (one JSON line each)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times "
                          "(reference for the HBM byte counters) and exit")
