@@ -282,7 +282,8 @@ int tern_gemv5(const uint8_t* packed5, const float* s_row, const int32_t* rowsum
 int tern_quantize_weights(const float* W, int64_t N, int64_t K, int64_t ldw, int64_t B, int8_t* w,
                           int64_t ldt, float* s_b, hipStream_t stream) {
   if (N < 0 || K < 1 || B < 1 || ldw < K || ldt < K) return TERN_ERR_INVALID_ARG;
-  if (N > kI32Max || K > kI32Max) return TERN_ERR_RANGE;
+  // one thread per (row, block): at most 2^40 of them (a 32-bit grid)
+  if (N > kI32Max || K > kI32Max || N * ((K + B - 1) / B) > ((int64_t)1 << 40)) return TERN_ERR_RANGE;
   if (N == 0) return TERN_OK;
   if (!W || !w || !s_b) return TERN_ERR_INVALID_ARG;
   if (!aligned(W, 4) || !aligned(s_b, 4)) return TERN_ERR_ALIGNMENT;

@@ -283,7 +283,7 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
 template <int BM>
 __device__ __forceinline__ void gemm_range(const LinearArgs& a, int tile0, int tile1, int tstride,
                                            int lane, int w, GemmTiles<BM>& L) {
-  const int ntok = (a.M + BM - 1) / BM;
+  const int ntok = (int)(((int64_t)a.M + BM - 1) / BM);
   for (int tile = tile0; tile < tile1; tile += tstride) {
     const int rt = tile / ntok, tt = tile - rt * ntok;
     gemm_tile<BM>(a, rt * GemmShape<BM>::ROWS, tt * BM, lane, w, L);
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(64 * GemmShape<BM>::WAVES) __attribute__((amdgpu_wa
 void gemm_linear_kernel(LinearArgs a) {
   __shared__ __attribute__((aligned(16))) GemmTiles<BM> L;
   constexpr int ROWS = GemmShape<BM>::ROWS;
-  const int ntiles = ((a.N + ROWS - 1) / ROWS) * ((a.M + BM - 1) / BM);
+  const int ntiles = (int)((((int64_t)a.N + ROWS - 1) / ROWS) * (((int64_t)a.M + BM - 1) / BM));
   gemm_range<BM>(a, gemm_xcd_block(), ntiles, gridDim.x, threadIdx.x & 63, gemm_wave_id(), L);
 }
 
@@ -340,7 +340,7 @@ static int gemm_block(int bm) { return 64 * (bm == 128 ? GemmShape<128>::WAVES :
 hipError_t launch_gemm_linear(const LinearArgs& a, hipStream_t s) {
   const int bm = gemm_tile_tokens(a.M);
   const int rows = gemm_unit_rows(bm);
-  const int64_t tiles = (int64_t)((a.N + rows - 1) / rows) * ((a.M + bm - 1) / bm);
+  const int64_t tiles = (((int64_t)a.N + rows - 1) / rows) * (((int64_t)a.M + bm - 1) / bm);
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(tiles, 65535));
   const dim3 grid((unsigned)blocks), block(gemm_block(bm));
   if (bm == 128)

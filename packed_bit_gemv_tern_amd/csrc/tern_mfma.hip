@@ -572,7 +572,7 @@ int32_t mfma_stack_variant(int32_t M, bool ragged, bool big) {
 int32_t mfma_token_tiles(int32_t variant, int32_t M) {
   if (variant != kGemm64Variant && variant != kGemm128Variant) return 0;
   const int bm = variant == kGemm128Variant ? 128 : 64;
-  return (M + bm - 1) / bm;
+  return (int32_t)(((int64_t)M + bm - 1) / bm);
 }
 
 bool mfma_per_workgroup(int32_t) { return true; }

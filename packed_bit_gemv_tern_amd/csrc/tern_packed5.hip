@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kP5Block) void gemv5_kernel(Gemv5Args a) {
 
   const int g = lane / LPR, r = lane % LPR;
   const int steps = (a.nch + LPR - 1) / LPR;
-  const int units = (a.N + UR - 1) / UR;
+  const int units = (int)(((int64_t)a.N + UR - 1) / UR);
   const int wstride = (int)gridDim.x * kP5Waves;
   int unit = (int)blockIdx.x * kP5Waves + wave;
   if (unit >= units) return;

@@ -253,3 +253,5 @@ def test_weight_quantiser_argument_errors(lib):
         assert wq(**{field: None}) == tern.TERN_ERR_INVALID_ARG, field
     assert wq(W=A16 + 2) == tern.TERN_ERR_ALIGNMENT
     assert wq(s=A16 + 1) == tern.TERN_ERR_ALIGNMENT
+    # one thread per (row, block): more than 2^40 of them is refused
+    assert wq(N=2 ** 31 - 1, K=2 ** 20, ldw=2 ** 20, ldt=2 ** 20, B=1) == tern.TERN_ERR_RANGE
