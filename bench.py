@@ -88,7 +88,7 @@ def kernel_name(plan) -> str:
         return "valu_stack_kernel<%d, 0u>" % {4: 2, 5: 4, 6: 8}[k]
     v = k - 8
     if v == 8:
-        return "mfma_win_stack_kernel"
+        return "mfma_win_stack_kernel<%s>" % ("true" if getattr(plan, "splits", 0) else "false")
     if v in (9, 10):
         return "gemm_stack_kernel<%d>" % (64 if v == 9 else 128)
     ragged = "true" if v & 2 else "false"

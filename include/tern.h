@@ -188,6 +188,10 @@ typedef struct {
   int32_t segments;  /* schedule entries */
   int32_t kernel;    /* internal kernel selector */
   int64_t bytes;     /* algorithmic bytes one launch moves (see below) */
+  int32_t splits;    /* linears split along K (then tern_linear_stack enqueues
+                        a fill kernel and a finishing kernel around the main
+                        one; see tern_linear_stack_prepare) */
+  int32_t pad;
 } tern_stack_plan;
 
 /* Upper bound of the workspace tern_linear_stack_prepare needs for L linears
@@ -202,12 +206,19 @@ int64_t tern_linear_stack_workspace_bytes(int64_t L, int64_t M);
  * aligned).  Enqueues the copy on `stream` and synchronises that stream
  * before returning (a one-time set-up step).  Fills *plan.
  * plan->bytes = sum over linears of N*row_bytes(K) + 8*N + M*K + 8*M + 4*M*N.
+ * On the activation-window path (2 <= M <= 8), a stack too small to spread
+ * its longest units (e.g. one 8B layer, whose K = 12,288 projection walks
+ * three 4,096-column windows per unit) has such linears split along K:
+ * their windows run as separate work, the exact int32 partial sums are
+ * added into y (used as int32 scratch), and a finishing kernel writes y and
+ * acc -- the results are the same bits.
  */
 int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
                               void* workspace, int64_t workspace_bytes,
                               tern_stack_plan* plan, hipStream_t stream);
 
-/* tern_linear_stack -- one launch over the prepared stack. */
+/* tern_linear_stack -- one launch over the prepared stack (three when
+ * plan->splits > 0: clear, main, finish). */
 int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream);
 
 /*

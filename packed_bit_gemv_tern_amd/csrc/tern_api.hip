@@ -111,15 +111,18 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 constexpr double kRestageCost = 40000.0;
 
 struct Layout {
-  int64_t off_lin, off_seg_start, off_seg, total;
+  int64_t off_lin, off_seg_start, off_seg, off_split, total;
 };
 
-Layout layout_for(int64_t L, int64_t workers, int64_t nseg) {
+// nlin LinearArgs entries, `workers` schedule heads, nseg segments, nsplit
+// split linears
+Layout layout_for(int64_t nlin, int64_t workers, int64_t nseg, int64_t nsplit) {
   Layout l;
   l.off_lin = (int64_t)sizeof(StackHeader);
-  l.off_seg_start = align_up(l.off_lin + L * (int64_t)sizeof(LinearArgs), 16);
+  l.off_seg_start = align_up(l.off_lin + nlin * (int64_t)sizeof(LinearArgs), 16);
   l.off_seg = align_up(l.off_seg_start + (workers + 1) * 4, 16);
-  l.total = l.off_seg + nseg * (int64_t)sizeof(Segment);
+  l.off_split = align_up(l.off_seg + nseg * (int64_t)sizeof(Segment), 16);
+  l.total = l.off_split + nsplit * 4;
   return l;
 }
 
@@ -334,7 +337,10 @@ int64_t tern_linear_stack_workspace_bytes(int64_t L, int64_t M) {
   int cus = device_cus();
   if (cus <= 0) cus = 256;
   const int64_t workers = (int64_t)cus * kMaxWavesPerCu * kValuOversubscribe;
-  return layout_for(L, workers, workers + L).total;
+  // every linear may be split into kMaxSplitWindows windows, each with its
+  // own LinearArgs entry and segments
+  const int64_t nlin = L * (1 + kMaxSplitWindows);
+  return layout_for(nlin, workers, workers + nlin, L).total;
 }
 
 int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
@@ -399,39 +405,84 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   // Granules: units of each linear's rows, cost = packed bytes + a fixed
   // per-unit overhead; contiguous granule runs balanced over the workers.
   std::vector<LinearArgs> lin((size_t)L);
-  struct Gran {
-    int32_t lin, r0, r1;
-    double cost;
-  };
-  std::vector<Gran> gran;
-  double total = 0.0;
-  // 0: segments hold rows; else the prefill GEMM's token tiles per row unit
-  // (its segments hold tile indices)
-  const int32_t ntok = p == TERN_PATH_VALU ? 0 : mfma_token_tiles(kernel - SK_MFMA, (int32_t)M);
   for (int64_t i = 0; i < L; ++i) {
     const tern_linear_desc& d = descs[i];
     lin[(size_t)i] = make_args(d.packed, d.s_row, d.rowsum, d.N, d.K, M, d.q, d.ldq, d.s_act, d.z,
                                d.y, d.ldy, d.acc);
-    if (d.N == 0) continue;
-    const int unit = p == TERN_PATH_VALU ? valu_unit_rows(lin[(size_t)i].variant, (int32_t)M)
+  }
+  struct Gran {
+    int32_t lin, r0, r1, flags;
+    double cost;
+  };
+  std::vector<Gran> gran;
+  std::vector<int32_t> split;  // linears split along K
+  double total = 0.0, gmax = 0.0;
+  // 0: segments hold rows; else the prefill GEMM's token tiles per row unit
+  // (its segments hold tile indices)
+  const int32_t ntok = p == TERN_PATH_VALU ? 0 : mfma_token_tiles(kernel - SK_MFMA, (int32_t)M);
+  const bool window = p == TERN_PATH_MFMA && mfma_is_window(kernel - SK_MFMA);
+  const int64_t wk_k = mfma_window_k();
+  auto add_units = [&](int32_t li, int32_t flags) {
+    const LinearArgs& a = lin[(size_t)li];
+    const int unit = p == TERN_PATH_VALU ? valu_unit_rows(a.variant, (int32_t)M)
                                          : mfma_unit_rows(kernel - SK_MFMA);
-    const double ld = (double)row_bytes(d.K);
+    const double ld = 16.0 * a.nch;  // packed bytes of a row the unit reads
     // a unit that restages the activation window stalls its workgroup for
     // about as long as streaming kRestageCost bytes takes
     const double fixed =
-        256.0 + (p == TERN_PATH_VALU ? 0.0 : kRestageCost * mfma_unit_restages(kernel - SK_MFMA, d.K));
-    for (int64_t r0 = 0; r0 < d.N; r0 += unit) {
-      const int64_t r1 = std::min<int64_t>(d.N, r0 + unit);
+        256.0 + (p == TERN_PATH_VALU ? 0.0 : kRestageCost * mfma_unit_restages(kernel - SK_MFMA, a.K));
+    for (int64_t r0 = 0; r0 < a.N; r0 += unit) {
+      const int64_t r1 = std::min<int64_t>(a.N, r0 + unit);
       const double c = (double)(r1 - r0) * ld + fixed;
       if (ntok == 0) {
-        gran.push_back({(int32_t)i, (int32_t)r0, (int32_t)r1, c});
+        gran.push_back({li, (int32_t)r0, (int32_t)r1, flags, c});
       } else {
         // prefill GEMM: one granule per (row tile, token tile), numbered
         // row tile first, so a run keeps reusing one weight tile
         const int32_t t0 = (int32_t)(r0 / unit) * ntok;
-        for (int32_t tt = 0; tt < ntok; ++tt) gran.push_back({(int32_t)i, t0 + tt, t0 + tt + 1, c});
+        for (int32_t tt = 0; tt < ntok; ++tt) gran.push_back({li, t0 + tt, t0 + tt + 1, flags, c});
       }
       total += c * (ntok == 0 ? 1 : ntok);
+      gmax = std::max(gmax, c);
+    }
+  };
+  for (int64_t i = 0; i < L; ++i)
+    if (descs[i].N > 0) add_units((int32_t)i, 0);
+  // A small stack whose longest unit outlasts the even share of a worker
+  // (one layer: a K = 12,288 unit restages its window three times while
+  // most workgroups idle) splits such linears along K: one entry per
+  // 4,096-column window, each window's units scheduled on their own, their
+  // int32 partial sums added into the output buffer, which a fill kernel
+  // clears before and a finishing kernel turns into y (and acc) after.
+  if (window && gmax > total / (double)workers) {
+    bool any = false;
+    for (int64_t i = 0; i < L && !any; ++i) {
+      const int64_t nwin = (lin[(size_t)i].K + wk_k - 1) / wk_k;
+      any = lin[(size_t)i].N > 0 && nwin > 1 && nwin <= kMaxSplitWindows;
+    }
+    if (any) {
+      gran.clear();
+      total = gmax = 0.0;
+      for (int64_t i = 0; i < L; ++i) {
+        const LinearArgs a = lin[(size_t)i];
+        if (a.N == 0) continue;
+        const int64_t nwin = (a.K + wk_k - 1) / wk_k;
+        if (nwin <= 1 || nwin > kMaxSplitWindows) {
+          add_units((int32_t)i, 0);
+          continue;
+        }
+        split.push_back((int32_t)i);
+        for (int64_t w = 0; w < nwin; ++w) {
+          LinearArgs v = a;
+          v.packed = a.packed + w * (wk_k / 4);  // 2-bit codes: K / 4 bytes
+          v.q = a.q + w * wk_k;
+          v.K = (int32_t)std::min<int64_t>(wk_k, a.K - w * wk_k);
+          v.nch = (v.K + 63) / 64;
+          v.acc = nullptr;
+          lin.push_back(v);
+          add_units((int32_t)lin.size() - 1, kSegPartial | (w == 0 ? kSegZeroPoint : 0));
+        }
+      }
     }
   }
   // Contiguous runs of granules, the largest run as small as it can be: the
@@ -441,11 +492,7 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   // worker numbering (and so over the XCDs).
   const size_t G = gran.size();
   std::vector<double> pre(G + 1, 0.0);
-  double gmax = 0.0;
-  for (size_t i = 0; i < G; ++i) {
-    pre[i + 1] = pre[i] + gran[i].cost;
-    gmax = std::max(gmax, gran[i].cost);
-  }
+  for (size_t i = 0; i < G; ++i) pre[i + 1] = pre[i] + gran[i].cost;
   auto runs_for = [&](double cap, std::vector<size_t>* ends) {
     int64_t n = 0;
     size_t i = 0;
@@ -489,12 +536,12 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
         segs.back().row_end = g.r1;
         continue;
       }
-      segs.push_back({g.lin, g.r0, g.r1, 0});
+      segs.push_back({g.lin, g.r0, g.r1, g.flags});
     }
   }
   while (wk <= workers) seg_start[(size_t)wk++] = (int32_t)segs.size();
 
-  const Layout lay = layout_for(L, workers, (int64_t)segs.size());
+  const Layout lay = layout_for((int64_t)lin.size(), workers, (int64_t)segs.size(), (int64_t)split.size());
   if (workspace_bytes < lay.total) return TERN_ERR_WORKSPACE;
   std::vector<char> host((size_t)lay.total, 0);
   StackHeader h;
@@ -505,13 +552,17 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   h.workers = (int32_t)workers;
   h.nseg = (int32_t)segs.size();
   h.kernel = kernel;
+  h.nlin = (int32_t)lin.size();
+  h.nsplit = (int32_t)split.size();
   h.off_lin = lay.off_lin;
   h.off_seg_start = lay.off_seg_start;
   h.off_seg = lay.off_seg;
+  h.off_split = lay.off_split;
   memcpy(host.data(), &h, sizeof(h));
   memcpy(host.data() + lay.off_lin, lin.data(), lin.size() * sizeof(LinearArgs));
   memcpy(host.data() + lay.off_seg_start, seg_start.data(), seg_start.size() * 4);
   if (!segs.empty()) memcpy(host.data() + lay.off_seg, segs.data(), segs.size() * sizeof(Segment));
+  if (!split.empty()) memcpy(host.data() + lay.off_split, split.data(), split.size() * 4);
   hipError_t e = hipMemcpyAsync(workspace, host.data(), (size_t)lay.total, hipMemcpyHostToDevice,
                                 stream);
   if (e != hipSuccess) return hip_fail(e);
@@ -522,6 +573,7 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   plan->workers = (int32_t)workers;
   plan->segments = (int32_t)segs.size();
   plan->kernel = kernel;
+  plan->splits = (int32_t)split.size();
   return TERN_OK;
 }
 
@@ -546,7 +598,9 @@ int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream) {
   shp.grid = plan->grid;
   shp.block = plan->block;
   shp.waves_per_block = plan->block / 64;
-  if (shp.grid <= 0 || shp.block != kStackBlock) return TERN_ERR_INVALID_ARG;
+  shp.M = plan->M;
+  shp.splits = plan->splits;
+  if (shp.grid <= 0 || shp.block != kStackBlock || shp.splits < 0) return TERN_ERR_INVALID_ARG;
   const hipError_t e = plan->kernel >= SK_MFMA
                            ? launch_mfma_stack(plan->kernel - SK_MFMA, plan->workspace, shp, stream)
                            : launch_valu_stack(plan->kernel, plan->workspace, shp, stream);

@@ -44,15 +44,27 @@ static_assert(sizeof(LinearArgs) == 96, "LinearArgs layout");
 // One schedule entry: rows [row_begin, row_end) of linear `lin` (all
 // tokens); for the prefill GEMM instead its tiles [row_begin, row_end) in
 // (row tile, token tile) order, tile = row_tile * token_tiles + token_tile.
+// `flags` marks entries of a linear split along K (activation-window kernel).
 struct Segment {
-  int32_t lin, row_begin, row_end, pad;
+  int32_t lin, row_begin, row_end, flags;
 };
+// The entry covers one K-window of a split linear: its int32 partial sums
+// are added into the output buffer (viewed as int32) instead of stored; the
+// zero-point term is part of exactly one window's sums.
+constexpr int32_t kSegPartial = 1, kSegZeroPoint = 2;
+// Windows a linear may be split into (each K-window is 4,096 columns).
+constexpr int kMaxSplitWindows = 4;
 
 // Stack workspace layout (device memory, 256-byte aligned):
-//   StackHeader | LinearArgs[L] | int32 seg_start[workers + 1] | Segment[nseg]
+//   StackHeader | LinearArgs[nlin] | int32 seg_start[workers + 1] |
+//   Segment[nseg] | int32 split[nsplit]
+// The first L entries of LinearArgs are the caller's linears; a linear split
+// along K adds one entry per window after them, and split[] lists the split
+// linears (their outputs are cleared before and finished after the main
+// kernel).
 struct alignas(256) StackHeader {
-  int32_t magic, L, M, workers, nseg, kernel, pad0, pad1;
-  int64_t off_lin, off_seg_start, off_seg;
+  int32_t magic, L, M, workers, nseg, kernel, nlin, nsplit;
+  int64_t off_lin, off_seg_start, off_seg, off_split;
 };
 constexpr int32_t kStackMagic = 0x7e54a11;
 
@@ -70,6 +82,7 @@ enum StackKernel : int32_t {
 // Launch parameters chosen by the launchers below.
 struct LaunchShape {
   int grid, block, waves_per_block;
+  int M, splits;  // tokens; linears split along K (0: no extra kernels)
 };
 
 // ---- launchers (defined in the .hip files) ----
@@ -104,6 +117,9 @@ int valu_stack_blocks_per_cu(int32_t kernel);
 // of the activation-window kernel (see mfma_win_offsets_fit)
 int32_t mfma_stack_variant(int32_t M, bool ragged, bool big);
 bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy);
+// the activation-window kernel: is `variant` it, and its window width in K
+bool mfma_is_window(int32_t variant);
+int mfma_window_k();
 
 // Prefill GEMM (M > 16; tern_gemm.hip): tiles of gemm_unit_rows(bm) rows x
 // bm = gemm_tile_tokens(M) tokens, one workgroup per tile.

@@ -299,9 +299,12 @@ struct WinStaged {
   }
 };
 
+// SPLIT: segments may be windows of linears split along K (their flags say
+// so); compiled apart so that the kernel for unsplit stacks carries none of it.
+template <bool SPLIT>
 __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, int row_hi, int unit0,
                                                int ustride, int lane, int w, WinTiles& L,
-                                               WinStaged& staged) {
+                                               WinStaged& staged, int flags) {
   constexpr int R = kWinR;
   constexpr int NLD = 16 * R / 8;  // 1 KB wave loads per K-step
   const int r = lane & 15, g = lane >> 4;
@@ -452,11 +455,19 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
       }
     }
 
-    // epilogue: lane holds tokens 4g + v of row base + 16b + r
+    // epilogue: lane holds tokens 4g + v of row base + 16b + r.  A window of
+    // a linear split along K adds its exact partial sums into y, viewed as
+    // int32 (cleared before the launch, finished after it); the zero-point
+    // term belongs to one window only.
+    const bool partial = SPLIT && (flags & kSegPartial) != 0;
+    const bool zpoint = !partial || (flags & kSegZeroPoint) != 0;
     int32_t zt[4];
     float sa[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) zt[v] = L.z[(4 * g + v) & 7], sa[v] = L.s_act[(4 * g + v) & 7];
+    for (int v = 0; v < 4; ++v) {
+      zt[v] = zpoint ? L.z[(4 * g + v) & 7] : 0;
+      sa[v] = L.s_act[(4 * g + v) & 7];
+    }
 #pragma unroll
     for (int b = 0; b < R; ++b) {
       const int row = base + 16 * b + r;
@@ -470,9 +481,15 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
                                          (uint32_t)zt[v] * (uint32_t)rs[b]);
           // byte offset of (m, row) in y and acc: below 2^32 (checked by the host)
           const uint32_t off = ((uint32_t)m * (uint32_t)a.ldy + (uint32_t)row) * 4u;
-          store_g(reinterpret_cast<float*>(reinterpret_cast<char*>(a.y) + off),
-                  epilogue(sr[b], accv, sa[v]));
-          if (a.acc) store_g(reinterpret_cast<int32_t*>(reinterpret_cast<char*>(a.acc) + off), accv);
+          if (partial) {
+            __hip_atomic_fetch_add((int32_t __attribute__((address_space(1)))*)(
+                                       reinterpret_cast<char*>(a.y) + off),
+                                   accv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            store_g(reinterpret_cast<float*>(reinterpret_cast<char*>(a.y) + off),
+                    epilogue(sr[b], accv, sa[v]));
+            if (a.acc) store_g(reinterpret_cast<int32_t*>(reinterpret_cast<char*>(a.acc) + off), accv);
+          }
         }
       }
     }
@@ -528,9 +545,10 @@ __global__ __launch_bounds__(kBlock) void mfma_wg_stack_kernel(const StackHeader
 __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void mfma_win_linear_kernel(LinearArgs a) {
   __shared__ __attribute__((aligned(16))) WinTiles L;
   WinStaged staged;
-  mfma_win_range(a, 0, a.N, blockIdx.x, gridDim.x, threadIdx.x & 63, wave_id_uniform(), L, staged);
+  mfma_win_range<false>(a, 0, a.N, blockIdx.x, gridDim.x, threadIdx.x & 63, wave_id_uniform(), L, staged, 0);
 }
 
+template <bool SPLIT>
 __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void mfma_win_stack_kernel(const StackHeader* __restrict__ h) {
   __shared__ __attribute__((aligned(16))) WinTiles L;
   const int worker = xcd_logical_block();
@@ -546,7 +564,38 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4)
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
-    mfma_win_range(a, sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged);
+    mfma_win_range<SPLIT>(a, sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged, SPLIT ? sg.flags : 0);
+  }
+}
+
+// Linears split along K: before the main kernel their outputs are cleared
+// (the windows add int32 partial sums into them), after it each sum becomes
+// y = (s_row * acc) * s_act, and acc when asked for.  One workgroup per
+// (split linear, token).
+__global__ __launch_bounds__(256) void split_clear_kernel(const StackHeader* __restrict__ h) {
+  const char* base = reinterpret_cast<const char*>(h);
+  const LinearArgs* lin = reinterpret_cast<const LinearArgs*>(base + h->off_lin);
+  const int32_t* split = reinterpret_cast<const int32_t*>(base + h->off_split);
+  const int M = h->M;
+  const LinearArgs& a = lin[split[blockIdx.x / M]];
+  const int m = blockIdx.x % M;
+  int32_t* y = reinterpret_cast<int32_t*>(a.y) + (int64_t)m * a.ldy;
+  for (int row = threadIdx.x; row < a.N; row += blockDim.x) store_g(y + row, 0);
+}
+
+__global__ __launch_bounds__(256) void split_finish_kernel(const StackHeader* __restrict__ h) {
+  const char* base = reinterpret_cast<const char*>(h);
+  const LinearArgs* lin = reinterpret_cast<const LinearArgs*>(base + h->off_lin);
+  const int32_t* split = reinterpret_cast<const int32_t*>(base + h->off_split);
+  const int M = h->M;
+  const LinearArgs& a = lin[split[blockIdx.x / M]];
+  const int m = blockIdx.x % M;
+  const int64_t o0 = (int64_t)m * a.ldy;
+  const float sa = load_g(a.s_act + m);
+  for (int row = threadIdx.x; row < a.N; row += blockDim.x) {
+    const int32_t acc = load_g(reinterpret_cast<const int32_t*>(a.y) + o0 + row);
+    store_g(a.y + o0 + row, epilogue(load_g(a.s_row + row), acc, sa));
+    if (a.acc) store_g(a.acc + o0 + row, acc);
   }
 }
 
@@ -562,6 +611,10 @@ bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy) {
   // weight row offsets and output byte offsets are 32-bit in that kernel
   return N * ld < (1ll << 32) && M * ldy * 4 < (1ll << 32);
 }
+
+bool mfma_is_window(int32_t variant) { return variant == kWinVariant; }
+
+int mfma_window_k() { return kWinK; }
 
 int32_t mfma_stack_variant(int32_t M, bool ragged, bool big) {
   if (M > 16) return gemm_tile_tokens(M) == 128 ? kGemm128Variant : kGemm64Variant;
@@ -595,7 +648,7 @@ static hipError_t with_mfma_stack_kernel(int32_t variant, F&& f) {
     case 2: return f(mfma_wg_stack_kernel<8, true>);
     case 4: return f(mfma_wg_stack_kernel<16, false>);
     case 6: return f(mfma_wg_stack_kernel<16, true>);
-    case kWinVariant: return f(mfma_win_stack_kernel);
+    case kWinVariant: return f(mfma_win_stack_kernel<false>);
     default: return hipErrorInvalidValue;
   }
 }
@@ -624,10 +677,26 @@ hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape&
     return launch_gemm_stack(variant == kGemm128Variant ? 128 : 64, ws, shp, s);
   const StackHeader* h = static_cast<const StackHeader*>(ws);
   const dim3 grid(shp.grid), block(variant == kWinVariant ? kWinBlock : shp.block);
-  return with_mfma_stack_kernel(variant, [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, s, h);
-    return hipGetLastError();
-  });
+  const bool split = variant == kWinVariant && shp.splits > 0;
+  const dim3 sgrid((unsigned)(shp.splits * shp.M));
+  if (split) {
+    hipLaunchKernelGGL(split_clear_kernel, sgrid, dim3(256), 0, s, h);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e;
+  if (split) {
+    hipLaunchKernelGGL(mfma_win_stack_kernel<true>, grid, block, 0, s, h);
+    e = hipGetLastError();
+  } else {
+    e = with_mfma_stack_kernel(variant, [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, block, 0, s, h);
+      return hipGetLastError();
+    });
+  }
+  if (e != hipSuccess || !split) return e;
+  hipLaunchKernelGGL(split_finish_kernel, sgrid, dim3(256), 0, s, h);
+  return hipGetLastError();
 }
 
 int mfma_stack_blocks_per_cu(int32_t variant) {

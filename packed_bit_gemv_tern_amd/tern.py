@@ -65,6 +65,7 @@ class tern_stack_plan(ctypes.Structure):
         ("L", ctypes.c_int32), ("M", ctypes.c_int32), ("path", ctypes.c_int32),
         ("grid", ctypes.c_int32), ("block", ctypes.c_int32), ("workers", ctypes.c_int32),
         ("segments", ctypes.c_int32), ("kernel", ctypes.c_int32), ("bytes", ctypes.c_int64),
+        ("splits", ctypes.c_int32), ("pad", ctypes.c_int32),
     ]
 
 
