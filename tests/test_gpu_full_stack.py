@@ -27,6 +27,7 @@ def stack():
 def test_full_8b_stack_sampled(stack, M):
     b = stack.bind(M, with_acc=True)
     assert b.plan.L == 252
+    assert b.plan.splits == 0  # a full stack keeps every linear whole
     b.run()
     b.run()  # the benchmark launches the same plan back to back
     torch.cuda.synchronize()

@@ -239,11 +239,31 @@ def test_stack_8b_one_layer(M):
     ws = torch.empty(tern.tern_linear_stack_workspace_bytes(len(ups), M), dtype=torch.uint8,
                      device=DEV)
     plan = tern.tern_linear_stack_prepare([u.desc() for u in ups], M, ws)
+    # one layer at M = 8 is small enough that the K = 12,288 down projection
+    # is split per window (partial sums through the output buffer)
+    assert plan.splits == (1 if M == 8 else 0)
     tern.tern_linear_stack(plan)
     tern.tern_linear_stack(plan)  # a second launch over the same plan
     for lin, up in zip(lins, ups):
         y, acc = up.results()
         assert_parity(y, acc, oracle_ref(lin), "8b layer %s M=%d" % (lin.name, M))
+
+
+@pytest.mark.parametrize("M", [2, 5, 8])
+def test_stack_split_windows(M):
+    # two K = 12,288 linears and a K = 8,192 one among short ones: split, and
+    # launched twice (the fill kernel must clear the previous sums)
+    specs = [(300, 12288, 1), (64, 4096, 2), (257, 8192, 3), (40, 12288, 4), (100, 1024, 5)]
+    lins = [synth.make_linear(13, s, 0, N, K, 0.626, M, "s%d" % s) for (N, K, s) in specs]
+    ups = [Uploaded(lin) for lin in lins]
+    ws = torch.empty(tern.tern_linear_stack_workspace_bytes(len(ups), M), dtype=torch.uint8, device=DEV)
+    plan = tern.tern_linear_stack_prepare([u.desc() for u in ups], M, ws, tern.TERN_PATH_MFMA)
+    assert plan.splits == 3
+    for _ in range(3):
+        tern.tern_linear_stack(plan)
+    for lin, up in zip(lins, ups):
+        y, acc = up.results()
+        assert_parity(y, acc, oracle_ref(lin), "split %s M=%d" % (lin.name, M))
 
 
 def test_stack_mixed_shapes_and_empty_linear():
