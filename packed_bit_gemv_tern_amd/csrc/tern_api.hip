@@ -101,6 +101,12 @@ constexpr int kMaxWavesPerCu = 32;  // 8 waves per SIMD x 4 SIMDs
 // layer: 14.4 us at 1x, 19.8 at 16x).  The MFMA window kernel gained nothing
 // from it.
 constexpr int kValuOversubscribe = 16;
+// A stack is split along K when its longest unit costs more than this many
+// times a worker's even share.  Measured on 8B layers: one layer (about 4x
+// at M = 17..64, 9x at M <= 8) gains 23-26 %; four layers at M <= 8 (2.3x)
+// lose 30 %, and at about 1x (four layers at M = 64, one at M = 512) the
+// partial sums' atomics cost more than the shorter tail saves.
+constexpr double kSplitRatio = 3.0;
 constexpr int64_t kValuWaveBytes = 24 << 10;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -420,7 +426,7 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   // 0: segments hold rows; else the prefill GEMM's token tiles per row unit
   // (its segments hold tile indices)
   const int32_t ntok = p == TERN_PATH_VALU ? 0 : mfma_token_tiles(kernel - SK_MFMA, (int32_t)M);
-  const bool window = p == TERN_PATH_MFMA && mfma_is_window(kernel - SK_MFMA);
+  const bool splittable = p == TERN_PATH_MFMA && mfma_can_split(kernel - SK_MFMA);
   const int64_t wk_k = mfma_window_k();
   auto add_units = [&](int32_t li, int32_t flags) {
     const LinearArgs& a = lin[(size_t)li];
@@ -449,17 +455,21 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   for (int64_t i = 0; i < L; ++i)
     if (descs[i].N > 0) add_units((int32_t)i, 0);
   // A small stack whose longest unit outlasts the even share of a worker
-  // (one layer: a K = 12,288 unit restages its window three times while
-  // most workgroups idle) splits such linears along K: one entry per
-  // 4,096-column window, each window's units scheduled on their own, their
-  // int32 partial sums added into the output buffer, which a fill kernel
-  // clears before and a finishing kernel turns into y (and acc) after.
-  if (window && gmax > total / (double)workers) {
+  // (one layer: a K = 12,288 unit restages its window three times, or walks
+  // 192 GEMM K-steps, while most workgroups idle) splits such linears along
+  // K: one entry per 4,096-column window, each window's units scheduled on
+  // their own, their int32 partial sums added into the output buffer, which
+  // a fill kernel clears before and a finishing kernel turns into y (and
+  // acc) after.
+  if (splittable && gmax > kSplitRatio * total / (double)workers) {
+    // only K a multiple of 64: every window's reads then lie inside the
+    // linear's K columns (the kernels clamp activation addresses to the row)
+    auto splits_k = [&](const LinearArgs& a) {
+      const int64_t nwin = (a.K + wk_k - 1) / wk_k;
+      return a.N > 0 && a.K % 64 == 0 && nwin > 1 && nwin <= kMaxSplitWindows;
+    };
     bool any = false;
-    for (int64_t i = 0; i < L && !any; ++i) {
-      const int64_t nwin = (lin[(size_t)i].K + wk_k - 1) / wk_k;
-      any = lin[(size_t)i].N > 0 && nwin > 1 && nwin <= kMaxSplitWindows;
-    }
+    for (int64_t i = 0; i < L && !any; ++i) any = splits_k(lin[(size_t)i]);
     if (any) {
       gran.clear();
       total = gmax = 0.0;
@@ -467,7 +477,7 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
         const LinearArgs a = lin[(size_t)i];
         if (a.N == 0) continue;
         const int64_t nwin = (a.K + wk_k - 1) / wk_k;
-        if (nwin <= 1 || nwin > kMaxSplitWindows) {
+        if (!splits_k(a)) {
           add_units((int32_t)i, 0);
           continue;
         }

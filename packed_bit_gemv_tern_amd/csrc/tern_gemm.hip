@@ -123,10 +123,13 @@ __device__ __forceinline__ i32x4 gemm_mask_tail(i32x4 v, int j0, int K) {
   return v;
 }
 
-// One ROWS x BM tile over all of K: rows row0.., tokens tok0..
-template <int BM>
+// One ROWS x BM tile over all of K: rows row0.., tokens tok0..  With SPLIT,
+// `flags` may mark the tile as one K-window of a linear split along K: its
+// exact int32 sums are then added into y viewed as int32 (cleared before the
+// launch and finished after it), the zero-point term in one window only.
+template <int BM, bool SPLIT>
 __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok0, int lane, int w,
-                                          GemmTiles<BM>& L) {
+                                          GemmTiles<BM>& L, int flags) {
   using S = GemmShape<BM>;
   const int r = lane & 15, g = lane >> 4;
   const int K = a.K, M = a.M, N = a.N;
@@ -250,6 +253,8 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
   }
 
   // epilogue: lane holds tokens tok0 + tbase + 16t + 4g + v of row row0 + rbase + 16b + r
+  const bool partial = SPLIT && (flags & kSegPartial) != 0;
+  const bool zpoint = !partial || (flags & kSegZeroPoint) != 0;
 #pragma unroll
   for (int b = 0; b < S::WR; ++b) {
     const int rl = rbase + 16 * b + r;
@@ -264,10 +269,16 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
         const int ml = tbase + 16 * t + 4 * g + v;
         const int m = tok0 + ml;
         if (m < M) {
-          const int32_t accv = (int32_t)((uint32_t)acc[b][t][v] - (uint32_t)L.z[ml] * (uint32_t)rs);
+          const int32_t zz = zpoint ? L.z[ml] : 0;
+          const int32_t accv = (int32_t)((uint32_t)acc[b][t][v] - (uint32_t)zz * (uint32_t)rs);
           const int64_t o = (int64_t)m * a.ldy + row;
-          store_g(a.y + o, epilogue(sr, accv, L.s_act[ml]));
-          if (a.acc) store_g(a.acc + o, accv);
+          if (partial) {
+            __hip_atomic_fetch_add((int32_t __attribute__((address_space(1)))*)(reinterpret_cast<int32_t*>(a.y) + o),
+                                   accv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+            store_g(a.y + o, epilogue(sr, accv, L.s_act[ml]));
+            if (a.acc) store_g(a.acc + o, accv);
+          }
         }
       }
     }
@@ -280,13 +291,13 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
 // Tiles tile0, tile0 + tstride, ... below tile1 of a linear, numbered in
 // (row tile, token tile) order: tile = row_tile * token_tiles + token_tile,
 // so the token tiles of one row tile are adjacent.
-template <int BM>
+template <int BM, bool SPLIT>
 __device__ __forceinline__ void gemm_range(const LinearArgs& a, int tile0, int tile1, int tstride,
-                                           int lane, int w, GemmTiles<BM>& L) {
+                                           int lane, int w, GemmTiles<BM>& L, int flags) {
   const int ntok = (int)(((int64_t)a.M + BM - 1) / BM);
   for (int tile = tile0; tile < tile1; tile += tstride) {
     const int rt = tile / ntok, tt = tile - rt * ntok;
-    gemm_tile<BM>(a, rt * GemmShape<BM>::ROWS, tt * BM, lane, w, L);
+    gemm_tile<BM, SPLIT>(a, rt * GemmShape<BM>::ROWS, tt * BM, lane, w, L, flags);
   }
 }
 
@@ -301,10 +312,10 @@ void gemm_linear_kernel(LinearArgs a) {
   __shared__ __attribute__((aligned(16))) GemmTiles<BM> L;
   constexpr int ROWS = GemmShape<BM>::ROWS;
   const int ntiles = (int)((((int64_t)a.N + ROWS - 1) / ROWS) * (((int64_t)a.M + BM - 1) / BM));
-  gemm_range<BM>(a, gemm_xcd_block(), ntiles, gridDim.x, threadIdx.x & 63, gemm_wave_id(), L);
+  gemm_range<BM, false>(a, gemm_xcd_block(), ntiles, gridDim.x, threadIdx.x & 63, gemm_wave_id(), L, 0);
 }
 
-template <int BM>
+template <int BM, bool SPLIT>
 __global__ __launch_bounds__(64 * GemmShape<BM>::WAVES) __attribute__((amdgpu_waves_per_eu(BM == 128 ? 2 : 4)))
 void gemm_stack_kernel(const StackHeader* __restrict__ h) {
   __shared__ __attribute__((aligned(16))) GemmTiles<BM> L;
@@ -320,13 +331,14 @@ void gemm_stack_kernel(const StackHeader* __restrict__ h) {
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
-    gemm_range<BM>(a, sg.row_begin, sg.row_end, 1, lane, w, L);
+    gemm_range<BM, SPLIT>(a, sg.row_begin, sg.row_end, 1, lane, w, L, SPLIT ? sg.flags : 0);
   }
 }
 
 template <typename F>
-static hipError_t with_gemm_stack_kernel(int bm, F&& f) {
-  return bm == 128 ? f(gemm_stack_kernel<128>) : f(gemm_stack_kernel<64>);
+static hipError_t with_gemm_stack_kernel(int bm, bool split, F&& f) {
+  if (split) return bm == 128 ? f(gemm_stack_kernel<128, true>) : f(gemm_stack_kernel<64, true>);
+  return bm == 128 ? f(gemm_stack_kernel<128, false>) : f(gemm_stack_kernel<64, false>);
 }
 
 }  // namespace
@@ -352,15 +364,22 @@ hipError_t launch_gemm_linear(const LinearArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_stack(int bm, const void* ws, const LaunchShape& shp, hipStream_t s) {
   const StackHeader* h = static_cast<const StackHeader*>(ws);
-  return with_gemm_stack_kernel(bm, [&](auto kern) {
+  const bool split = shp.splits > 0;
+  if (split) {
+    const hipError_t e = launch_split_clear(ws, shp, s);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = with_gemm_stack_kernel(bm, split, [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(shp.grid), dim3(gemm_block(bm)), 0, s, h);
     return hipGetLastError();
   });
+  if (e != hipSuccess || !split) return e;
+  return launch_split_finish(ws, shp, s);
 }
 
 int gemm_stack_blocks_per_cu(int bm) {
   int n = 0;
-  const hipError_t e = with_gemm_stack_kernel(bm, [&](auto kern) {
+  const hipError_t e = with_gemm_stack_kernel(bm, false, [&](auto kern) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, gemm_block(bm), 0);
   });
   if (e != hipSuccess || n < 1) n = 1;

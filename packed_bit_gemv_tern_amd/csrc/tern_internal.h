@@ -120,6 +120,11 @@ bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy);
 // the activation-window kernel: is `variant` it, and its window width in K
 bool mfma_is_window(int32_t variant);
 int mfma_window_k();
+// kernels that take linears split along K (window kernel, prefill GEMM), and
+// the fill and finishing kernels of split linears
+bool mfma_can_split(int32_t variant);
+hipError_t launch_split_clear(const void* ws, const LaunchShape& shp, hipStream_t s);
+hipError_t launch_split_finish(const void* ws, const LaunchShape& shp, hipStream_t s);
 
 // Prefill GEMM (M > 16; tern_gemm.hip): tiles of gemm_unit_rows(bm) rows x
 // bm = gemm_tile_tokens(M) tokens, one workgroup per tile.

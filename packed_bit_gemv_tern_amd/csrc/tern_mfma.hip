@@ -614,6 +614,22 @@ bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy) {
 
 bool mfma_is_window(int32_t variant) { return variant == kWinVariant; }
 
+bool mfma_can_split(int32_t variant) {
+  return variant == kWinVariant || variant == kGemm64Variant || variant == kGemm128Variant;
+}
+
+hipError_t launch_split_clear(const void* ws, const LaunchShape& shp, hipStream_t s) {
+  hipLaunchKernelGGL(split_clear_kernel, dim3((unsigned)(shp.splits * shp.M)), dim3(256), 0, s,
+                     static_cast<const StackHeader*>(ws));
+  return hipGetLastError();
+}
+
+hipError_t launch_split_finish(const void* ws, const LaunchShape& shp, hipStream_t s) {
+  hipLaunchKernelGGL(split_finish_kernel, dim3((unsigned)(shp.splits * shp.M)), dim3(256), 0, s,
+                     static_cast<const StackHeader*>(ws));
+  return hipGetLastError();
+}
+
 int mfma_window_k() { return kWinK; }
 
 int32_t mfma_stack_variant(int32_t M, bool ragged, bool big) {
@@ -678,10 +694,8 @@ hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape&
   const StackHeader* h = static_cast<const StackHeader*>(ws);
   const dim3 grid(shp.grid), block(variant == kWinVariant ? kWinBlock : shp.block);
   const bool split = variant == kWinVariant && shp.splits > 0;
-  const dim3 sgrid((unsigned)(shp.splits * shp.M));
   if (split) {
-    hipLaunchKernelGGL(split_clear_kernel, sgrid, dim3(256), 0, s, h);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_split_clear(ws, shp, s);
     if (e != hipSuccess) return e;
   }
   hipError_t e;
@@ -695,8 +709,7 @@ hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape&
     });
   }
   if (e != hipSuccess || !split) return e;
-  hipLaunchKernelGGL(split_finish_kernel, sgrid, dim3(256), 0, s, h);
-  return hipGetLastError();
+  return launch_split_finish(ws, shp, s);
 }
 
 int mfma_stack_blocks_per_cu(int32_t variant) {

@@ -249,7 +249,7 @@ def test_stack_8b_one_layer(M):
         assert_parity(y, acc, oracle_ref(lin), "8b layer %s M=%d" % (lin.name, M))
 
 
-@pytest.mark.parametrize("M", [2, 5, 8])
+@pytest.mark.parametrize("M", [2, 5, 8, 17, 64, 130])
 def test_stack_split_windows(M):
     # two K = 12,288 linears and a K = 8,192 one among short ones: split, and
     # launched twice (the fill kernel must clear the previous sums)
@@ -261,6 +261,23 @@ def test_stack_split_windows(M):
     assert plan.splits == 3
     for _ in range(3):
         tern.tern_linear_stack(plan)
+    for lin, up in zip(lins, ups):
+        y, acc = up.results()
+        assert_parity(y, acc, oracle_ref(lin), "split %s M=%d" % (lin.name, M))
+
+
+@pytest.mark.parametrize("M", [20, 100])
+def test_stack_split_ragged_k_prefill(M):
+    # prefill GEMM: K = 8,384 in windows of 4,096, 4,096 and 192 columns; a
+    # ragged K (not split) and a short one beside it
+    specs = [(200, 8384, 1), (70, 4100, 2), (33, 100, 3), (90, 12288, 4)]
+    lins = [synth.make_linear(17, s, 0, N, K, 0.626, M, "r%d" % s) for (N, K, s) in specs]
+    ups = [Uploaded(lin) for lin in lins]
+    ws = torch.empty(tern.tern_linear_stack_workspace_bytes(len(ups), M), dtype=torch.uint8, device=DEV)
+    plan = tern.tern_linear_stack_prepare([u.desc() for u in ups], M, ws, tern.TERN_PATH_MFMA)
+    assert plan.splits == 2
+    tern.tern_linear_stack(plan)
+    tern.tern_linear_stack(plan)
     for lin, up in zip(lins, ups):
         y, acc = up.results()
         assert_parity(y, acc, oracle_ref(lin), "split %s M=%d" % (lin.name, M))
