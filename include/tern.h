@@ -206,12 +206,13 @@ int64_t tern_linear_stack_workspace_bytes(int64_t L, int64_t M);
  * aligned).  Enqueues the copy on `stream` and synchronises that stream
  * before returning (a one-time set-up step).  Fills *plan.
  * plan->bytes = sum over linears of N*row_bytes(K) + 8*N + M*K + 8*M + 4*M*N.
- * On the activation-window path (2 <= M <= 8), a stack too small to spread
- * its longest units (e.g. one 8B layer, whose K = 12,288 projection walks
- * three 4,096-column windows per unit) has such linears split along K:
- * their windows run as separate work, the exact int32 partial sums are
- * added into y (used as int32 scratch), and a finishing kernel writes y and
- * acc -- the results are the same bits.
+ * On the MFMA path (M >= 2), a stack too small to spread its longest units
+ * (their cost over 3x a worker's share: e.g. one 8B layer, whose K = 12,288
+ * projection walks three 4,096-column windows per unit) has such linears
+ * (K a multiple of 64, at most 4 windows) split along K: their windows run
+ * as separate work, the exact int32 partial sums are added into y (used as
+ * int32 scratch), and a finishing kernel writes y and acc -- the results
+ * are the same bits.  plan->splits counts them.
  */
 int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
                               void* workspace, int64_t workspace_bytes,
