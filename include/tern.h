@@ -212,7 +212,10 @@ int64_t tern_linear_stack_workspace_bytes(int64_t L, int64_t M);
  * (K a multiple of 64, at most 4 windows) split along K: their windows run
  * as separate work, the exact int32 partial sums are added into y (used as
  * int32 scratch), and a finishing kernel writes y and acc -- the results
- * are the same bits.  plan->splits counts them.
+ * are the same bits.  plan->splits counts them.  At 9..16 tokens such a
+ * small stack also takes the prefill GEMM's kernel in place of the lockstep
+ * one (the same test on the lockstep kernel's units); the results are the
+ * same bits either way.
  */
 int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
                               void* workspace, int64_t workspace_bytes,

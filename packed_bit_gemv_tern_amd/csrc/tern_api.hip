@@ -388,13 +388,34 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
     big = big || !mfma_win_offsets_fit(descs[i].N, row_bytes(descs[i].K), M, descs[i].ldy);
   }
   const bool ragged = (used >> VGEN) & 1u;
-  const int32_t kernel = p == TERN_PATH_VALU
-                             ? valu_stack_kernel_for((int32_t)M, used)
-                             : (int32_t)SK_MFMA + mfma_stack_variant((int32_t)M, ragged, big);
+  int32_t kernel = p == TERN_PATH_VALU ? valu_stack_kernel_for((int32_t)M, used)
+                                       : (int32_t)SK_MFMA + mfma_stack_variant((int32_t)M, ragged, big);
   const int cus = device_cus();
   if (cus <= 0) return hip_fail(hipErrorNoDevice);
-  int per_cu = p == TERN_PATH_VALU ? valu_stack_blocks_per_cu(kernel)
-                                   : mfma_stack_blocks_per_cu(kernel - SK_MFMA);
+  auto mfma_per_cu = [&](int32_t v) {
+    return std::min(mfma_stack_blocks_per_cu(v), kMaxWavesPerCu / kWavesPerBlock);
+  };
+  // The lockstep kernel at 9..16 tokens keeps a workgroup on one unit of
+  // rows for the linear's whole K.  When its longest unit outlasts
+  // kSplitRatio even shares of a workgroup (a stack of a few layers), the
+  // prefill GEMM, whose tiles end sooner and which may split long K, takes
+  // the stack instead; deeper stacks keep the lockstep kernel, which streams
+  // them faster.
+  if (p == TERN_PATH_MFMA && M > 8 && mfma_is_lockstep(kernel - SK_MFMA)) {
+    const int32_t v = kernel - SK_MFMA;
+    const int unit = mfma_unit_rows(v);
+    const double workers_v = (double)std::max(8, cus * mfma_per_cu(v) / 8 * 8);
+    double tot = 0.0, gm = 0.0;
+    for (int64_t i = 0; i < L; ++i) {
+      const tern_linear_desc& d = descs[i];
+      if (d.N == 0) continue;
+      const double ld = (double)row_bytes(d.K);
+      tot += (double)d.N * ld + 256.0 * (double)((d.N + unit - 1) / unit);
+      gm = std::max(gm, (double)std::min<int64_t>(unit, d.N) * ld + 256.0);
+    }
+    if (gm > kSplitRatio * tot / workers_v) kernel = (int32_t)SK_MFMA + mfma_gemm_variant((int32_t)M);
+  }
+  int per_cu = p == TERN_PATH_VALU ? valu_stack_blocks_per_cu(kernel) : mfma_per_cu(kernel - SK_MFMA);
   per_cu = std::min(per_cu, kMaxWavesPerCu / kWavesPerBlock);
   int over = 1;
   if (p == TERN_PATH_VALU) {

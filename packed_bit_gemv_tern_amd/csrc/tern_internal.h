@@ -117,6 +117,10 @@ int valu_stack_blocks_per_cu(int32_t kernel);
 // of the activation-window kernel (see mfma_win_offsets_fit)
 int32_t mfma_stack_variant(int32_t M, bool ragged, bool big);
 bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy);
+// the prefill GEMM's variant for M tokens (any M >= 1, any K), and whether
+// `variant` is the lockstep kernel (a workgroup takes whole rows over all K)
+int32_t mfma_gemm_variant(int32_t M);
+bool mfma_is_lockstep(int32_t variant);
 // the activation-window kernel: is `variant` it, and its window width in K
 bool mfma_is_window(int32_t variant);
 int mfma_window_k();

@@ -632,8 +632,14 @@ hipError_t launch_split_finish(const void* ws, const LaunchShape& shp, hipStream
 
 int mfma_window_k() { return kWinK; }
 
+int32_t mfma_gemm_variant(int32_t M) {
+  return gemm_tile_tokens(M) == 128 ? kGemm128Variant : kGemm64Variant;
+}
+
+bool mfma_is_lockstep(int32_t variant) { return variant >= 0 && variant < kWinVariant; }
+
 int32_t mfma_stack_variant(int32_t M, bool ragged, bool big) {
-  if (M > 16) return gemm_tile_tokens(M) == 128 ? kGemm128Variant : kGemm64Variant;
+  if (M > 16) return mfma_gemm_variant(M);
   if (M <= kWinTokens && !ragged && !big) return kWinVariant;
   return (ragged ? 2 : 0) | (M > 8 ? 4 : 0);
 }
