@@ -232,8 +232,14 @@ __device__ __forceinline__ void clear_zero_row(WgTiles<MQ>& L) {
 // 16*lane): load i brings rows 8i..8i+7 of the wave's 32 rows, lane l chunk
 // (l%8) ^ (row%8) of row 8i + l/8 of the K-step -- whole 128-byte lines per
 // instruction, and the XOR spreads the 16 lanes that later read one chunk of
-// 16 rows over the banks.  The next step's load is issued as soon as the
-// current tile has been read into registers.
+// 16 rows over the banks.  Two tiles per wave are in flight: a step's tile is
+// read into registers and the tile two steps ahead is issued into its slot.
+// The stack kernel holds its fp32 outputs in registers and stores them when
+// its run of work ends: output stores trickled into the saturated weight
+// stream slow it by about 1 us per MB, one burst at the end far less.  That
+// takes 2 waves per SIMD (256 VGPRs); two 4-wave workgroups per CU keep the
+// same 64 KB of weights in flight as four waves per SIMD with one tile each,
+// and one workgroup streams while the other restages its window.
 // Decode by code planes: word & (0x03030303 << 2k) holds the codes c = w + 1
 // of weights 4k..4k+3 of the word scaled by 4^k (the top plane is shifted
 // down instead), so plane k of four words is one MFMA operand for four ANDs.
@@ -247,8 +253,8 @@ constexpr int kWinK = 4096;    // activation window (K positions)
 constexpr int kWinPitch = kWinK + 16;
 constexpr int kWinTokens = 8;
 constexpr int kWinR = 2;       // row blocks of 16 per wave
-constexpr int kWinDepth = 1;   // weight tiles per wave (K-steps loaded ahead)
-constexpr int kWinWaves = 8;   // waves per workgroup
+constexpr int kWinDepth = 2;   // weight tiles per wave (K-steps in flight)
+constexpr int kWinWaves = 4;   // waves per workgroup
 constexpr int kWinBlock = 64 * kWinWaves;
 constexpr int kWinRows = kWinWaves * 16 * kWinR;
 constexpr int kWinTile = 16 * kWinR * kStepBytes;
@@ -286,6 +292,14 @@ __device__ __forceinline__ float settled(float x) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// Workgroup barrier for the activation window: the wave's LDS accesses are
+// complete and no memory access moves across it.  Unlike __syncthreads it
+// does not wait for the wave's global loads: the weight tiles in flight,
+// which land in the wave's own tile slots, never in the window.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // What the workgroup's window holds: the activations, zero points and scales
 // of one single-window linear, reused by the next segment when that reads the
 // same buffers (q == nullptr: nothing reusable is staged).
@@ -299,12 +313,53 @@ struct WinStaged {
   }
 };
 
+// Outputs held in registers until the worker's run ends (or the buffer is
+// full).  The 16 x 16 MFMA result of a row block holds tokens 0..7 twice
+// (activation rows 8..15 repeat 0..7), so lane (r, g) keeps row block g >> 1
+// of a unit, tokens 4 (g & 1) + v, v = 0..3: four registers per unit.
+template <int MAXU>
+struct OutBuf {
+  float v[MAXU > 0 ? MAXU : 1][4];
+  int n = 0;
+};
+// where a held unit goes (one entry per wave and held unit, in LDS)
+struct OutMeta {
+  float* y;
+  int32_t ldy, M, base, row_hi;
+  int32_t pad[2];
+};
+static_assert(sizeof(OutMeta) == 32, "OutMeta");
+// units a wave holds: 96 registers, what the kernel leaves free at 256
+constexpr int kOutUnits = 24;
+
+template <int MAXU>
+__device__ __forceinline__ void flush_out(OutBuf<MAXU>& ob, const OutMeta* meta, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < MAXU; ++i) {
+    if (i < ob.n) {
+      const OutMeta mt = meta[i];
+      const int row = mt.base + 16 * (g >> 1) + r;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * (g & 1) + v;
+        if (m < mt.M && row < mt.row_hi) {
+          const uint32_t off = ((uint32_t)m * (uint32_t)mt.ldy + (uint32_t)row) * 4u;
+          store_g(reinterpret_cast<float*>(reinterpret_cast<char*>(mt.y) + off), ob.v[i][v]);
+        }
+      }
+    }
+  }
+  ob.n = 0;
+}
+
 // SPLIT: segments may be windows of linears split along K (their flags say
 // so); compiled apart so that the kernel for unsplit stacks carries none of it.
-template <bool SPLIT>
+template <bool SPLIT, int MAXU>
 __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, int row_hi, int unit0,
                                                int ustride, int lane, int w, WinTiles& L,
-                                               WinStaged& staged, int flags) {
+                                               WinStaged& staged, int flags, OutBuf<MAXU>& ob,
+                                               OutMeta* meta) {
   constexpr int R = kWinR;
   constexpr int NLD = 16 * R / 8;  // 1 KB wave loads per K-step
   const int r = lane & 15, g = lane >> 4;
@@ -319,8 +374,10 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
 #pragma unroll
     for (int i = 0; i < NLD; ++i) src[i] = (uint32_t)min(base + 8 * i + lrow, row_hi - 1) * (uint32_t)a.ld;
   };
-  auto issue = [&](const uint32_t (&src)[NLD], int ks) {
-    uint8_t* tile = L.w[w][ks % kWinDepth];
+  // K-step ks of a unit into the slot of tile number t (tiles are numbered
+  // in the order the wave consumes them, across units)
+  auto issue = [&](const uint32_t (&src)[NLD], int ks, int t) {
+    uint8_t* tile = L.w[w][t % kWinDepth];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int ch = min(8 * ks + (lpos ^ ((8 * i + lrow) & 7)), nch - 1);
@@ -343,16 +400,20 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   float nsr[R];
 #pragma unroll
   for (int b = 0; b < R; ++b) nrs[b] = 0, nsr[b] = 0.0f;
+  // tiles in flight ahead of the one being consumed: never more than a
+  // unit's K-steps, so a lookahead reaches at most into the next unit
+  const int depth = min(kWinDepth, nks);
   if (row_lo + unit0 * kWinRows < row_hi) {
     unit_src(unit0, src);
 #pragma unroll
     for (int d = 0; d < kWinDepth; ++d)
-      if (d < nks) issue(src, d);
+      if (d < depth) issue(src, d, d);
     load_rowops(unit0, nrs, nsr);
   }
 
+  // tb: number of the unit's first tile
 #pragma unroll 1
-  for (int unit = unit0;; unit += ustride) {
+  for (int unit = unit0, tb = 0;; unit += ustride, tb += nks) {
     const int ubase = row_lo + unit * kWinRows;
     if (ubase >= row_hi) break;  // the same for every wave of the workgroup
     const int base = ubase + 16 * R * w;
@@ -365,25 +426,38 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
 #pragma unroll
     for (int b = 0; b < R; ++b) acc1[b] = acc4[b] = acc16[b] = i32x4{0, 0, 0, 0};
     for (int ks = 0; ks < nks; ++ks) {
-      const uint8_t* tile = L.w[w][ks % kWinDepth];
+      const uint8_t* tile = L.w[w][(tb + ks) % kWinDepth];
       if ((ks & 7) == 0) {
         const int win = ks >> 3;
         // a single-window linear whose activations are already staged (the
         // same buffers, e.g. the previous unit) skips the restaging
         if (nwin > 1 || !staged.holds(a)) {
           // every wave is done with the previous window before it is replaced
-          __syncthreads();
-          for (int e = threadIdx.x; e < kWinTokens * (kWinK / 16); e += blockDim.x) {
-            const int tq = e / (kWinK / 16), off = 16 * (e % (kWinK / 16));
-            const int pos = win * kWinK + off;  // K position
-            u32x4 v = u32x4{0, 0, 0, 0};
-            if (tq < M && pos < K) v = load16(a.q + (int64_t)tq * a.ldq + pos);
-            // word j = (off % 64) / 16 of its chunk: dword k goes to 16k + 4j
-            uint32_t* dst = reinterpret_cast<uint32_t*>(&L.q[tq][off & ~63]) + ((off % 64) / 16);
+          lds_barrier();
+          {
+            // all of a thread's window loads first, then the LDS writes
+            constexpr int NE = kWinTokens * (kWinK / 16) / kWinBlock;
+            static_assert(NE * kWinBlock == kWinTokens * (kWinK / 16), "window split");
+            u32x4 rv[NE];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) dst[4 * k] = v[k];
+            for (int i = 0; i < NE; ++i) {
+              const int e = threadIdx.x + i * kWinBlock;
+              const int tq = e / (kWinK / 16), off = 16 * (e % (kWinK / 16));
+              const int pos = win * kWinK + off;  // K position
+              rv[i] = u32x4{0, 0, 0, 0};
+              if (tq < M && pos < K) rv[i] = load16(a.q + (int64_t)tq * a.ldq + pos);
+            }
+#pragma unroll
+            for (int i = 0; i < NE; ++i) {
+              const int e = threadIdx.x + i * kWinBlock;
+              const int tq = e / (kWinK / 16), off = 16 * (e % (kWinK / 16));
+              // word j = (off % 64) / 16 of its chunk: dword k goes to 16k + 4j
+              uint32_t* dst = reinterpret_cast<uint32_t*>(&L.q[tq][off & ~63]) + ((off % 64) / 16);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) dst[4 * k] = rv[i][k];
+            }
           }
-          __syncthreads();
+          lds_barrier();
           // per-token activation sums of this window; wave w owns tokens
           // w, w + kWinWaves, ... so no two waves write one entry
           for (int tq = w; tq < kWinTokens; tq += kWinWaves) {
@@ -401,7 +475,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
             L.z[tq] = tq < M ? load_g(a.z + tq) : 0;
             L.s_act[tq] = tq < M ? load_g(a.s_act + tq) : 0.0f;
           }
-          __syncthreads();
+          lds_barrier();
           staged.q = nwin > 1 ? nullptr : a.q;
           staged.z = a.z;
           staged.s_act = a.s_act;
@@ -409,8 +483,10 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
           staged.ldq = a.ldq;
         }
       }
-      // this step's weight tile has landed (later steps' loads may still fly)
-      if (kWinDepth > 1 && ks + 1 < nks)
+      // this step's weight tile has landed: when the next tile's NLD loads
+      // were issued after it (they complete in order; stores in between
+      // only add to the count), at most NLD may still be in flight
+      if (depth > 1 && (ks + 1 < nks || has_next))
         wait_vm<(kWinDepth > 1 ? NLD : 0)>();
       else
         wait_vm<0>();
@@ -430,10 +506,10 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
           wv[b][half] = *reinterpret_cast<const u32x4*>(
               tile + (16 * b + r) * kStepBytes + 16 * ((2 * g + half) ^ (r & 7)));
       wait_lgkm();  // tile read: it may be overwritten
-      if (ks + kWinDepth < nks)
-        issue(src, ks + kWinDepth);
-      else if (has_next && ks + kWinDepth - nks < nks)
-        issue(nsrc, ks + kWinDepth - nks);  // the next unit's first tiles
+      if (ks + depth < nks)
+        issue(src, ks + depth, tb + ks + depth);
+      else if (has_next)
+        issue(nsrc, ks + depth - nks, tb + ks + depth);  // the next unit's first tiles
       // activations come from the window, which the loads never overwrite
       const uint8_t* qrow = &L.q[r & 7][64 * (8 * (ks & 7) + 2 * g)];
 #pragma unroll
@@ -461,6 +537,44 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
     // term belongs to one window only.
     const bool partial = SPLIT && (flags & kSegPartial) != 0;
     const bool zpoint = !partial || (flags & kSegZeroPoint) != 0;
+    // held outputs: every unit that stores y only (a split window's partial
+    // sums and linears that also return acc are stored at once, below)
+    if (MAXU > 0 && !partial && !a.acc) {
+      static_assert(kWinR == 2, "one row block per half-wave");
+      const int bs = g >> 1;
+      const int32_t rsel = bs ? rs[1] : rs[0];
+      const float ssel = bs ? sr[1] : sr[0];
+      float vals[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * (g & 1) + v;
+        const int32_t c1 = bs ? acc1[1][v] : acc1[0][v];
+        const int32_t c4 = bs ? acc4[1][v] : acc4[0][v];
+        const int32_t c16 = bs ? acc16[1][v] : acc16[0][v];
+        const int32_t cq = c1 + (c4 >> 2) + (c16 >> 4);
+        const int32_t accv = (int32_t)((uint32_t)cq - (uint32_t)L.qsum[m] - (uint32_t)L.z[m] * (uint32_t)rsel);
+        vals[v] = epilogue(ssel, accv, L.s_act[m]);
+      }
+      if (ob.n == MAXU) flush_out(ob, meta, lane);
+#pragma unroll
+      for (int i = 0; i < MAXU; ++i)
+        if (i == ob.n) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) ob.v[i][v] = vals[v];
+        }
+      OutMeta mt;
+      mt.y = a.y;
+      mt.ldy = a.ldy;
+      mt.M = M;
+      mt.base = base;
+      mt.row_hi = row_hi;
+      mt.pad[0] = mt.pad[1] = 0;
+      meta[ob.n] = mt;  // every lane writes the same entry
+      ob.n = ob.n + 1;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) src[i] = nsrc[i];
+      continue;
+    }
     int32_t zt[4];
     float sa[4];
 #pragma unroll
@@ -545,12 +659,17 @@ __global__ __launch_bounds__(kBlock) void mfma_wg_stack_kernel(const StackHeader
 __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void mfma_win_linear_kernel(LinearArgs a) {
   __shared__ __attribute__((aligned(16))) WinTiles L;
   WinStaged staged;
-  mfma_win_range<false>(a, 0, a.N, blockIdx.x, gridDim.x, threadIdx.x & 63, wave_id_uniform(), L, staged, 0);
+  OutBuf<0> ob;
+  mfma_win_range<false, 0>(a, 0, a.N, blockIdx.x, gridDim.x, threadIdx.x & 63, wave_id_uniform(), L, staged, 0,
+                           ob, nullptr);
 }
 
+// The stack kernel: a worker's segments in order, y-only outputs held in
+// registers (kOutUnits units per wave) and stored at the end of the run.
 template <bool SPLIT>
-__global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void mfma_win_stack_kernel(const StackHeader* __restrict__ h) {
+__global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_win_stack_kernel(const StackHeader* __restrict__ h) {
   __shared__ __attribute__((aligned(16))) WinTiles L;
+  __shared__ OutMeta meta[kWinWaves][kOutUnits];
   const int worker = xcd_logical_block();
   if (worker >= h->workers) return;  // the same for the whole workgroup
   const int lane = threadIdx.x & 63;
@@ -561,11 +680,14 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4)
   const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
   const int s1 = seg_start[worker + 1];
   WinStaged staged;
+  OutBuf<kOutUnits> ob;
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
-    mfma_win_range<SPLIT>(a, sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged, SPLIT ? sg.flags : 0);
+    mfma_win_range<SPLIT, kOutUnits>(a, sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged, SPLIT ? sg.flags : 0,
+                                     ob, meta[w]);
   }
+  flush_out(ob, meta[w], lane);
 }
 
 // Linears split along K: before the main kernel their outputs are cleared

@@ -23,9 +23,11 @@ def stack():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("M", [1, 8])
-def test_full_8b_stack_sampled(stack, M):
-    b = stack.bind(M, with_acc=True)
+@pytest.mark.parametrize("M,with_acc", [(1, True), (8, True), (1, False), (8, False)])
+def test_full_8b_stack_sampled(stack, M, with_acc):
+    # y only is the benchmark's configuration; at M = 8 its outputs are held
+    # in registers until each worker's run ends
+    b = stack.bind(M, with_acc=with_acc)
     assert b.plan.L == 252
     assert b.plan.splits == 0  # a full stack keeps every linear whole
     b.run()
@@ -41,9 +43,9 @@ def test_full_8b_stack_sampled(stack, M):
         assert np.array_equal(got_packed, rp), pl.name
         assert np.array_equal(pl.rowsum.cpu().numpy()[rows], rr), pl.name
         racc, ry32, ry64 = oracle.linear(rp, pl.sample_s_row, rr, pl.K, q, s_act, z)
-        acc = b.acc[i].cpu().numpy()[:, rows]
+        if with_acc:
+            assert np.array_equal(b.acc[i].cpu().numpy()[:, rows], racc), pl.name
         y = b.y[i].cpu().numpy()[:, rows]
-        assert np.array_equal(acc, racc), pl.name
         assert np.all(np.abs(y.astype(np.float64) - ry64) <= RTOL * np.abs(ry64)), pl.name
         assert np.array_equal(y.view(np.uint32), ry32.view(np.uint32)), pl.name
         checked += rows.size

@@ -285,6 +285,60 @@ def test_stack_split_ragged_k_prefill(M):
         assert_parity(y, acc, oracle_ref(lin), "split %s M=%d" % (lin.name, M))
 
 
+# Stacks whose linears return y only: the activation-window kernel (M <= 8)
+# holds such outputs in registers until a worker's run ends (every other
+# stack test also asks for acc, which is stored at once).
+
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
+def test_stack_y_only(M):
+    lins = synth.make_stack(4, M, model="0.6b", layers=2, threads=8)
+    ups = [Uploaded(lin, ldy_extra=3, with_acc=False) for lin in lins]
+    ws = torch.empty(tern.tern_linear_stack_workspace_bytes(len(ups), M), dtype=torch.uint8, device=DEV)
+    plan = tern.tern_linear_stack_prepare([u.desc() for u in ups], M, ws)
+    tern.tern_linear_stack(plan)
+    tern.tern_linear_stack(plan)
+    for lin, up in zip(lins, ups):
+        y, acc = up.results()
+        assert acc is None
+        assert_parity(y, None, oracle_ref(lin), "y-only %s M=%d" % (lin.name, M))
+        assert torch.isnan(up.y[:, lin.N:]).all()  # nothing past N written
+
+
+@pytest.mark.parametrize("M", [4, 8])
+def test_stack_y_only_8b_layer_and_mixed_acc(M):
+    # one 8B layer (its down projection is split: partial sums stored at
+    # once beside held outputs); every other linear also asks for acc
+    lins, _ = _stack_case("8b", 1, M, seed=6)
+    ups = [Uploaded(lin, ldy_extra=1, with_acc=(i % 2 == 1)) for i, lin in enumerate(lins)]
+    ws = torch.empty(tern.tern_linear_stack_workspace_bytes(len(ups), M), dtype=torch.uint8, device=DEV)
+    plan = tern.tern_linear_stack_prepare([u.desc() for u in ups], M, ws)
+    assert plan.splits == 1
+    for _ in range(2):
+        tern.tern_linear_stack(plan)
+    for lin, up in zip(lins, ups):
+        y, acc = up.results()
+        assert_parity(y, acc, oracle_ref(lin), "8b mixed %s M=%d" % (lin.name, M))
+        assert torch.isnan(up.y[:, lin.N:]).all()
+
+
+def test_stack_y_only_more_rows_than_held():
+    # K = 64 rows are cheap, so each worker takes far more 128-row units than
+    # the 24 a wave holds: the held outputs are stored when the buffer fills
+    # as well as at the end of the run
+    M = 8
+    specs = [(1000003, 64, 1), (999997, 64, 2), (300, 4096, 3)]
+    lins = [synth.make_linear(21, s, 0, N, K, 0.626, M, "o%d" % s) for (N, K, s) in specs]
+    ups = [Uploaded(lin, with_acc=False) for lin in lins]
+    ws = torch.empty(tern.tern_linear_stack_workspace_bytes(len(ups), M), dtype=torch.uint8, device=DEV)
+    plan = tern.tern_linear_stack_prepare([u.desc() for u in ups], M, ws)
+    units = sum(-(-N // 128) for (N, _, _) in specs)
+    assert units > 24 * plan.workers * 1.2, (units, plan.workers)
+    tern.tern_linear_stack(plan)
+    for lin, up in zip(lins, ups):
+        y, _ = up.results()
+        assert_parity(y, None, oracle_ref(lin), "overflow %s" % lin.name)
+
+
 def test_stack_mixed_shapes_and_empty_linear():
     specs = [(5, 1, 1), (300, 4096, 2), (0, 64, 3), (77, 100, 4), (40, 12288, 5), (129, 1000, 6)]
     for M in (1, 3, 8, 12, 40, 130):
