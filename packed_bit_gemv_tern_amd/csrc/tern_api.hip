@@ -395,13 +395,13 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   auto mfma_per_cu = [&](int32_t v) {
     return std::min(mfma_stack_blocks_per_cu(v), kMaxWavesPerCu / kWavesPerBlock);
   };
-  // The lockstep kernel at 9..16 tokens keeps a workgroup on one unit of
-  // rows for the linear's whole K.  When its longest unit outlasts
+  // The kernels at 9..16 tokens keep a workgroup on one unit of rows for
+  // the linear's whole K.  When the longest unit outlasts
   // kSplitRatio even shares of a workgroup (a stack of a few layers), the
   // prefill GEMM, whose tiles end sooner and which may split long K, takes
-  // the stack instead; deeper stacks keep the lockstep kernel, which streams
-  // them faster.
-  if (p == TERN_PATH_MFMA && M > 8 && mfma_is_lockstep(kernel - SK_MFMA)) {
+  // the stack instead; deeper stacks keep their kernel, which streams them
+  // faster.
+  if (p == TERN_PATH_MFMA && M > 8 && (mfma_is_lockstep(kernel - SK_MFMA) || mfma_is_window(kernel - SK_MFMA))) {
     const int32_t v = kernel - SK_MFMA;
     const int unit = mfma_unit_rows(v);
     const double workers_v = (double)std::max(8, cus * mfma_per_cu(v) / 8 * 8);

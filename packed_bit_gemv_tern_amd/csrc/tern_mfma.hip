@@ -257,14 +257,25 @@ constexpr int kWinDepth = 2;   // weight tiles per wave (K-steps in flight)
 constexpr int kWinWaves = 4;   // waves per workgroup
 constexpr int kWinBlock = 64 * kWinWaves;
 constexpr int kWinRows = kWinWaves * 16 * kWinR;
+// Geometry per staged token count: the 16-token window (66 KB) leaves room
+// for one workgroup per CU, so that kernel runs 8 waves to keep the same
+// weight tiles in flight.
+template <int T>
+struct WinGeo {
+  static_assert(T == 8 || T == 16, "window tokens");
+  static constexpr int WAVES = T == 16 ? 8 : kWinWaves;
+  static constexpr int BLOCK = 64 * WAVES;
+  static constexpr int ROWS = WAVES * 16 * kWinR;
+};
 constexpr int kWinTile = 16 * kWinR * kStepBytes;
 
+template <int T>
 struct WinTiles {
-  uint8_t w[kWinWaves][kWinDepth][kWinTile];
-  uint8_t q[kWinTokens][kWinPitch];  // each 64-byte chunk stored dword-transposed
-  int32_t qsum[kWinTokens];          // sum of the token's activations over all of K
-  int32_t z[kWinTokens];             // zero points and scales of the staged tokens
-  float s_act[kWinTokens];
+  uint8_t w[WinGeo<T>::WAVES][kWinDepth][kWinTile];
+  uint8_t q[T][kWinPitch];  // each 64-byte chunk stored dword-transposed
+  int32_t qsum[T];          // sum of the token's activations over all of K
+  int32_t z[T];             // zero points and scales of the staged tokens
+  float s_act[T];
 };
 
 // s_waitcnt on this wave's global loads (LDS DMA included): at most N still
@@ -355,13 +366,16 @@ __device__ __forceinline__ void flush_out(OutBuf<MAXU>& ob, const OutMeta* meta,
 
 // SPLIT: segments may be windows of linears split along K (their flags say
 // so); compiled apart so that the kernel for unsplit stacks carries none of it.
-template <bool SPLIT, int MAXU>
+// T: tokens staged (8: activation rows 8..15 of the MFMA repeat 0..7; 16).
+template <bool SPLIT, int MAXU, int T>
 __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, int row_hi, int unit0,
-                                               int ustride, int lane, int w, WinTiles& L,
+                                               int ustride, int lane, int w, WinTiles<T>& L,
                                                WinStaged& staged, int flags, OutBuf<MAXU>& ob,
                                                OutMeta* meta) {
   constexpr int R = kWinR;
   constexpr int NLD = 16 * R / 8;  // 1 KB wave loads per K-step
+  constexpr int ROWS = WinGeo<T>::ROWS, BLOCK = WinGeo<T>::BLOCK, WAVES = WinGeo<T>::WAVES;
+  static_assert(MAXU == 0 || T == 8, "held outputs use the repeated half of the MFMA result");
   const int r = lane & 15, g = lane >> 4;
   const int lrow = lane >> 3, lpos = lane & 7;
   const int nch = a.nch, K = a.K, M = a.M;
@@ -370,7 +384,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   // byte offsets (below 2^32: checked by the host) of the wave's weight rows
   // within a unit, and the chunk each lane brings
   auto unit_src = [&](int unit, uint32_t (&src)[NLD]) {
-    const int base = row_lo + unit * kWinRows + 16 * R * w;
+    const int base = row_lo + unit * ROWS + 16 * R * w;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) src[i] = (uint32_t)min(base + 8 * i + lrow, row_hi - 1) * (uint32_t)a.ld;
   };
@@ -387,7 +401,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   };
   // rowsum and s_row of a unit's rows, loaded one unit ahead
   auto load_rowops = [&](int unit, int32_t (&rs)[R], float (&sr)[R]) {
-    const int base = row_lo + unit * kWinRows + 16 * R * w;
+    const int base = row_lo + unit * ROWS + 16 * R * w;
 #pragma unroll
     for (int b = 0; b < R; ++b) {
       const int row = min(base + 16 * b + r, row_hi - 1);
@@ -403,7 +417,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   // tiles in flight ahead of the one being consumed: never more than a
   // unit's K-steps, so a lookahead reaches at most into the next unit
   const int depth = min(kWinDepth, nks);
-  if (row_lo + unit0 * kWinRows < row_hi) {
+  if (row_lo + unit0 * ROWS < row_hi) {
     unit_src(unit0, src);
 #pragma unroll
     for (int d = 0; d < kWinDepth; ++d)
@@ -414,10 +428,10 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   // tb: number of the unit's first tile
 #pragma unroll 1
   for (int unit = unit0, tb = 0;; unit += ustride, tb += nks) {
-    const int ubase = row_lo + unit * kWinRows;
+    const int ubase = row_lo + unit * ROWS;
     if (ubase >= row_hi) break;  // the same for every wave of the workgroup
     const int base = ubase + 16 * R * w;
-    const bool has_next = ubase + ustride * kWinRows < row_hi;
+    const bool has_next = ubase + ustride * ROWS < row_hi;
     uint32_t nsrc[NLD];
     if (has_next) unit_src(unit + ustride, nsrc);
     int32_t rs[R];
@@ -436,12 +450,12 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
           lds_barrier();
           {
             // all of a thread's window loads first, then the LDS writes
-            constexpr int NE = kWinTokens * (kWinK / 16) / kWinBlock;
-            static_assert(NE * kWinBlock == kWinTokens * (kWinK / 16), "window split");
+            constexpr int NE = T * (kWinK / 16) / BLOCK;
+            static_assert(NE * BLOCK == T * (kWinK / 16), "window split");
             u32x4 rv[NE];
 #pragma unroll
             for (int i = 0; i < NE; ++i) {
-              const int e = threadIdx.x + i * kWinBlock;
+              const int e = threadIdx.x + i * BLOCK;
               const int tq = e / (kWinK / 16), off = 16 * (e % (kWinK / 16));
               const int pos = win * kWinK + off;  // K position
               rv[i] = u32x4{0, 0, 0, 0};
@@ -449,7 +463,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
             }
 #pragma unroll
             for (int i = 0; i < NE; ++i) {
-              const int e = threadIdx.x + i * kWinBlock;
+              const int e = threadIdx.x + i * BLOCK;
               const int tq = e / (kWinK / 16), off = 16 * (e % (kWinK / 16));
               // word j = (off % 64) / 16 of its chunk: dword k goes to 16k + 4j
               uint32_t* dst = reinterpret_cast<uint32_t*>(&L.q[tq][off & ~63]) + ((off % 64) / 16);
@@ -459,8 +473,8 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
           }
           lds_barrier();
           // per-token activation sums of this window; wave w owns tokens
-          // w, w + kWinWaves, ... so no two waves write one entry
-          for (int tq = w; tq < kWinTokens; tq += kWinWaves) {
+          // w, w + WAVES, ... so no two waves write one entry
+          for (int tq = w; tq < T; tq += WAVES) {
             uint32_t part = 0;
             for (int off = 16 * lane; off < kWinK; off += 16 * 64) {
               const u32x4 v = *reinterpret_cast<const u32x4*>(&L.q[tq][off]);
@@ -470,7 +484,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
             const int32_t tot = (int32_t)group_sum<64>(part);
             if (lane == 0) L.qsum[tq] = (win == 0 ? 0 : L.qsum[tq]) + tot;
           }
-          if (win == 0 && threadIdx.x < kWinTokens) {
+          if (win == 0 && threadIdx.x < T) {
             const int tq = threadIdx.x;
             L.z[tq] = tq < M ? load_g(a.z + tq) : 0;
             L.s_act[tq] = tq < M ? load_g(a.s_act + tq) : 0.0f;
@@ -511,7 +525,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
       else if (has_next)
         issue(nsrc, ks + depth - nks, tb + ks + depth);  // the next unit's first tiles
       // activations come from the window, which the loads never overwrite
-      const uint8_t* qrow = &L.q[r & 7][64 * (8 * (ks & 7) + 2 * g)];
+      const uint8_t* qrow = &L.q[r & (T - 1)][64 * (8 * (ks & 7) + 2 * g)];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         u32x4 qv[4];
@@ -579,8 +593,8 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
     float sa[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      zt[v] = zpoint ? L.z[(4 * g + v) & 7] : 0;
-      sa[v] = L.s_act[(4 * g + v) & 7];
+      zt[v] = zpoint ? L.z[(4 * g + v) & (T - 1)] : 0;
+      sa[v] = L.s_act[(4 * g + v) & (T - 1)];
     }
 #pragma unroll
     for (int b = 0; b < R; ++b) {
@@ -657,10 +671,10 @@ __global__ __launch_bounds__(kBlock) void mfma_wg_stack_kernel(const StackHeader
 
 // M <= 8, every K a multiple of 64: the activation-window kernel.
 __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void mfma_win_linear_kernel(LinearArgs a) {
-  __shared__ __attribute__((aligned(16))) WinTiles L;
+  __shared__ __attribute__((aligned(16))) WinTiles<8> L;
   WinStaged staged;
   OutBuf<0> ob;
-  mfma_win_range<false, 0>(a, 0, a.N, blockIdx.x, gridDim.x, threadIdx.x & 63, wave_id_uniform(), L, staged, 0,
+  mfma_win_range<false, 0, 8>(a, 0, a.N, blockIdx.x, gridDim.x, threadIdx.x & 63, wave_id_uniform(), L, staged, 0,
                            ob, nullptr);
 }
 
@@ -668,7 +682,7 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4)
 // registers (kOutUnits units per wave) and stored at the end of the run.
 template <bool SPLIT>
 __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_win_stack_kernel(const StackHeader* __restrict__ h) {
-  __shared__ __attribute__((aligned(16))) WinTiles L;
+  __shared__ __attribute__((aligned(16))) WinTiles<8> L;
   __shared__ OutMeta meta[kWinWaves][kOutUnits];
   const int worker = xcd_logical_block();
   if (worker >= h->workers) return;  // the same for the whole workgroup
@@ -684,10 +698,35 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2)
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
-    mfma_win_range<SPLIT, kOutUnits>(a, sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged, SPLIT ? sg.flags : 0,
+    mfma_win_range<SPLIT, kOutUnits, 8>(a, sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged, SPLIT ? sg.flags : 0,
                                      ob, meta[w]);
   }
   flush_out(ob, meta[w], lane);
+}
+
+// 9 <= M <= 16 tokens, every K a multiple of 64: the same window kernel with
+// all 16 activation rows staged, one 8-wave workgroup per CU, outputs stored
+// at once.  (Only SPLIT = false is launched.)
+template <bool SPLIT>
+__global__ __launch_bounds__(WinGeo<16>::BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_win16_stack_kernel(
+    const StackHeader* __restrict__ h) {
+  __shared__ __attribute__((aligned(16))) WinTiles<16> L;
+  const int worker = xcd_logical_block();
+  if (worker >= h->workers) return;  // the same for the whole workgroup
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id_uniform();
+  const char* base = reinterpret_cast<const char*>(h);
+  const LinearArgs* lin = reinterpret_cast<const LinearArgs*>(base + h->off_lin);
+  const int32_t* seg_start = reinterpret_cast<const int32_t*>(base + h->off_seg_start);
+  const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
+  const int s1 = seg_start[worker + 1];
+  WinStaged staged;
+  OutBuf<0> ob;
+  for (int s = seg_start[worker]; s < s1; ++s) {
+    const Segment sg = seg[s];
+    mfma_win_range<SPLIT, 0, 16>(lin[sg.lin], sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged,
+                                 SPLIT ? sg.flags : 0, ob, nullptr);
+  }
 }
 
 // Linears split along K: before the main kernel their outputs are cleared
@@ -728,14 +767,17 @@ __global__ __launch_bounds__(256) void split_finish_kernel(const StackHeader* __
 constexpr int32_t kWinVariant = 8;
 constexpr int32_t kGemm64Variant = 9;
 constexpr int32_t kGemm128Variant = 10;
+constexpr int32_t kWin16Variant = 11;  // the window kernel for 9 <= M <= 16
 
 bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy) {
   // weight row offsets and output byte offsets are 32-bit in that kernel
   return N * ld < (1ll << 32) && M * ldy * 4 < (1ll << 32);
 }
 
-bool mfma_is_window(int32_t variant) { return variant == kWinVariant; }
+bool mfma_is_window(int32_t variant) { return variant == kWinVariant || variant == kWin16Variant; }
 
+// (the 16-token window kernel never splits: stacks small enough to want it
+// take the prefill GEMM at 9..16 tokens)
 bool mfma_can_split(int32_t variant) {
   return variant == kWinVariant || variant == kGemm64Variant || variant == kGemm128Variant;
 }
@@ -763,6 +805,7 @@ bool mfma_is_lockstep(int32_t variant) { return variant >= 0 && variant < kWinVa
 int32_t mfma_stack_variant(int32_t M, bool ragged, bool big) {
   if (M > 16) return mfma_gemm_variant(M);
   if (M <= kWinTokens && !ragged && !big) return kWinVariant;
+  if (M <= 16 && !ragged && !big) return kWin16Variant;
   return (ragged ? 2 : 0) | (M > 8 ? 4 : 0);
 }
 
@@ -776,13 +819,14 @@ bool mfma_per_workgroup(int32_t) { return true; }
 
 int mfma_unit_rows(int32_t variant) {
   if (variant == kWinVariant) return kWinRows;
+  if (variant == kWin16Variant) return WinGeo<16>::ROWS;
   if (variant == kGemm64Variant || variant == kGemm128Variant)
     return gemm_unit_rows(variant == kGemm128Variant ? 128 : 64);
   return kWgRows;
 }
 
 int mfma_unit_restages(int32_t variant, int64_t K) {
-  return variant == kWinVariant && K > kWinK ? (int)((K + kWinK - 1) / kWinK) : 0;
+  return mfma_is_window(variant) && K > kWinK ? (int)((K + kWinK - 1) / kWinK) : 0;
 }
 
 template <typename F>
@@ -793,13 +837,15 @@ static hipError_t with_mfma_stack_kernel(int32_t variant, F&& f) {
     case 4: return f(mfma_wg_stack_kernel<16, false>);
     case 6: return f(mfma_wg_stack_kernel<16, true>);
     case kWinVariant: return f(mfma_win_stack_kernel<false>);
+    case kWin16Variant: return f(mfma_win16_stack_kernel<false>);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
-  const int32_t v = mfma_stack_variant(a.M, (a.K & 63) != 0, !mfma_win_offsets_fit(a.N, a.ld, a.M, a.ldy));
+  int32_t v = mfma_stack_variant(a.M, (a.K & 63) != 0, !mfma_win_offsets_fit(a.N, a.ld, a.M, a.ldy));
   if (v == kGemm64Variant || v == kGemm128Variant) return launch_gemm_linear(a, s);
+  if (v == kWin16Variant) v = 4;  // one linear at 9..16 tokens: the lockstep kernel
   const int64_t units = (a.N + mfma_unit_rows(v) - 1) / mfma_unit_rows(v);
   int64_t blocks = units;
   if (blocks > 8192) blocks = 8192;
@@ -820,7 +866,9 @@ hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape&
   if (variant == kGemm64Variant || variant == kGemm128Variant)
     return launch_gemm_stack(variant == kGemm128Variant ? 128 : 64, ws, shp, s);
   const StackHeader* h = static_cast<const StackHeader*>(ws);
-  const dim3 grid(shp.grid), block(variant == kWinVariant ? kWinBlock : shp.block);
+  const dim3 grid(shp.grid), block(variant == kWinVariant     ? kWinBlock
+                                    : variant == kWin16Variant ? WinGeo<16>::BLOCK
+                                                               : shp.block);
   const bool split = variant == kWinVariant && shp.splits > 0;
   if (split) {
     const hipError_t e = launch_split_clear(ws, shp, s);
@@ -844,7 +892,7 @@ int mfma_stack_blocks_per_cu(int32_t variant) {
   if (variant == kGemm64Variant || variant == kGemm128Variant)
     return gemm_stack_blocks_per_cu(variant == kGemm128Variant ? 128 : 64);
   int n = 0;
-  const int block = variant == kWinVariant ? kWinBlock : kBlock;
+  const int block = variant == kWinVariant ? kWinBlock : variant == kWin16Variant ? WinGeo<16>::BLOCK : kBlock;
   const hipError_t e = with_mfma_stack_kernel(variant, [&](auto kern) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, block, 0);
   });

@@ -23,7 +23,7 @@ def stack():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("M,with_acc", [(1, True), (8, True), (1, False), (8, False)])
+@pytest.mark.parametrize("M,with_acc", [(1, True), (8, True), (1, False), (8, False), (16, False)])
 def test_full_8b_stack_sampled(stack, M, with_acc):
     # y only is the benchmark's configuration; at M = 8 its outputs are held
     # in registers until each worker's run ends

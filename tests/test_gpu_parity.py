@@ -339,6 +339,25 @@ def test_stack_y_only_more_rows_than_held():
         assert_parity(y, None, oracle_ref(lin), "overflow %s" % lin.name)
 
 
+@pytest.mark.parametrize("M", [9, 12, 16])
+@pytest.mark.parametrize("with_acc", [True, False])
+def test_stack_16_token_window(M, with_acc):
+    # six 0.6B layers at 9..16 tokens: the window kernel with all 16
+    # activation rows staged, one workgroup per CU; launched twice
+    lins = synth.make_stack(8, M, model="0.6b", layers=6, threads=8)
+    ups = [Uploaded(lin, ldy_extra=3, with_acc=with_acc) for lin in lins]
+    ws = torch.empty(tern.tern_linear_stack_workspace_bytes(len(ups), M), dtype=torch.uint8, device=DEV)
+    plan = tern.tern_linear_stack_prepare([u.desc() for u in ups], M, ws)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert plan.splits == 0 and plan.grid == cus // 8 * 8, (plan.grid, cus)
+    tern.tern_linear_stack(plan)
+    tern.tern_linear_stack(plan)
+    for lin, up in zip(lins, ups):
+        y, acc = up.results()
+        assert_parity(y, acc, oracle_ref(lin), "16-token %s M=%d" % (lin.name, M))
+        assert torch.isnan(up.y[:, lin.N:]).all()
+
+
 def test_stack_mixed_shapes_and_empty_linear():
     specs = [(5, 1, 1), (300, 4096, 2), (0, 64, 3), (77, 100, 4), (40, 12288, 5), (129, 1000, 6)]
     for M in (1, 3, 8, 12, 40, 130):
