@@ -91,6 +91,8 @@ def kernel_name(plan) -> str:
         return "mfma_win_stack_kernel<%s>" % ("true" if getattr(plan, "splits", 0) else "false")
     if v in (9, 10):
         return "gemm_stack_kernel<%d>" % (64 if v == 9 else 128)
+    if v == 11:
+        return "mfma_win16_stack_kernel<false>"
     ragged = "true" if v & 2 else "false"
     if v & 1:
         return "mfma_stack_kernel<4, %s>" % ragged
@@ -523,6 +525,12 @@ def suite(args):
               "M": M, "eager": _stats(eager, db), "graph_replay": _stats(replay, db),
               "note": "three kernel launches; the stack's linears take independent synthetic activations"})
         del b, g, xd, logits
+    # --- the same 252-linear stack at 16 tokens (a longer verify pass), one launch
+    b16 = st.bind(16)
+    us = _event_times(lambda i: b16.run(), 20)
+    emit({"suite": "stack8b_m16", "workload": "full 8B-shaped stack (252 linears) at M = 16, one stack launch",
+          "M": 16, "kernel": kernel_name(b16.plan), **_stats(us, b16.bytes)})
+    del b16
     del st, Whd, srhd, rshd
     torch.cuda.empty_cache()
 
