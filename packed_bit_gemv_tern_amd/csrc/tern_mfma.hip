@@ -328,9 +328,11 @@ struct WinStaged {
 // full).  The 16 x 16 MFMA result of a row block holds tokens 0..7 twice
 // (activation rows 8..15 repeat 0..7), so lane (r, g) keeps row block g >> 1
 // of a unit, tokens 4 (g & 1) + v, v = 0..3: four registers per unit.
-template <int MAXU>
+// NV values per unit and lane: 4 with 8 tokens staged, 8 (both row blocks)
+// with 16.
+template <int MAXU, int NV = 4>
 struct OutBuf {
-  float v[MAXU > 0 ? MAXU : 1][4];
+  float v[MAXU > 0 ? MAXU : 1][NV];
   int n = 0;
 };
 // where a held unit goes (one entry per wave and held unit, in LDS)
@@ -340,23 +342,26 @@ struct OutMeta {
   int32_t pad[2];
 };
 static_assert(sizeof(OutMeta) == 32, "OutMeta");
-// units a wave holds: 96 registers, what the kernel leaves free at 256
-constexpr int kOutUnits = 24;
+// units a wave holds: what each kernel leaves free at 256 VGPRs (96 and
+// 112 registers)
+constexpr int kOutUnits = 24, kOut16Units = 14;
 
-template <int MAXU>
-__device__ __forceinline__ void flush_out(OutBuf<MAXU>& ob, const OutMeta* meta, int lane) {
+// value j of a held unit: with 8 tokens row block g >> 1, token
+// 4 (g & 1) + j; with 16, row block j >> 2, token 4 g + (j & 3)
+template <int MAXU, int NV>
+__device__ __forceinline__ void flush_out(OutBuf<MAXU, NV>& ob, const OutMeta* meta, int lane) {
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < MAXU; ++i) {
     if (i < ob.n) {
       const OutMeta mt = meta[i];
-      const int row = mt.base + 16 * (g >> 1) + r;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = 4 * (g & 1) + v;
+      for (int j = 0; j < NV; ++j) {
+        const int row = mt.base + 16 * (NV == 4 ? g >> 1 : j >> 2) + r;
+        const int m = NV == 4 ? 4 * (g & 1) + j : 4 * g + (j & 3);
         if (m < mt.M && row < mt.row_hi) {
           const uint32_t off = ((uint32_t)m * (uint32_t)mt.ldy + (uint32_t)row) * 4u;
-          store_g(reinterpret_cast<float*>(reinterpret_cast<char*>(mt.y) + off), ob.v[i][v]);
+          store_g(reinterpret_cast<float*>(reinterpret_cast<char*>(mt.y) + off), ob.v[i][j]);
         }
       }
     }
@@ -370,12 +375,11 @@ __device__ __forceinline__ void flush_out(OutBuf<MAXU>& ob, const OutMeta* meta,
 template <bool SPLIT, int MAXU, int T>
 __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, int row_hi, int unit0,
                                                int ustride, int lane, int w, WinTiles<T>& L,
-                                               WinStaged& staged, int flags, OutBuf<MAXU>& ob,
+                                               WinStaged& staged, int flags, OutBuf<MAXU, T / 2>& ob,
                                                OutMeta* meta) {
   constexpr int R = kWinR;
   constexpr int NLD = 16 * R / 8;  // 1 KB wave loads per K-step
   constexpr int ROWS = WinGeo<T>::ROWS, BLOCK = WinGeo<T>::BLOCK, WAVES = WinGeo<T>::WAVES;
-  static_assert(MAXU == 0 || T == 8, "held outputs use the repeated half of the MFMA result");
   const int r = lane & 15, g = lane >> 4;
   const int lrow = lane >> 3, lpos = lane & 7;
   const int nch = a.nch, K = a.K, M = a.M;
@@ -555,26 +559,37 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
     // sums and linears that also return acc are stored at once, below)
     if (MAXU > 0 && !partial && !a.acc) {
       static_assert(kWinR == 2, "one row block per half-wave");
-      const int bs = g >> 1;
-      const int32_t rsel = bs ? rs[1] : rs[0];
-      const float ssel = bs ? sr[1] : sr[0];
-      float vals[4];
+      constexpr int NV = T / 2;
+      float vals[NV];
+      if (T == 8) {
+        const int bs = g >> 1;
+        const int32_t rsel = bs ? rs[1] : rs[0];
+        const float ssel = bs ? sr[1] : sr[0];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int m = 4 * (g & 1) + v;
-        const int32_t c1 = bs ? acc1[1][v] : acc1[0][v];
-        const int32_t c4 = bs ? acc4[1][v] : acc4[0][v];
-        const int32_t c16 = bs ? acc16[1][v] : acc16[0][v];
-        const int32_t cq = c1 + (c4 >> 2) + (c16 >> 4);
-        const int32_t accv = (int32_t)((uint32_t)cq - (uint32_t)L.qsum[m] - (uint32_t)L.z[m] * (uint32_t)rsel);
-        vals[v] = epilogue(ssel, accv, L.s_act[m]);
+        for (int v = 0; v < 4; ++v) {
+          const int m = 4 * (g & 1) + v;
+          const int32_t c1 = bs ? acc1[1][v] : acc1[0][v];
+          const int32_t c4 = bs ? acc4[1][v] : acc4[0][v];
+          const int32_t c16 = bs ? acc16[1][v] : acc16[0][v];
+          const int32_t cq = c1 + (c4 >> 2) + (c16 >> 4);
+          const int32_t accv = (int32_t)((uint32_t)cq - (uint32_t)L.qsum[m] - (uint32_t)L.z[m] * (uint32_t)rsel);
+          vals[v] = epilogue(ssel, accv, L.s_act[m]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          const int b = j >> 2, v = j & 3, m = (4 * g + v) & (T - 1);
+          const int32_t cq = acc1[b][v] + (acc4[b][v] >> 2) + (acc16[b][v] >> 4);
+          const int32_t accv = (int32_t)((uint32_t)cq - (uint32_t)L.qsum[m] - (uint32_t)L.z[m] * (uint32_t)rs[b]);
+          vals[j] = epilogue(sr[b], accv, L.s_act[m]);
+        }
       }
       if (ob.n == MAXU) flush_out(ob, meta, lane);
 #pragma unroll
       for (int i = 0; i < MAXU; ++i)
         if (i == ob.n) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) ob.v[i][v] = vals[v];
+          for (int j = 0; j < NV; ++j) ob.v[i][j] = vals[j];
         }
       OutMeta mt;
       mt.y = a.y;
@@ -673,7 +688,7 @@ __global__ __launch_bounds__(kBlock) void mfma_wg_stack_kernel(const StackHeader
 __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void mfma_win_linear_kernel(LinearArgs a) {
   __shared__ __attribute__((aligned(16))) WinTiles<8> L;
   WinStaged staged;
-  OutBuf<0> ob;
+  OutBuf<0, 4> ob;
   mfma_win_range<false, 0, 8>(a, 0, a.N, blockIdx.x, gridDim.x, threadIdx.x & 63, wave_id_uniform(), L, staged, 0,
                            ob, nullptr);
 }
@@ -694,7 +709,7 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2)
   const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
   const int s1 = seg_start[worker + 1];
   WinStaged staged;
-  OutBuf<kOutUnits> ob;
+  OutBuf<kOutUnits, 4> ob;
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
@@ -705,12 +720,13 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2)
 }
 
 // 9 <= M <= 16 tokens, every K a multiple of 64: the same window kernel with
-// all 16 activation rows staged, one 8-wave workgroup per CU, outputs stored
-// at once.  (Only SPLIT = false is launched.)
+// all 16 activation rows staged, one 8-wave workgroup per CU, y-only outputs
+// held (kOut16Units units per wave).  (Only SPLIT = false is launched.)
 template <bool SPLIT>
 __global__ __launch_bounds__(WinGeo<16>::BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_win16_stack_kernel(
     const StackHeader* __restrict__ h) {
   __shared__ __attribute__((aligned(16))) WinTiles<16> L;
+  __shared__ OutMeta meta[WinGeo<16>::WAVES][kOut16Units];
   const int worker = xcd_logical_block();
   if (worker >= h->workers) return;  // the same for the whole workgroup
   const int lane = threadIdx.x & 63;
@@ -721,12 +737,13 @@ __global__ __launch_bounds__(WinGeo<16>::BLOCK) __attribute__((amdgpu_waves_per_
   const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
   const int s1 = seg_start[worker + 1];
   WinStaged staged;
-  OutBuf<0> ob;
+  OutBuf<kOut16Units, 8> ob;
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
-    mfma_win_range<SPLIT, 0, 16>(lin[sg.lin], sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged,
-                                 SPLIT ? sg.flags : 0, ob, nullptr);
+    mfma_win_range<SPLIT, kOut16Units, 16>(lin[sg.lin], sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged,
+                                           SPLIT ? sg.flags : 0, ob, meta[w]);
   }
+  flush_out(ob, meta[w], lane);
 }
 
 // Linears split along K: before the main kernel their outputs are cleared
