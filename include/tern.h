@@ -213,9 +213,13 @@ int64_t tern_linear_stack_workspace_bytes(int64_t L, int64_t M);
  * as separate work, the exact int32 partial sums are added into y (used as
  * int32 scratch), and a finishing kernel writes y and acc -- the results
  * are the same bits.  plan->splits counts them.  At 9..16 tokens such a
- * small stack also takes the prefill GEMM's kernel in place of the lockstep
- * one (the same test on the lockstep kernel's units); the results are the
- * same bits either way.
+ * small stack takes the prefill GEMM's kernel instead (the same test on the
+ * units of the kernel it would otherwise take); the results are the same
+ * bits either way.
+ * Outputs of linears that return y only (acc NULL) may be held on chip by
+ * the kernel and written when its work ends: as always, y is complete once
+ * the launch has completed on the stream, and no other work may read or
+ * write it in between.
  */
 int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
                               void* workspace, int64_t workspace_bytes,
