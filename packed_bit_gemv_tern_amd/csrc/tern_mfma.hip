@@ -237,9 +237,10 @@ __device__ __forceinline__ void clear_zero_row(WgTiles<MQ>& L) {
 // The stack kernel holds its fp32 outputs in registers and stores them when
 // its run of work ends: output stores trickled into the saturated weight
 // stream slow it by about 1 us per MB, one burst at the end far less.  That
-// takes 2 waves per SIMD (256 VGPRs); two 4-wave workgroups per CU keep the
+// takes 2 waves per SIMD (256 VGPRs): one 8-wave workgroup per CU keeps the
 // same 64 KB of weights in flight as four waves per SIMD with one tile each,
-// and one workgroup streams while the other restages its window.
+// with 256-row units (a window restage serves twice the rows of a 4-wave
+// unit, and 24 held units cover a whole run of the 8B stack).
 // Decode by code planes: word & (0x03030303 << 2k) holds the codes c = w + 1
 // of weights 4k..4k+3 of the word scaled by 4^k (the top plane is shifted
 // down instead), so plane k of four words is one MFMA operand for four ANDs.
@@ -254,16 +255,14 @@ constexpr int kWinPitch = kWinK + 16;
 constexpr int kWinTokens = 8;
 constexpr int kWinR = 2;       // row blocks of 16 per wave
 constexpr int kWinDepth = 2;   // weight tiles per wave (K-steps in flight)
-constexpr int kWinWaves = 4;   // waves per workgroup
+constexpr int kWinWaves = 8;   // waves per workgroup
 constexpr int kWinBlock = 64 * kWinWaves;
 constexpr int kWinRows = kWinWaves * 16 * kWinR;
-// Geometry per staged token count: the 16-token window (66 KB) leaves room
-// for one workgroup per CU, so that kernel runs 8 waves to keep the same
-// weight tiles in flight.
+// Geometry per staged token count (both run one 8-wave workgroup per CU).
 template <int T>
 struct WinGeo {
   static_assert(T == 8 || T == 16, "window tokens");
-  static constexpr int WAVES = T == 16 ? 8 : kWinWaves;
+  static constexpr int WAVES = kWinWaves;
   static constexpr int BLOCK = 64 * WAVES;
   static constexpr int ROWS = WAVES * 16 * kWinR;
 };

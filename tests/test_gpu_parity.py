@@ -322,16 +322,16 @@ def test_stack_y_only_8b_layer_and_mixed_acc(M):
 
 
 def test_stack_y_only_more_rows_than_held():
-    # K = 64 rows are cheap, so each worker takes far more 128-row units than
+    # K = 64 rows are cheap, so each worker takes far more 256-row units than
     # the 24 a wave holds: the held outputs are stored when the buffer fills
     # as well as at the end of the run
     M = 8
-    specs = [(1000003, 64, 1), (999997, 64, 2), (300, 4096, 3)]
+    specs = [(1200007, 64, 1), (1199993, 64, 2), (300, 4096, 3)]
     lins = [synth.make_linear(21, s, 0, N, K, 0.626, M, "o%d" % s) for (N, K, s) in specs]
     ups = [Uploaded(lin, with_acc=False) for lin in lins]
     ws = torch.empty(tern.tern_linear_stack_workspace_bytes(len(ups), M), dtype=torch.uint8, device=DEV)
     plan = tern.tern_linear_stack_prepare([u.desc() for u in ups], M, ws)
-    units = sum(-(-N // 128) for (N, _, _) in specs)
+    units = sum(-(-N // 256) for (N, _, _) in specs)
     assert units > 24 * plan.workers * 1.2, (units, plan.workers)
     tern.tern_linear_stack(plan)
     for lin, up in zip(lins, ups):
