@@ -456,8 +456,11 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
     const double ld = 16.0 * a.nch;  // packed bytes of a row the unit reads
     // a unit that restages the activation window stalls its workgroup for
     // about as long as streaming kRestageCost bytes takes
+    // (a 16-token window, M > 8, is twice the activation bytes to restage:
+    // 80 KB measured best for it, 40 KB for the 8-token one)
+    const double restage = kRestageCost * (M > 8 ? 2.0 : 1.0);
     const double fixed =
-        256.0 + (p == TERN_PATH_VALU ? 0.0 : kRestageCost * mfma_unit_restages(kernel - SK_MFMA, a.K));
+        256.0 + (p == TERN_PATH_VALU ? 0.0 : restage * mfma_unit_restages(kernel - SK_MFMA, a.K));
     for (int64_t r0 = 0; r0 < a.N; r0 += unit) {
       const int64_t r1 = std::min<int64_t>(a.N, r0 + unit);
       const double c = (double)(r1 - r0) * ld + fixed;
