@@ -126,11 +126,21 @@ def read_probe(nbytes: int, reps: int = 5):
     return {"bytes": nbytes, "best_GBps": best["GBps"], "best": best, "all": results}
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(seconds: float):
     """The oracle, as it stands, on a bounded sample of the same workload:
     layer 0's seven linears at M = 1 and at M = 8, repeated until `seconds`
-    of CPU time have passed."""
-    import numpy as np
+    of CPU time have passed, on every host core and then on one."""
     import oracle
     from packed_bit_gemv_tern_amd import synth
 
@@ -143,22 +153,34 @@ def cpu_baseline(seconds: float):
             q, s_act, z = synth.make_activations(0, layer, idx, K, M)
             nbytes = N * packed.shape[1] + 8 * N + M * K + 8 * M + 4 * M * N
             cases.append((packed, s_row, rowsum, K, q, s_act, z, nbytes))
-    done_bytes, t = 0, 0.0
-    reps = 0
-    while t < seconds:
-        for (packed, s_row, rowsum, K, q, s_act, z, nbytes) in cases:
-            t0 = time.perf_counter()
-            oracle.linear(packed, s_row, rowsum, K, q, s_act, z, lib=lib)
-            t += time.perf_counter() - t0
-            done_bytes += nbytes
-        reps += 1
+
+    def timed(limit):
+        done_bytes, t, reps = 0, 0.0, 0
+        while t < limit:
+            for (packed, s_row, rowsum, K, q, s_act, z, nbytes) in cases:
+                t0 = time.perf_counter()
+                oracle.linear(packed, s_row, rowsum, K, q, s_act, z, lib=lib)
+                t += time.perf_counter() - t0
+                done_bytes += nbytes
+            reps += 1
+        return done_bytes / t / 1e9, reps, t
+
+    all_cores = oracle.threads()
+    gbs, reps, t = timed(seconds * 2 / 3)
+    oracle.set_threads(1)
+    gbs1, reps1, t1 = timed(seconds / 3)
+    oracle.set_threads(all_cores)
     return {
-        "value": round(done_bytes / t / 1e9, 4),
+        "value": round(gbs, 4),
         "unit": "GB/s",
-        "cores": oracle.threads(),
+        "cores": all_cores,
         "kind": "oracle",
         "sample": "layer 0 of the 8B-shaped stack (7 linears, 48.7 MB packed + metadata) at "
                   "M=1 and M=8, %d repetitions, %.1f s" % (reps, t),
+        "single_thread": {"value": round(gbs1, 4), "unit": "GB/s", "cores": 1,
+                          "sample": "the same, %d repetitions, %.1f s" % (reps1, t1)},
+        "host": {"nproc": os.cpu_count(), "cpu_model": _cpu_model(),
+                 "oracle_build": "gcc " + " ".join(oracle.CFLAGS[:-2])},
     }
 
 
@@ -551,17 +573,36 @@ def suite(args):
               "cpu_oracle": {"us": round(ot * 1e6, 2), "cores": cores, "reps": oreps}})
 
 
+def prefill_case(args, M: int):
+    """Four 8B layers at M tokens, --steps launches after the warm-up (a
+    profiling workload for the prefill GEMM); prints one JSON line."""
+    import torch
+    from packed_bit_gemv_tern_amd import synth
+    from packed_bit_gemv_tern_amd.stack import DeviceStack
+    st4 = DeviceStack("8b", layers=4, seed=3, threads=16)
+    b4 = st4.bind(M)
+    us = _event_times(lambda i: b4.run(), args.steps, warm=args.warmup, warm_s=args.warmup_seconds)
+    st = _stats(us, b4.bytes)
+    dense_ops = 2 * M * sum(N * K for (_, _, _, N, K, _) in synth.stack_specs("8b", 4))
+    st["dense_TOPS"] = round(dense_ops / st["median_us"] / 1e6, 2)
+    st["frac_of_int8_peak"] = round(st["dense_TOPS"] / INT8_DENSE_PEAK_TOPS, 4)
+    print(json.dumps({"case": "prefill_4layers", "M": M, "kernel": kernel_name(b4.plan), **st}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="untimed warm-up lasts at least this long (and --warmup steps)")
     ap.add_argument("--layers", type=int, default=None, help="fewer layers (testing only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth probe")
-    ap.add_argument("--only", choices=["m1", "m8"], default=None,
-                    help="launch a single pass per step (for profiling)")
+    ap.add_argument("--only", choices=["m1", "m8", "prefill64", "prefill512"], default=None,
+                    help="launch a single pass per step (for profiling); prefill64 / prefill512: "
+                         "four 8B layers (28 linears) at M = 64 / 512 instead of the headline")
     ap.add_argument("--suite", action="store_true",
                     help="measure the single GEMV, one 8B layer, the prefill sweeps, the 0.6B "
                          "stack, the int8 head, block scales, 1.6-bit rows, the quantisers and a "
@@ -596,6 +637,9 @@ def main():
     if args.suite:
         suite(args)
         return
+    if args.only in ("prefill64", "prefill512"):
+        prefill_case(args, 64 if args.only == "prefill64" else 512)
+        return
     # Each pass gets its own copy of the stack (different seeds): the two
     # passes never share weights, so neither can hit lines the other left in
     # the caches (as in drafted decoding, where they are different models).
@@ -620,10 +664,18 @@ def main():
             if events is not None:
                 events[i][1].record(stream)
 
-    for _ in range(args.warmup):
+    # untimed warm-up: at least --warmup steps and --warmup-seconds of them
+    # (the first launches after the stacks are built run up to ~8 % slow)
+    t_w = time.perf_counter()
+    warm_steps = 0
+    while warm_steps < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
         step()
+        warm_steps += 1
+        if warm_steps % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    log("warmup done")
+    warm_s = time.perf_counter() - t_w
+    log("warmup done: %d steps, %.2f s" % (warm_steps, warm_s))
 
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in passes] for _ in range(args.steps)]
@@ -645,6 +697,7 @@ def main():
         kname = kernel_name(b.plan)
         per_pass[name] = {
             "M": b.M, "kernel": kname, "bytes": b.bytes, "avg_us": round(avg * 1e3, 3),
+            "median_us": round(ms[len(ms) // 2] * 1e3, 3),
             "p10_us": round(ms[len(ms) // 10] * 1e3, 3), "p90_us": round(ms[(9 * len(ms)) // 10] * 1e3, 3),
             "GBps": round(b.bytes / (avg * 1e-3) / 1e9, 1),
             "frac_of_peak": round(b.bytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -664,6 +717,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
+        "warmup_s": round(warm_s, 3),
         "ms_per_step": round(elapsed / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -90,6 +90,9 @@ enum {
 
 #define TERN_MAX_K 5600000
 #define TERN_VALU_MAX_M 8
+/* Rows tern_pack, tern_unpack and tern_validate take in one call (one
+ * 64-lane wave per row, and a launch counts at most 2^32 - 1 lanes). */
+#define TERN_MAX_ROWS_PACK 67108860
 
 /* Bytes of one packed row: 16 * ceil(K / 64); 0 for K < 1. */
 int64_t tern_row_bytes(int64_t K);
@@ -191,7 +194,11 @@ typedef struct {
   int32_t splits;    /* linears split along K (then tern_linear_stack enqueues
                         a fill kernel and a finishing kernel around the main
                         one; see tern_linear_stack_prepare) */
-  int32_t pad;
+  int32_t restages;  /* activation windows (4,096 columns of the M tokens)
+                        the workgroups of one launch load into LDS (the
+                        M = 2..16 window kernels; 0 otherwise): linears that
+                        read the same activation buffers and follow each other
+                        in a workgroup's run share one load */
 } tern_stack_plan;
 
 /* Upper bound of the workspace tern_linear_stack_prepare needs for L linears

@@ -64,6 +64,8 @@ def _declare(lib):
     lib.oracle_row_bytes.argtypes = [i64]
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_pack.restype = i64
     lib.oracle_pack.argtypes = [_p(ctypes.c_int8), i64, i64, i64,
                                 _p(ctypes.c_uint8), _p(i32)]
@@ -132,6 +134,12 @@ def row_bytes(K: int) -> int:
 def threads() -> int:
     """OpenMP threads the oracle's loops use."""
     return int(load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's loops from now on (timing only; results do
+    not depend on it)."""
+    load().oracle_set_threads(int(n))
 
 
 def pack(w: np.ndarray, lib=None):

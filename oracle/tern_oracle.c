@@ -80,6 +80,16 @@ int oracle_threads(void) {
 #endif
 }
 
+/* Threads the parallel loops use from now on (the CPU baseline is timed
+ * single-threaded and on every core); no effect on any result. */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /*
  * Pack an N x K int8 matrix (row stride ldw elements) whose entries are in
  * {-1, 0, +1}.  Writes N rows of row_bytes(K) bytes and rowsum[i] = sum_j w_ij.

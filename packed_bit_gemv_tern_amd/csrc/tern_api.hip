@@ -111,10 +111,13 @@ constexpr int64_t kValuWaveBytes = 24 << 10;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
-// Schedule cost of one activation-window restage, in streamed bytes
-// (measured: ~5.8 us per restage at ~10 GB/s per workgroup at M = 8, and
-// 30-60 KB the best setting in a sweep).
+// Schedule cost of one activation-window restage, in streamed bytes: a
+// restage stalls its workgroup about 2 us (the barriers wait for its
+// slowest wave), about what a workgroup streams in 50 KB at M = 8.
 constexpr double kRestageCost = 40000.0;
+// Units a window-major group is taken to hold, for the schedule's cost of
+// its restages (each window is staged once per group)
+constexpr double kWindowMajorGroup = 8.0;
 
 struct Layout {
   int64_t off_lin, off_seg_start, off_seg, off_split, total;
@@ -156,7 +159,7 @@ int tern_last_hip_error(void) { return g_last_hip; }
 int tern_pack(const int8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed,
               int32_t* rowsum, int32_t* bad_count, hipStream_t stream) {
   if (N < 0 || K < 1 || ldw < K) return TERN_ERR_INVALID_ARG;
-  if (K > TERN_MAX_K || N > kI32Max) return TERN_ERR_RANGE;
+  if (K > TERN_MAX_K || N > TERN_MAX_ROWS_PACK) return TERN_ERR_RANGE;
   if (bad_count && !aligned(bad_count, 4)) return TERN_ERR_ALIGNMENT;
   if (bad_count) {
     hipError_t e = launch_zero_i32(bad_count, 1, stream);
@@ -172,7 +175,7 @@ int tern_pack(const int8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packe
 int tern_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* w, int64_t ldw,
                 hipStream_t stream) {
   if (N < 0 || K < 1 || ldw < K) return TERN_ERR_INVALID_ARG;
-  if (K > TERN_MAX_K || N > kI32Max) return TERN_ERR_RANGE;
+  if (K > TERN_MAX_K || N > TERN_MAX_ROWS_PACK) return TERN_ERR_RANGE;
   if (N == 0) return TERN_OK;
   if (!packed || !w) return TERN_ERR_INVALID_ARG;
   if (!aligned(packed, 16)) return TERN_ERR_ALIGNMENT;
@@ -183,7 +186,7 @@ int tern_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* w, int64_t 
 int tern_validate(const uint8_t* packed, int64_t N, int64_t K, int32_t* counts,
                   hipStream_t stream) {
   if (N < 0 || K < 1 || !counts) return TERN_ERR_INVALID_ARG;
-  if (K > TERN_MAX_K || N > kI32Max) return TERN_ERR_RANGE;
+  if (K > TERN_MAX_K || N > TERN_MAX_ROWS_PACK) return TERN_ERR_RANGE;
   if (!aligned(counts, 4)) return TERN_ERR_ALIGNMENT;
   if (N > 0 && !packed) return TERN_ERR_INVALID_ARG;
   if (N > 0 && !aligned(packed, 16)) return TERN_ERR_ALIGNMENT;
@@ -224,6 +227,7 @@ int tern_block_rowsum(const uint8_t* packed, int64_t N, int64_t K, int64_t B, in
                       hipStream_t stream) {
   if (N < 0 || K < 1 || !block_size_ok(B)) return TERN_ERR_INVALID_ARG;
   if (K > TERN_BLOCK_MAX_K || N > kI32Max) return TERN_ERR_RANGE;
+  if (block_rowsum_work_items(N, K, B) > kMaxDispatchItems) return TERN_ERR_RANGE;
   if (N == 0) return TERN_OK;
   if (!packed || !rowsum_b) return TERN_ERR_INVALID_ARG;
   if (!aligned(packed, 16) || !aligned(rowsum_b, 4)) return TERN_ERR_ALIGNMENT;
@@ -252,7 +256,7 @@ int tern_gemv_blocked(const uint8_t* packed, const float* s_b, const int32_t* ro
 int tern_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
                       float* s_act, int32_t* z, hipStream_t stream) {
   if (M < 0 || K < 1 || ldx < K || ldq < K) return TERN_ERR_INVALID_ARG;
-  if (M > kI32Max) return TERN_ERR_RANGE;
+  if (M > kI32Max || quantize_act_work_items(M) > kMaxDispatchItems) return TERN_ERR_RANGE;
   if (M == 0) return TERN_OK;
   if (!x || !q || !s_act || !z) return TERN_ERR_INVALID_ARG;
   if (!aligned(x, 4) || !aligned(s_act, 4) || !aligned(z, 4)) return TERN_ERR_ALIGNMENT;
@@ -265,7 +269,7 @@ int64_t tern_row_bytes5(int64_t K) { return K < 1 ? 0 : 16 * ((K + 79) / 80); }
 int tern_pack5(const int8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed5,
                int32_t* rowsum, int32_t* bad_count, hipStream_t stream) {
   if (N < 0 || K < 1 || ldw < K) return TERN_ERR_INVALID_ARG;
-  if (K > TERN5_MAX_K || N > kI32Max) return TERN_ERR_RANGE;
+  if (K > TERN5_MAX_K || N > kI32Max || pack5_work_items(N) > kMaxDispatchItems) return TERN_ERR_RANGE;
   if (bad_count && !aligned(bad_count, 4)) return TERN_ERR_ALIGNMENT;
   if (bad_count) {
     hipError_t e = launch_zero_i32(bad_count, 1, stream);
@@ -283,6 +287,7 @@ int tern_gemv5(const uint8_t* packed5, const float* s_row, const int32_t* rowsum
                int32_t* acc, hipStream_t stream) {
   if (K > TERN5_MAX_K) return TERN_ERR_RANGE;
   const int st = check_linear(packed5, s_row, rowsum, N, K, 1, q, K, s_act, z, y, N, acc);
+  if (st == TERN_OK && gemv5_work_items(N, K) > kMaxDispatchItems) return TERN_ERR_RANGE;
   if (st != TERN_OK || N == 0) return st;
   const hipError_t e = launch_gemv5(packed5, s_row, rowsum, N, K, q, s_act, z, y, acc, stream);
   return e == hipSuccess ? TERN_OK : hip_fail(e);
@@ -291,8 +296,9 @@ int tern_gemv5(const uint8_t* packed5, const float* s_row, const int32_t* rowsum
 int tern_quantize_weights(const float* W, int64_t N, int64_t K, int64_t ldw, int64_t B, int8_t* w,
                           int64_t ldt, float* s_b, hipStream_t stream) {
   if (N < 0 || K < 1 || B < 1 || ldw < K || ldt < K) return TERN_ERR_INVALID_ARG;
-  // one thread per (row, block): at most 2^40 of them (a 32-bit grid)
-  if (N > kI32Max || K > kI32Max || N * ((K + B - 1) / B) > ((int64_t)1 << 40)) return TERN_ERR_RANGE;
+  // one thread per (row, block), all in one 32-bit dispatch
+  if (N > kI32Max || K > kI32Max || quantize_weights_work_items(N, K, B) > kMaxDispatchItems)
+    return TERN_ERR_RANGE;
   if (N == 0) return TERN_OK;
   if (!W || !w || !s_b) return TERN_ERR_INVALID_ARG;
   if (!aligned(W, 4) || !aligned(s_b, 4)) return TERN_ERR_ALIGNMENT;
@@ -303,7 +309,8 @@ int tern_quantize_weights(const float* W, int64_t N, int64_t K, int64_t ldw, int
 int tern_head_rowsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw, int32_t* rowsum,
                      hipStream_t stream) {
   if (N < 0 || K < 1 || ldw < K) return TERN_ERR_INVALID_ARG;
-  if (K > TERN_HEAD_MAX_K || N > kI32Max) return TERN_ERR_RANGE;
+  if (K > TERN_HEAD_MAX_K || N > kI32Max || head_rowsum_work_items(N) > kMaxDispatchItems)
+    return TERN_ERR_RANGE;
   if (N == 0) return TERN_OK;
   if (!W || !rowsum) return TERN_ERR_INVALID_ARG;
   if (!aligned(rowsum, 4)) return TERN_ERR_ALIGNMENT;
@@ -459,8 +466,12 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
     // (a 16-token window, M > 8, is twice the activation bytes to restage:
     // 80 KB measured best for it, 40 KB for the 8-token one)
     const double restage = kRestageCost * (M > 8 ? 2.0 : 1.0);
-    const double fixed =
-        256.0 + (p == TERN_PATH_VALU ? 0.0 : restage * mfma_unit_restages(kernel - SK_MFMA, a.K));
+    const int32_t mv = kernel - SK_MFMA;
+    const double restages = p == TERN_PATH_VALU ? 0.0
+                            : mfma_window_major(mv, a.K, a.acc == nullptr && !(flags & kSegPartial))
+                                ? mfma_unit_restages(mv, a.K) / kWindowMajorGroup
+                                : (double)mfma_unit_restages(mv, a.K);
+    const double fixed = 256.0 + restage * restages;
     for (int64_t r0 = 0; r0 < a.N; r0 += unit) {
       const int64_t r1 = std::min<int64_t>(a.N, r0 + unit);
       const double c = (double)(r1 - r0) * ld + fixed;
@@ -485,7 +496,10 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   // their own, their int32 partial sums added into the output buffer, which
   // a fill kernel clears before and a finishing kernel turns into y (and
   // acc) after.
-  if (splittable && gmax > kSplitRatio * total / (double)workers) {
+  // (the fill and finishing kernels take one workgroup per split linear and
+  // token: all of them must fit one dispatch)
+  if (splittable && gmax > kSplitRatio * total / (double)workers &&
+      L * M * (int64_t)kSplitBlock <= kMaxDispatchItems) {
     // only K a multiple of 64: every window's reads then lie inside the
     // linear's K columns (the kernels clamp activation addresses to the row)
     auto splits_k = [&](const LinearArgs& a) {
@@ -608,6 +622,52 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   plan->segments = (int32_t)segs.size();
   plan->kernel = kernel;
   plan->splits = (int32_t)split.size();
+  // activation-window loads of one launch (window kernels): a segment of a
+  // single-window linear loads its window unless the workgroup's segment
+  // before it read the same activations; a longer K loads every window of
+  // every unit
+  // (the kernel's own walk: units in order, all windows of each; a
+  // window-major linear in groups of held units, each window once per group)
+  if (p == TERN_PATH_MFMA && mfma_is_window(kernel - SK_MFMA)) {
+    const int32_t mv = kernel - SK_MFMA;
+    const int unit = mfma_unit_rows(mv);
+    const int64_t hmax = mfma_held_units(mv);
+    int64_t restages = 0;
+    for (int64_t wr = 0; wr < workers; ++wr) {
+      const LinearArgs* prev = nullptr;  // staged window: window `pwin` of prev's activations
+      int64_t pwin = 0, nheld = 0;
+      for (int32_t sx = seg_start[(size_t)wr]; sx < seg_start[(size_t)wr + 1]; ++sx) {
+        const Segment& sg = segs[(size_t)sx];
+        const LinearArgs& a = lin[(size_t)sg.lin];
+        const int64_t nwin = (a.K + wk_k - 1) / wk_k;
+        const int64_t units = (sg.row_end - sg.row_begin + unit - 1) / unit;
+        const bool y_only = a.acc == nullptr && !(sg.flags & kSegPartial);
+        auto stage = [&](int64_t w) {
+          const bool same = prev && prev->q == a.q && prev->z == a.z && prev->s_act == a.s_act &&
+                            prev->K == a.K && prev->ldq == a.ldq && pwin == w;
+          if (!same) ++restages;
+          prev = &a;
+          pwin = w;
+        };
+        if (hmax > 0 && mfma_window_major(mv, a.K, y_only)) {
+          for (int64_t rem = units; rem > 0;) {
+            const int64_t need = std::min(rem, hmax);
+            if (hmax - nheld < need) nheld = 0;
+            const int64_t gn = std::min(rem, hmax - nheld);
+            for (int64_t w = 0; w < nwin; ++w) stage(w);
+            nheld += gn;
+            rem -= gn;
+          }
+          continue;
+        }
+        for (int64_t k = 0; k < units; ++k) {
+          for (int64_t w = 0; w < nwin; ++w) stage(w);
+          if (hmax > 0 && y_only) nheld = nheld == hmax ? 1 : nheld + 1;
+        }
+      }
+    }
+    plan->restages = (int32_t)std::min<int64_t>(restages, kI32Max);
+  }
   return TERN_OK;
 }
 

@@ -327,6 +327,10 @@ int blocked_rows_per_wave(int64_t K) {
   return cpl == 1 ? BlkU<1>::U : cpl == 2 ? BlkU<2>::U : 1;
 }
 
+int64_t block_rowsum_work_items(int64_t N, int64_t K, int64_t B) {
+  return (N * ((K + B - 1) / B) + kBlkBlock - 1) / kBlkBlock * kBlkBlock;
+}
+
 hipError_t launch_block_rowsum(const uint8_t* packed, int64_t N, int64_t K, int64_t B, int32_t* rowsum_b,
                                hipStream_t s) {
   const int64_t nb = (K + B - 1) / B;

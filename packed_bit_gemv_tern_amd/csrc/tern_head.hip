@@ -240,6 +240,8 @@ hipError_t launch_head(const int8_t* W, const float* s_row, const int32_t* rowsu
   return hipGetLastError();
 }
 
+int64_t head_rowsum_work_items(int64_t N) { return (N + kHeadWaves - 1) / kHeadWaves * kHeadBlock; }
+
 hipError_t launch_head_rowsum(const int8_t* W, int64_t N, int64_t K, int64_t ldw, int32_t* rowsum,
                               hipStream_t s) {
   const dim3 grid((unsigned)((N + kHeadWaves - 1) / kHeadWaves)), block(kHeadBlock);

@@ -85,6 +85,21 @@ struct LaunchShape {
   int M, splits;  // tokens; linears split along K (0: no extra kernels)
 };
 
+// A launch counts its work-items (workgroups x threads per workgroup) in 32
+// bits; the entry points refuse sizes whose launch would need more.
+constexpr int64_t kMaxDispatchItems = 0xFFFFFFFFll;
+// Work-items of the launches whose grid grows with the problem size.
+int64_t pack_work_items(int64_t N);  // tern_pack, tern_unpack, tern_validate
+int64_t pack5_work_items(int64_t N);
+int64_t gemv5_work_items(int64_t N, int64_t K);
+int64_t head_rowsum_work_items(int64_t N);
+int64_t block_rowsum_work_items(int64_t N, int64_t K, int64_t B);
+int64_t quantize_weights_work_items(int64_t N, int64_t K, int64_t B);
+int64_t quantize_act_work_items(int64_t M);
+// threads of one workgroup of the split clear / finish kernels (one per
+// split linear and token)
+constexpr int kSplitBlock = 256;
+
 // ---- launchers (defined in the .hip files) ----
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 hipError_t launch_pack(const int8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed,
@@ -105,6 +120,11 @@ int mfma_unit_rows(int32_t variant);
 // activation-window restages per unit of a linear with K columns (the
 // window kernel restages once per 4096 columns when K exceeds one window)
 int mfma_unit_restages(int32_t variant, int64_t K);
+// y-only outputs a wave of the window stack kernel holds (0: none held), and
+// whether a linear of K columns is walked window-major (its units in groups,
+// window by window: each window staged once per group)
+int mfma_held_units(int32_t variant);
+bool mfma_window_major(int32_t variant, int64_t K, bool y_only);
 bool mfma_per_workgroup(int32_t variant);
 int32_t valu_variant_for(int64_t K);
 

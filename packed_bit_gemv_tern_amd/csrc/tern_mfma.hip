@@ -254,7 +254,7 @@ constexpr int kWinK = 4096;    // activation window (K positions)
 constexpr int kWinPitch = kWinK + 16;
 constexpr int kWinTokens = 8;
 constexpr int kWinR = 2;       // row blocks of 16 per wave
-constexpr int kWinDepth = 2;   // weight tiles per wave (K-steps in flight)
+constexpr int kWinDepth8 = 2;  // weight tiles per wave (K-steps in flight), 8 tokens
 constexpr int kWinWaves = 8;   // waves per workgroup
 constexpr int kWinBlock = 64 * kWinWaves;
 constexpr int kWinRows = kWinWaves * 16 * kWinR;
@@ -265,12 +265,14 @@ struct WinGeo {
   static constexpr int WAVES = kWinWaves;
   static constexpr int BLOCK = 64 * WAVES;
   static constexpr int ROWS = WAVES * 16 * kWinR;
+  // weight tiles in flight per wave (the 16-token window leaves LDS for two)
+  static constexpr int DEPTH = T == 8 ? kWinDepth8 : 2;
 };
 constexpr int kWinTile = 16 * kWinR * kStepBytes;
 
 template <int T>
 struct WinTiles {
-  uint8_t w[WinGeo<T>::WAVES][kWinDepth][kWinTile];
+  uint8_t w[WinGeo<T>::WAVES][WinGeo<T>::DEPTH][kWinTile];
   uint8_t q[T][kWinPitch];  // each 64-byte chunk stored dword-transposed
   int32_t qsum[T];          // sum of the token's activations over all of K
   int32_t z[T];             // zero points and scales of the staged tokens
@@ -310,16 +312,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// What the workgroup's window holds: the activations, zero points and scales
-// of one single-window linear, reused by the next segment when that reads the
-// same buffers (q == nullptr: nothing reusable is staged).
+// What the workgroup's window holds: window `win` of the activations (with
+// their zero points and scales) at q, reused by the next unit or segment that
+// needs the same window of the same buffers (q == nullptr: nothing staged).
 struct WinStaged {
   const int8_t* q = nullptr;
   const int32_t* z = nullptr;
   const float* s_act = nullptr;
-  int K = 0, ldq = 0;
-  __device__ bool holds(const LinearArgs& a) const {
-    return q && q == a.q && z == a.z && s_act == a.s_act && K == a.K && ldq == a.ldq;
+  int K = 0, ldq = 0, win = 0;
+  __device__ bool holds(const LinearArgs& a, int w) const {
+    return q && q == a.q && z == a.z && s_act == a.s_act && K == a.K && ldq == a.ldq && win == w;
   }
 };
 
@@ -379,11 +381,31 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   constexpr int R = kWinR;
   constexpr int NLD = 16 * R / 8;  // 1 KB wave loads per K-step
   constexpr int ROWS = WinGeo<T>::ROWS, BLOCK = WinGeo<T>::BLOCK, WAVES = WinGeo<T>::WAVES;
+  constexpr int D = WinGeo<T>::DEPTH;
+  constexpr int NV = T / 2;  // held values per unit and lane
+  static_assert(D >= 1 && D <= 3, "tile depth");
+  static_assert(kWinR == 2, "one row block per half-wave");
   const int r = lane & 15, g = lane >> 4;
   const int lrow = lane >> 3, lpos = lane & 7;
   const int nch = a.nch, K = a.K, M = a.M;
   const int nks = (nch + 7) / 8;
   const int nwin = (K + kWinK - 1) / kWinK;
+  const bool partial = SPLIT && (flags & kSegPartial) != 0;
+  const bool zpoint = !partial || (flags & kSegZeroPoint) != 0;
+  // y-only outputs are held in registers until the worker's run ends (a
+  // split window's partial sums and linears that also return acc are
+  // stored at once)
+  const bool held = MAXU > 0 && !partial && !a.acc;
+  // Window-major order: a held linear of several whole windows takes its
+  // units in groups (as many as the held slots take) and walks each group
+  // window by window -- window 0 of every unit of the group, then window 1,
+  // ... -- so the group stages each window once, where unit by unit every
+  // unit would stage all of them (restaging stalls the workgroup at a
+  // barrier until its slowest wave arrives).  The exact int32 sums of the
+  // earlier windows wait in the units' held slots.
+  const bool wmajor = held && nwin > 1 && (K % kWinK) == 0 && ustride == 1;
+  const int ufirst = row_lo + unit0 * ROWS;
+  const int uend = ufirst < row_hi ? unit0 + (row_hi - ufirst + ROWS - 1) / ROWS : unit0;
   // byte offsets (below 2^32: checked by the host) of the wave's weight rows
   // within a unit, and the chunk each lane brings
   auto unit_src = [&](int unit, uint32_t (&src)[NLD]) {
@@ -394,7 +416,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   // K-step ks of a unit into the slot of tile number t (tiles are numbered
   // in the order the wave consumes them, across units)
   auto issue = [&](const uint32_t (&src)[NLD], int ks, int t) {
-    uint8_t* tile = L.w[w][t % kWinDepth];
+    uint8_t* tile = L.w[w][t % D];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int ch = min(8 * ks + (lpos ^ ((8 * i + lrow) & 7)), nch - 1);
@@ -418,37 +440,72 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
 #pragma unroll
   for (int b = 0; b < R; ++b) nrs[b] = 0, nsr[b] = 0.0f;
   // tiles in flight ahead of the one being consumed: never more than a
-  // unit's K-steps, so a lookahead reaches at most into the next unit
-  const int depth = min(kWinDepth, nks);
-  if (row_lo + unit0 * ROWS < row_hi) {
+  // unit's (a window's, window-major) K-steps, so a lookahead reaches at
+  // most into the next unit
+  const int depth = min(D, nks);
+  if (ufirst < row_hi) {
     unit_src(unit0, src);
 #pragma unroll
-    for (int d = 0; d < kWinDepth; ++d)
+    for (int d = 0; d < D; ++d)
       if (d < depth) issue(src, d, d);
     load_rowops(unit0, nrs, nsr);
   }
 
-  // tb: number of the unit's first tile
+  // (unit u, window pass p): one pass over K-steps [kb, ke) of a unit --
+  // all of K, or window p of it window-major; g0 .. g0 + gn - 1: the
+  // window-major group; tb: number of the pass's first tile
+  int u = unit0, p = 0, g0 = unit0, gn = 0;
 #pragma unroll 1
-  for (int unit = unit0, tb = 0;; unit += ustride, tb += nks) {
-    const int ubase = row_lo + unit * ROWS;
-    if (ubase >= row_hi) break;  // the same for every wave of the workgroup
-    const int base = ubase + 16 * R * w;
-    const bool has_next = ubase + ustride * ROWS < row_hi;
+  for (int tb = 0; u < uend;) {
+    if (wmajor && p == 0 && u == g0 + gn) {
+      // a new group: empty the held slots first when fewer are free than
+      // it would take
+      const int need = min(uend - u, MAXU);
+      if (MAXU - ob.n < need) flush_out(ob, meta, lane);
+      g0 = u;
+      gn = min(uend - u, MAXU - ob.n);
+    }
+    const int base = row_lo + u * ROWS + 16 * R * w;
+    const int kb = wmajor ? 8 * p : 0, ke = wmajor ? 8 * p + 8 : nks;
+    const bool last_pass = !wmajor || p == nwin - 1;
+    // the pass after this one
+    int nu = -1, np = 0;
+    if (wmajor) {
+      if (u + 1 < g0 + gn)
+        nu = u + 1, np = p;
+      else if (p + 1 < nwin)
+        nu = g0, np = p + 1;
+      else if (g0 + gn < uend)
+        nu = g0 + gn, np = 0;
+    } else if (u + ustride < uend) {
+      nu = u + ustride;
+    }
+    const bool has_next = nu >= 0;
+    const int nkb = wmajor ? 8 * np : 0;
     uint32_t nsrc[NLD];
-    if (has_next) unit_src(unit + ustride, nsrc);
+    if (has_next) unit_src(nu, nsrc);
     int32_t rs[R];
     float sr[R];
     i32x4 acc1[R], acc4[R], acc16[R];
 #pragma unroll
     for (int b = 0; b < R; ++b) acc1[b] = acc4[b] = acc16[b] = i32x4{0, 0, 0, 0};
-    for (int ks = 0; ks < nks; ++ks) {
-      const uint8_t* tile = L.w[w][(tb + ks) % kWinDepth];
+    for (int ks = kb; ks < ke; ++ks) {
+      const uint8_t* tile = L.w[w][(tb + ks - kb) % D];
       if ((ks & 7) == 0) {
         const int win = ks >> 3;
-        // a single-window linear whose activations are already staged (the
-        // same buffers, e.g. the previous unit) skips the restaging
-        if (nwin > 1 || !staged.holds(a)) {
+        if (win > 0 && !wmajor) {
+          // fold the scaled planes into the exact sum once per window: a
+          // plane-2 sum is 16 * sum(c*q), which over all of a long K
+          // (beyond 2^21 columns) would pass 2^31
+#pragma unroll
+          for (int b = 0; b < R; ++b) {
+            acc1[b] += (acc4[b] >> 2) + (acc16[b] >> 4);
+            acc4[b] = acc16[b] = i32x4{0, 0, 0, 0};
+          }
+        }
+        // a window already staged (the previous unit's, or the previous
+        // segment's when it reads the same activations) is used as it is
+        if (!staged.holds(a, win)) {
           // every wave is done with the previous window before it is replaced
           lds_barrier();
           {
@@ -475,8 +532,9 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
             }
           }
           lds_barrier();
-          // per-token activation sums of this window; wave w owns tokens
-          // w, w + WAVES, ... so no two waves write one entry
+          // per-token activation sums of this window, added to the earlier
+          // windows' (windows are staged in order); wave w owns tokens w,
+          // w + WAVES, ... so no two waves write one entry
           for (int tq = w; tq < T; tq += WAVES) {
             uint32_t part = 0;
             for (int off = 16 * lane; off < kWinK; off += 16 * 64) {
@@ -493,27 +551,35 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
             L.s_act[tq] = tq < M ? load_g(a.s_act + tq) : 0.0f;
           }
           lds_barrier();
-          staged.q = nwin > 1 ? nullptr : a.q;
+          staged.q = a.q;
           staged.z = a.z;
           staged.s_act = a.s_act;
           staged.K = K;
           staged.ldq = a.ldq;
+          staged.win = win;
         }
       }
-      // this step's weight tile has landed: when the next tile's NLD loads
-      // were issued after it (they complete in order; stores in between
-      // only add to the count), at most NLD may still be in flight
-      if (depth > 1 && (ks + 1 < nks || has_next))
-        wait_vm<(kWinDepth > 1 ? NLD : 0)>();
-      else
-        wait_vm<0>();
-      if (ks == 0) {
-        // this unit's row operands arrived with (or before) its first tile
-        // (the wait above covers them); the next unit's are loaded now, a
-        // whole unit ahead of their use
+      // this step's weight tile has landed once no more loads are in flight
+      // than the tiles issued after it (NLD each; loads complete in order,
+      // and other loads and stores in between only add to the count)
+      {
+        const int after = has_next ? depth - 1 : min(depth - 1, ke - 1 - ks);
+        if (after >= 2)
+          wait_vm<2 * NLD>();
+        else if (after == 1)
+          wait_vm<NLD>();
+        else
+          wait_vm<0>();
+      }
+      if (ks == kb) {
+        // this pass's row operands arrived with (or before) its first tile
+        // (the wait above covers them); those of the next unit to finish
+        // are loaded now, a whole pass ahead of their use
+        if (last_pass) {
 #pragma unroll
-        for (int b = 0; b < R; ++b) rs[b] = settled(nrs[b]), sr[b] = settled(nsr[b]);
-        if (has_next) load_rowops(unit + ustride, nrs, nsr);
+          for (int b = 0; b < R; ++b) rs[b] = settled(nrs[b]), sr[b] = settled(nsr[b]);
+        }
+        if (has_next && (!wmajor || np == nwin - 1)) load_rowops(nu, nrs, nsr);
       }
       u32x4 wv[R][2];
 #pragma unroll
@@ -523,10 +589,10 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
           wv[b][half] = *reinterpret_cast<const u32x4*>(
               tile + (16 * b + r) * kStepBytes + 16 * ((2 * g + half) ^ (r & 7)));
       wait_lgkm();  // tile read: it may be overwritten
-      if (ks + depth < nks)
-        issue(src, ks + depth, tb + ks + depth);
+      if (ks + depth < ke)
+        issue(src, ks + depth, tb + ks - kb + depth);
       else if (has_next)
-        issue(nsrc, ks + depth - nks, tb + ks + depth);  // the next unit's first tiles
+        issue(nsrc, nkb + ks + depth - ke, tb + ks - kb + depth);  // the next pass's first tiles
       // activations come from the window, which the loads never overwrite
       const uint8_t* qrow = &L.q[r & (T - 1)][64 * (8 * (ks & 7) + 2 * g)];
 #pragma unroll
@@ -552,91 +618,122 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
     // a linear split along K adds its exact partial sums into y, viewed as
     // int32 (cleared before the launch, finished after it); the zero-point
     // term belongs to one window only.
-    const bool partial = SPLIT && (flags & kSegPartial) != 0;
-    const bool zpoint = !partial || (flags & kSegZeroPoint) != 0;
-    // held outputs: every unit that stores y only (a split window's partial
-    // sums and linears that also return acc are stored at once, below)
-    if (MAXU > 0 && !partial && !a.acc) {
-      static_assert(kWinR == 2, "one row block per half-wave");
-      constexpr int NV = T / 2;
-      float vals[NV];
+    if (held) {
+      // the lane's held values: with 8 tokens row block g >> 1, tokens
+      // 4 (g & 1) + v (the MFMA result holds tokens 0..7 twice); with 16
+      // both row blocks, tokens 4g + v
+      int32_t cq[NV];  // sum(c*q) of this pass, exact
       if (T == 8) {
         const int bs = g >> 1;
-        const int32_t rsel = bs ? rs[1] : rs[0];
-        const float ssel = bs ? sr[1] : sr[0];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int m = 4 * (g & 1) + v;
           const int32_t c1 = bs ? acc1[1][v] : acc1[0][v];
           const int32_t c4 = bs ? acc4[1][v] : acc4[0][v];
           const int32_t c16 = bs ? acc16[1][v] : acc16[0][v];
-          const int32_t cq = c1 + (c4 >> 2) + (c16 >> 4);
-          const int32_t accv = (int32_t)((uint32_t)cq - (uint32_t)L.qsum[m] - (uint32_t)L.z[m] * (uint32_t)rsel);
-          vals[v] = epilogue(ssel, accv, L.s_act[m]);
+          cq[v] = c1 + (c4 >> 2) + (c16 >> 4);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-          const int b = j >> 2, v = j & 3, m = (4 * g + v) & (T - 1);
-          const int32_t cq = acc1[b][v] + (acc4[b][v] >> 2) + (acc16[b][v] >> 4);
-          const int32_t accv = (int32_t)((uint32_t)cq - (uint32_t)L.qsum[m] - (uint32_t)L.z[m] * (uint32_t)rs[b]);
-          vals[j] = epilogue(sr[b], accv, L.s_act[m]);
+          const int b = j >> 2, v = j & 3;
+          cq[j] = acc1[b][v] + (acc4[b][v] >> 2) + (acc16[b][v] >> 4);
         }
       }
-      if (ob.n == MAXU) flush_out(ob, meta, lane);
+      if (!wmajor && ob.n == MAXU) flush_out(ob, meta, lane);
+      const int slot = wmajor ? ob.n + (u - g0) : ob.n;
+      if (wmajor && p > 0) {
+        // the earlier windows' sums, held in the slot as int32 bits
+#pragma unroll
+        for (int i = 0; i < MAXU; ++i)
+          if (i == slot) {
+#pragma unroll
+            for (int j = 0; j < NV; ++j) cq[j] += __float_as_int(ob.v[i][j]);
+          }
+      }
+      float vals[NV];
+      if (last_pass) {
+        if (T == 8) {
+          const int bs = g >> 1;
+          const int32_t rsel = bs ? rs[1] : rs[0];
+          const float ssel = bs ? sr[1] : sr[0];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int m = 4 * (g & 1) + v;
+            const int32_t accv = (int32_t)((uint32_t)cq[v] - (uint32_t)L.qsum[m] - (uint32_t)L.z[m] * (uint32_t)rsel);
+            vals[v] = epilogue(ssel, accv, L.s_act[m]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NV; ++j) {
+            const int b = j >> 2, m = (4 * g + (j & 3)) & (T - 1);
+            const int32_t accv = (int32_t)((uint32_t)cq[j] - (uint32_t)L.qsum[m] - (uint32_t)L.z[m] * (uint32_t)rs[b]);
+            vals[j] = epilogue(sr[b], accv, L.s_act[m]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) vals[j] = __int_as_float(cq[j]);
+      }
 #pragma unroll
       for (int i = 0; i < MAXU; ++i)
-        if (i == ob.n) {
+        if (i == slot) {
 #pragma unroll
           for (int j = 0; j < NV; ++j) ob.v[i][j] = vals[j];
         }
-      OutMeta mt;
-      mt.y = a.y;
-      mt.ldy = a.ldy;
-      mt.M = M;
-      mt.base = base;
-      mt.row_hi = row_hi;
-      mt.pad[0] = mt.pad[1] = 0;
-      meta[ob.n] = mt;  // every lane writes the same entry
-      ob.n = ob.n + 1;
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) src[i] = nsrc[i];
-      continue;
-    }
-    int32_t zt[4];
-    float sa[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      zt[v] = zpoint ? L.z[(4 * g + v) & (T - 1)] : 0;
-      sa[v] = L.s_act[(4 * g + v) & (T - 1)];
-    }
-#pragma unroll
-    for (int b = 0; b < R; ++b) {
-      const int row = base + 16 * b + r;
-      if (row >= row_hi) continue;
+      if (last_pass) {
+        OutMeta mt;
+        mt.y = a.y;
+        mt.ldy = a.ldy;
+        mt.M = M;
+        mt.base = row_lo + u * ROWS + 16 * R * w;
+        mt.row_hi = row_hi;
+        mt.pad[0] = mt.pad[1] = 0;
+        meta[slot] = mt;  // every lane writes the same entry
+        if (!wmajor)
+          ob.n = ob.n + 1;
+        else if (u == g0 + gn - 1)
+          ob.n = ob.n + gn;
+      }
+    } else {
+      int32_t zt[4];
+      float sa[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int m = 4 * g + v;
-        if (m < M) {
-          const int32_t cq = acc1[b][v] + (acc4[b][v] >> 2) + (acc16[b][v] >> 4);  // sum(c*q)
-          const int32_t accv = (int32_t)((uint32_t)cq - (uint32_t)L.qsum[m] -
-                                         (uint32_t)zt[v] * (uint32_t)rs[b]);
-          // byte offset of (m, row) in y and acc: below 2^32 (checked by the host)
-          const uint32_t off = ((uint32_t)m * (uint32_t)a.ldy + (uint32_t)row) * 4u;
-          if (partial) {
-            __hip_atomic_fetch_add((int32_t __attribute__((address_space(1)))*)(
-                                       reinterpret_cast<char*>(a.y) + off),
-                                   accv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          } else {
-            store_g(reinterpret_cast<float*>(reinterpret_cast<char*>(a.y) + off),
-                    epilogue(sr[b], accv, sa[v]));
-            if (a.acc) store_g(reinterpret_cast<int32_t*>(reinterpret_cast<char*>(a.acc) + off), accv);
+        zt[v] = zpoint ? L.z[(4 * g + v) & (T - 1)] : 0;
+        sa[v] = L.s_act[(4 * g + v) & (T - 1)];
+      }
+#pragma unroll
+      for (int b = 0; b < R; ++b) {
+        const int row = base + 16 * b + r;
+        if (row >= row_hi) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int m = 4 * g + v;
+          if (m < M) {
+            const int32_t cq = acc1[b][v] + (acc4[b][v] >> 2) + (acc16[b][v] >> 4);  // sum(c*q)
+            const int32_t accv = (int32_t)((uint32_t)cq - (uint32_t)L.qsum[m] -
+                                           (uint32_t)zt[v] * (uint32_t)rs[b]);
+            // byte offset of (m, row) in y and acc: below 2^32 (checked by the host)
+            const uint32_t off = ((uint32_t)m * (uint32_t)a.ldy + (uint32_t)row) * 4u;
+            if (partial) {
+              __hip_atomic_fetch_add((int32_t __attribute__((address_space(1)))*)(
+                                         reinterpret_cast<char*>(a.y) + off),
+                                     accv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+              store_g(reinterpret_cast<float*>(reinterpret_cast<char*>(a.y) + off),
+                      epilogue(sr[b], accv, sa[v]));
+              if (a.acc) store_g(reinterpret_cast<int32_t*>(reinterpret_cast<char*>(a.acc) + off), accv);
+            }
           }
         }
       }
     }
 #pragma unroll
     for (int i = 0; i < NLD; ++i) src[i] = nsrc[i];
+    tb += ke - kb;
+    if (!has_next) break;
+    u = nu;
+    p = np;
   }
 }
 
@@ -684,7 +781,7 @@ __global__ __launch_bounds__(kBlock) void mfma_wg_stack_kernel(const StackHeader
 }
 
 // M <= 8, every K a multiple of 64: the activation-window kernel.
-__global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void mfma_win_linear_kernel(LinearArgs a) {
+__global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_win_linear_kernel(LinearArgs a) {
   __shared__ __attribute__((aligned(16))) WinTiles<8> L;
   WinStaged staged;
   OutBuf<0, 4> ob;
@@ -749,7 +846,7 @@ __global__ __launch_bounds__(WinGeo<16>::BLOCK) __attribute__((amdgpu_waves_per_
 // (the windows add int32 partial sums into them), after it each sum becomes
 // y = (s_row * acc) * s_act, and acc when asked for.  One workgroup per
 // (split linear, token).
-__global__ __launch_bounds__(256) void split_clear_kernel(const StackHeader* __restrict__ h) {
+__global__ __launch_bounds__(kSplitBlock) void split_clear_kernel(const StackHeader* __restrict__ h) {
   const char* base = reinterpret_cast<const char*>(h);
   const LinearArgs* lin = reinterpret_cast<const LinearArgs*>(base + h->off_lin);
   const int32_t* split = reinterpret_cast<const int32_t*>(base + h->off_split);
@@ -760,7 +857,7 @@ __global__ __launch_bounds__(256) void split_clear_kernel(const StackHeader* __r
   for (int row = threadIdx.x; row < a.N; row += blockDim.x) store_g(y + row, 0);
 }
 
-__global__ __launch_bounds__(256) void split_finish_kernel(const StackHeader* __restrict__ h) {
+__global__ __launch_bounds__(kSplitBlock) void split_finish_kernel(const StackHeader* __restrict__ h) {
   const char* base = reinterpret_cast<const char*>(h);
   const LinearArgs* lin = reinterpret_cast<const LinearArgs*>(base + h->off_lin);
   const int32_t* split = reinterpret_cast<const int32_t*>(base + h->off_split);
@@ -799,13 +896,13 @@ bool mfma_can_split(int32_t variant) {
 }
 
 hipError_t launch_split_clear(const void* ws, const LaunchShape& shp, hipStream_t s) {
-  hipLaunchKernelGGL(split_clear_kernel, dim3((unsigned)(shp.splits * shp.M)), dim3(256), 0, s,
+  hipLaunchKernelGGL(split_clear_kernel, dim3((unsigned)(shp.splits * shp.M)), dim3(kSplitBlock), 0, s,
                      static_cast<const StackHeader*>(ws));
   return hipGetLastError();
 }
 
 hipError_t launch_split_finish(const void* ws, const LaunchShape& shp, hipStream_t s) {
-  hipLaunchKernelGGL(split_finish_kernel, dim3((unsigned)(shp.splits * shp.M)), dim3(256), 0, s,
+  hipLaunchKernelGGL(split_finish_kernel, dim3((unsigned)(shp.splits * shp.M)), dim3(kSplitBlock), 0, s,
                      static_cast<const StackHeader*>(ws));
   return hipGetLastError();
 }
@@ -843,6 +940,14 @@ int mfma_unit_rows(int32_t variant) {
 
 int mfma_unit_restages(int32_t variant, int64_t K) {
   return mfma_is_window(variant) && K > kWinK ? (int)((K + kWinK - 1) / kWinK) : 0;
+}
+
+int mfma_held_units(int32_t variant) {
+  return variant == kWinVariant ? kOutUnits : variant == kWin16Variant ? kOut16Units : 0;
+}
+
+bool mfma_window_major(int32_t variant, int64_t K, bool y_only) {
+  return mfma_is_window(variant) && y_only && K > kWinK && K % kWinK == 0;
 }
 
 template <typename F>

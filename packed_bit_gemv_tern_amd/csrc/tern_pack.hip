@@ -126,6 +126,8 @@ dim3 rows_grid(int64_t N) { return dim3((unsigned)((N + kWaves - 1) / kWaves)); 
 
 }  // namespace
 
+int64_t pack_work_items(int64_t N) { return (N + kWaves - 1) / kWaves * kBlock; }
+
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s) {
   hipLaunchKernelGGL(zero_i32_kernel, dim3((n + kBlock - 1) / kBlock), dim3(kBlock), 0, s, p, n);
   return hipGetLastError();

@@ -260,6 +260,13 @@ int packed5_lanes_per_row(int64_t K) {
   return s8 < s16 ? 8 : 16;
 }
 
+int64_t pack5_work_items(int64_t N) { return (N + kP5Waves - 1) / kP5Waves * kP5Block; }
+
+int64_t gemv5_work_items(int64_t N, int64_t K) {
+  const int64_t ur = (64 / packed5_lanes_per_row(K)) * (packed5_lanes_per_row(K) == 8 ? 2 : 4);
+  return ((N + ur - 1) / ur + kP5Waves - 1) / kP5Waves * kP5Block;
+}
+
 hipError_t launch_pack5(const int8_t* w, int64_t N, int64_t K, int64_t ldw, uint8_t* packed,
                         int32_t* rowsum, int32_t* bad, hipStream_t s) {
   const int words = (int)(4 * ((K + 79) / 80));

@@ -99,6 +99,12 @@ __global__ __launch_bounds__(kQuantBlock) void wquant_kernel(const float* W, int
 
 }  // namespace
 
+int64_t quantize_weights_work_items(int64_t N, int64_t K, int64_t B) {
+  return (N * ((K + B - 1) / B) + kQuantBlock - 1) / kQuantBlock * kQuantBlock;
+}
+
+int64_t quantize_act_work_items(int64_t M) { return M * kQuantBlock; }
+
 hipError_t launch_quantize_weights(const float* W, int64_t N, int64_t K, int64_t ldw, int64_t B,
                                    int8_t* t, int64_t ldt, float* s_b, hipStream_t s) {
   const int64_t nb = (K + B - 1) / B;

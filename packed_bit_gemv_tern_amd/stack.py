@@ -84,8 +84,13 @@ class DeviceStack:
         return sum(pl.N * pl.K for pl in self.linears)
 
     def bind(self, M: int, path: int = tern.TERN_PATH_AUTO, with_acc: bool = False,
-             act_seed: int | None = None) -> "StackBinding":
-        return StackBinding(self, M, path, with_acc, self.seed if act_seed is None else act_seed)
+             act_seed: int | None = None, share_inputs: bool = False) -> "StackBinding":
+        """Buffers and a prepared launch for M tokens.  With ``share_inputs``
+        the linears of a layer that read one input (``synth.INPUT_LEADER``:
+        q/k/v, gate/up) are given one activation buffer, drawn for the
+        group's first linear; otherwise every linear has its own."""
+        return StackBinding(self, M, path, with_acc, self.seed if act_seed is None else act_seed,
+                            share_inputs)
 
 
 @dataclass
@@ -96,6 +101,7 @@ class StackBinding:
     path: int
     with_acc: bool
     act_seed: int
+    share_inputs: bool = False
     q: list = field(default_factory=list)
     s_act: list = field(default_factory=list)
     z: list = field(default_factory=list)
@@ -106,14 +112,19 @@ class StackBinding:
     def __post_init__(self):
         dev, M = self.stack.device, self.M
         descs = []
+        shared = {}  # (layer, leader idx) -> (q, s_act, z) host arrays and device tensors
         for pl in self.stack.linears:
-            q, s_act, z = synth.make_activations(self.act_seed, pl.layer, pl.idx, pl.K, M)
-            ldq = _pad16(pl.K)
-            qp = np.zeros((M, ldq), np.int8)
-            qp[:, : pl.K] = q
-            qd = torch.from_numpy(qp).to(dev)
-            sd = torch.from_numpy(s_act).to(dev)
-            zd = torch.from_numpy(z).to(dev)
+            src = synth.INPUT_LEADER[pl.idx] if self.share_inputs else pl.idx
+            key = (pl.layer, src)
+            if key not in shared:
+                q, s_act, z = synth.make_activations(self.act_seed, pl.layer, src, pl.K, M)
+                ldq = _pad16(pl.K)
+                qp = np.zeros((M, ldq), np.int8)
+                qp[:, : pl.K] = q
+                shared[key] = ((q, s_act, z), torch.from_numpy(qp).to(dev), torch.from_numpy(s_act).to(dev),
+                               torch.from_numpy(z).to(dev))
+            (q, s_act, z), qd, sd, zd = shared[key]
+            ldq = qd.shape[1]
             yd = torch.empty((M, pl.N), dtype=torch.float32, device=dev)
             ad = torch.empty((M, pl.N), dtype=torch.int32, device=dev) if self.with_acc else None
             self.q.append(qd)

@@ -67,6 +67,14 @@ LAYERS_06B = 28
 P_ZERO_DEFAULT = 0.626
 P_ZERO_ATTENTION = 0.62
 
+# Linears of a decoder layer that read the same input (both tables above use
+# the order q, k, v, o, gate, up, down): the query, key and value projections
+# all take the layer's normalised hidden state, and the gate and up
+# projections of the gated feed-forward block take the same input (model
+# card "Architecture": grouped-query attention, SwiGLU).  Entry idx is the
+# linear whose activations linear idx reads.
+INPUT_LEADER = (0, 0, 0, 3, 4, 4, 6)
+
 # 0-based layer -> zero share, for the feed-forward spike.
 _DOWN_SPIKE = {0: 0.6059, 1: 0.70, 2: 0.7247, 3: 0.70}
 _GATE_SPIKE = {1: 0.70, 2: 0.70, 3: 0.7048}

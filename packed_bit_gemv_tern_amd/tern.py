@@ -24,6 +24,7 @@ TERN_ERR_HIP = 6
 TERN_PATH_AUTO, TERN_PATH_VALU, TERN_PATH_MFMA = 0, 1, 2
 TERN_MAX_K = 5600000
 TERN_VALU_MAX_M = 8
+TERN_MAX_ROWS_PACK = 67108860
 TERN_BLOCK_MAX_K = 16384
 TERN_HEAD_MAX_M = 8
 TERN_HEAD_MAX_K = 43803
@@ -65,7 +66,7 @@ class tern_stack_plan(ctypes.Structure):
         ("L", ctypes.c_int32), ("M", ctypes.c_int32), ("path", ctypes.c_int32),
         ("grid", ctypes.c_int32), ("block", ctypes.c_int32), ("workers", ctypes.c_int32),
         ("segments", ctypes.c_int32), ("kernel", ctypes.c_int32), ("bytes", ctypes.c_int64),
-        ("splits", ctypes.c_int32), ("pad", ctypes.c_int32),
+        ("splits", ctypes.c_int32), ("restages", ctypes.c_int32),
     ]
 
 

@@ -32,6 +32,14 @@ def test_header_lists_the_four_calls_and_helpers():
     assert set(names) == set(tern.EXPORTS)
 
 
+def test_header_constants_match_the_binding():
+    with open(HEADER) as f:
+        defs = dict(re.findall(r"^#define (TERN\w+) (\d+)\s*$", f.read(), flags=re.M))
+    assert defs, "no constants found"
+    for name, value in defs.items():
+        assert getattr(tern, name) == int(value), name
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
@@ -253,5 +261,25 @@ def test_weight_quantiser_argument_errors(lib):
         assert wq(**{field: None}) == tern.TERN_ERR_INVALID_ARG, field
     assert wq(W=A16 + 2) == tern.TERN_ERR_ALIGNMENT
     assert wq(s=A16 + 1) == tern.TERN_ERR_ALIGNMENT
-    # one thread per (row, block): more than 2^40 of them is refused
+    # one thread per (row, block) in one launch, which counts at most
+    # 2^32 - 1 work-items: 2^24 rows x 256 one-column blocks is one too many
+    assert wq(N=2 ** 24, K=256, ldw=256, ldt=256, B=1) == tern.TERN_ERR_RANGE
     assert wq(N=2 ** 31 - 1, K=2 ** 20, ldw=2 ** 20, ldt=2 ** 20, B=1) == tern.TERN_ERR_RANGE
+
+
+def test_dispatch_size_limits(lib):
+    # Each launch below would need 2^32 or more work-items (its grid times
+    # its 256-thread workgroups): refused up front with TERN_ERR_RANGE.
+    n = tern.TERN_MAX_ROWS_PACK + 1  # one wave per row, four rows per workgroup
+    assert (n + 3) // 4 * 256 > 2 ** 32 - 1 >= (n - 1 + 3) // 4 * 256
+    assert lib.tern_pack(A16, n, 64, 64, A16, A16, None, S) == tern.TERN_ERR_RANGE
+    assert lib.tern_unpack(A16, n, 64, A16, 64, S) == tern.TERN_ERR_RANGE
+    assert lib.tern_validate(A16, n, 64, A16, S) == tern.TERN_ERR_RANGE
+    assert lib.tern_head_rowsum(A16, 2 ** 26 - 3, 64, 64, A16, S) == tern.TERN_ERR_RANGE
+    assert lib.tern_pack5(A16, 2 ** 26 - 3, 64, 64, A16, A16, None, S) == tern.TERN_ERR_RANGE
+    # 1.6-bit GEMV at K = 100: 16 rows per wave, four waves per workgroup
+    assert lib.tern_gemv5(A16, A16, A16, 2 ** 30, 100, A16, A16, A16, A16, None, S) == tern.TERN_ERR_RANGE
+    # block row sums: one thread per (row, block)
+    assert lib.tern_block_rowsum(A16, 2 ** 26, 4096, 64, A16, S) == tern.TERN_ERR_RANGE
+    # activation quantiser: one workgroup per token
+    assert lib.tern_quantize_act(A16, 2 ** 24, 64, 64, A16, 64, A16, A16, S) == tern.TERN_ERR_RANGE

@@ -1,55 +1,99 @@
-"""Full-size parity: the whole 8B-shaped stack (252 linears, 6.95 G weights)
-in the launch configuration the benchmark times, at M = 1 and M = 8.  The
-oracle computes at least 256 sampled rows of every linear (first and last row
-included) from the same seeded weights and activations; the sampled packed
-bytes are compared too."""
+"""Full-size parity: the whole 8B-shaped stack (252 linears, 6.95 G weights,
+1,400,832 output rows) in the launch configuration the benchmark times, at
+M = 1 and M = 8, y only (the benchmark's configuration: at M = 8 the outputs
+are held in registers until each workgroup's run ends) and with acc, and at
+M = 16 (y only).  Every
+output row of every linear is compared with the oracle, which recomputes
+each linear from the same seeded weights and activations; every packed byte
+and row sum is compared too.  The stack is also run with the input sharing
+of a real layer (q/k/v and gate/up reading one activation buffer each)."""
 import numpy as np
 import pytest
 
 import oracle
+from packed_bit_gemv_tern_amd import synth
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 from gpu_util import RTOL  # noqa: E402
 
+SEED = 0
+CHUNKS = 6  # layers are checked in six groups of six
+
 
 @pytest.fixture(scope="module")
-def stack():
+def runs():
+    """Device stack, and host copies of y (and acc) of each configuration
+    after two back-to-back launches of its plan."""
     from packed_bit_gemv_tern_amd.stack import DeviceStack
-    st = DeviceStack("8b", seed=0, threads=16, sample_rows=256)
-    yield st
+    st = DeviceStack("8b", seed=SEED, threads=16)
+    out = {}
+    for M, with_acc, share in [(1, True, False), (8, True, False), (1, False, False), (8, False, False),
+                               (8, False, True), (16, False, False)]:
+        b = st.bind(M, with_acc=with_acc, share_inputs=share)
+        assert b.plan.L == 252
+        assert b.plan.splits == 0  # a full stack keeps every linear whole
+        b.run()
+        b.run()
+        torch.cuda.synchronize()
+        out[(M, with_acc, share)] = ([y.cpu().numpy() for y in b.y],
+                                     [a.cpu().numpy() for a in b.acc] if with_acc else None,
+                                     b.plan.restages)
+        del b
+        torch.cuda.empty_cache()
+    yield st, out
     del st
     torch.cuda.empty_cache()
 
 
-@pytest.mark.timeout(600)
-@pytest.mark.parametrize("M,with_acc", [(1, True), (8, True), (1, False), (8, False), (16, False)])
-def test_full_8b_stack_sampled(stack, M, with_acc):
-    # y only is the benchmark's configuration; at M = 8 its outputs are held
-    # in registers until each worker's run ends
-    b = stack.bind(M, with_acc=with_acc)
-    assert b.plan.L == 252
-    assert b.plan.splits == 0  # a full stack keeps every linear whole
-    b.run()
-    b.run()  # the benchmark launches the same plan back to back
-    torch.cuda.synchronize()
-    checked = 0
-    for i, pl in enumerate(stack.linears):
-        rows = pl.sample_rows
-        q, s_act, z = b.host_act[i]
-        rp, rr, bad = oracle.pack(pl.sample_w)
+def _check(y, ry32, ry64, ctx):
+    assert np.all(np.abs(y.astype(np.float64) - ry64) <= RTOL * np.abs(ry64)), ctx
+    assert np.array_equal(y.view(np.uint32), ry32.view(np.uint32)), ctx
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("chunk", range(CHUNKS))
+def test_full_8b_stack_every_row(runs, chunk):
+    st, out = runs
+    specs = st.specs
+    per = len(specs) // CHUNKS
+    rows = 0
+    for i in range(chunk * per, (chunk + 1) * per):
+        layer, idx, name, N, K, p0 = specs[i]
+        pl = st.linears[i]
+        w, s_row = synth.make_weights(SEED, layer, idx, N, K, p0)
+        rp, rr, bad = oracle.pack(w)
         assert bad == 0
-        got_packed = pl.packed[torch.from_numpy(rows).to(pl.packed.device)].cpu().numpy()
-        assert np.array_equal(got_packed, rp), pl.name
-        assert np.array_equal(pl.rowsum.cpu().numpy()[rows], rr), pl.name
-        racc, ry32, ry64 = oracle.linear(rp, pl.sample_s_row, rr, pl.K, q, s_act, z)
-        if with_acc:
-            assert np.array_equal(b.acc[i].cpu().numpy()[:, rows], racc), pl.name
-        y = b.y[i].cpu().numpy()[:, rows]
-        assert np.all(np.abs(y.astype(np.float64) - ry64) <= RTOL * np.abs(ry64)), pl.name
-        assert np.array_equal(y.view(np.uint32), ry32.view(np.uint32)), pl.name
-        checked += rows.size
-    assert checked >= 252 * 256
+        assert np.array_equal(pl.packed.cpu().numpy(), rp), pl.name
+        assert np.array_equal(pl.rowsum.cpu().numpy(), rr), pl.name
+        for M in (1, 8):
+            q, s_act, z = synth.make_activations(SEED, layer, idx, K, M)
+            racc, ry32, ry64 = oracle.linear(rp, s_row, rr, K, q, s_act, z)
+            ys, accs, _ = out[(M, True, False)]
+            assert np.array_equal(accs[i], racc), (pl.name, M)
+            _check(ys[i], ry32, ry64, (pl.name, M, "with acc"))
+            ys, _, _ = out[(M, False, False)]
+            _check(ys[i], ry32, ry64, (pl.name, M, "y only"))
+        # 16 tokens (the 16-token window kernel), y only
+        q, s_act, z = synth.make_activations(SEED, layer, idx, K, 16)
+        _, ry32, ry64 = oracle.linear(rp, s_row, rr, K, q, s_act, z)
+        ys, _, _ = out[(16, False, False)]
+        _check(ys[i], ry32, ry64, (pl.name, 16, "y only"))
+        # q/k/v and gate/up sharing one input: the group's first linear's
+        # activations
+        src = synth.INPUT_LEADER[idx]
+        q, s_act, z = synth.make_activations(SEED, layer, src, K, 8)
+        _, ry32, ry64 = oracle.linear(rp, s_row, rr, K, q, s_act, z)
+        ys, _, _ = out[(8, False, True)]
+        _check(ys[i], ry32, ry64, (pl.name, 8, "shared inputs"))
+        rows += N
+    assert rows == sum(s[3] for s in specs[chunk * per:(chunk + 1) * per])
+
+
+def test_full_8b_stack_shared_inputs_restage_less(runs):
+    _, out = runs
+    # 36 layers x (q/k/v + gate/up): sharing saves window loads
+    assert out[(8, False, True)][2] < out[(8, False, False)][2]
 
 
 @pytest.fixture(scope="module")

@@ -376,6 +376,106 @@ def test_stack_mixed_shapes_and_empty_linear():
             assert_parity(y, acc, oracle_ref(lin), "mixed %s M=%d" % (lin.name, M))
 
 
+# Linears of a layer that read one input (q/k/v, gate/up) given one
+# activation buffer: the window kernel stages it once for consecutive
+# segments of a workgroup that read it.  0.6B shapes: every window ends past K
+# (K = 1,024, 2,048, 3,072), so the staged tail beyond K must read as zero.
+
+@pytest.mark.parametrize("M", [2, 5, 8])
+def test_stack_shared_inputs_06b(M):
+    from packed_bit_gemv_tern_amd.stack import DeviceStack
+    st = DeviceStack("0.6b", layers=3, seed=7, threads=8)
+    b = st.bind(M, with_acc=False, share_inputs=True)
+    b_ind = st.bind(M, with_acc=False)
+    assert b.plan.restages <= b_ind.plan.restages  # (a shallow stack gives each workgroup ~1 segment)
+    b.run()
+    b.run()
+    torch.cuda.synchronize()
+    for i, (layer, idx, name, N, K, p0) in enumerate(st.specs):
+        w, s_row = synth.make_weights(7, layer, idx, N, K, p0)
+        q, s_act, z = synth.make_activations(7, layer, synth.INPUT_LEADER[idx], K, M)
+        packed, rowsum, _ = oracle.pack(w)
+        ref = oracle.linear(packed, s_row, rowsum, K, q, s_act, z)
+        assert_parity(b.y[i].cpu().numpy(), None, ref, "shared %d.%s M=%d" % (layer, name, M))
+
+
+# Window-major order: linears of several whole 4,096-column windows whose
+# outputs are held (y only) are walked by each workgroup a window at a time
+# over a group of its units, the int32 sums of the earlier windows waiting in
+# the held slots.  About three such units per workgroup here, with 2, 3 and 4
+# windows; the linear that also returns acc walks unit by unit.
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("M", [2, 5, 8])
+def test_stack_window_major(M):
+    specs = [(98304, 8192, 1), (40960, 12288, 2), (16384, 16384, 3), (700, 12288, 4)]
+    lins = [synth.make_linear(31, sd, 0, N, K, 0.626, M, "wm%d" % sd) for (N, K, sd) in specs]
+    ups = [Uploaded(lin, with_acc=(i == 3)) for i, lin in enumerate(lins)]
+    ws = torch.empty(tern.tern_linear_stack_workspace_bytes(len(ups), M), dtype=torch.uint8, device=DEV)
+    plan = tern.tern_linear_stack_prepare([u.desc() for u in ups], M, ws)
+    assert plan.splits == 0
+    # window-major: fewer window loads than units x windows
+    unit_windows = sum((N + 255) // 256 * (K // 4096) for (N, K, _) in specs)
+    assert plan.restages < unit_windows // 2
+    tern.tern_linear_stack(plan)
+    tern.tern_linear_stack(plan)
+    for lin, up in zip(lins, ups):
+        y, acc = up.results()
+        assert_parity(y, acc, oracle_ref(lin), "window-major %s M=%d" % (lin.name, M))
+
+
+# Long K on every path: past 2^21 columns a plane-scaled int32 sum of a whole
+# row (16 * sum(c*q) for code plane 2 on the M <= 8 window kernel) would pass
+# 2^31, while the exact result is well inside int32.  All +1 weights with
+# q = -128 reach that bound; |acc| > 2^24 here, so the conversion to float
+# rounds (to nearest even on both sides) and y is compared bit for bit.
+
+LONG_K = 2_101_248  # 513 activation windows of 4,096 columns
+
+
+def _long_k_linear(M):
+    N, K = 16, LONG_K
+    w = np.ones((N, K), np.int8)
+    w[1] = -1
+    w[2, 1::2] = 0
+    w[3] = np.where(np.arange(K) % 3 == 0, -1, 1)
+    w[4:] = synth.ternary(np.random.default_rng(77), N - 4, K, 0.626)
+    q = np.full((M, K), -128, np.int8)
+    if M > 1:
+        q[1] = 127
+    z = np.array([0, 255, -3, 5, 0, 1, 2, 3][:M], np.int32)
+    return synth.Linear("longK", w, np.full(N, 0.01, np.float32), q,
+                        np.full(M, 0.02, np.float32), z)
+
+
+def _long_k_check(y, acc, lin, ctx):
+    packed, rowsum, _ = oracle.pack(lin.w)
+    racc, ry32, _ = oracle.linear(packed, lin.s_row, rowsum, lin.K, lin.q, lin.s_act, lin.z,
+                                  check=False)
+    assert abs(int(racc[0, 0])) > 2 ** 24  # the case the test is for
+    if acc is not None:
+        bad = np.argwhere(acc != racc)
+        assert bad.size == 0, "%s acc mismatch at %s: gpu %s oracle %s" % (
+            ctx, bad[:5].tolist(), acc[tuple(bad[0])], racc[tuple(bad[0])])
+    assert np.array_equal(y.view(np.uint32), ry32.view(np.uint32)), "%s y differs" % ctx
+
+
+@pytest.mark.parametrize("M", [1, 2, 8])
+def test_long_k_past_2_21_columns(M):
+    lin = _long_k_linear(M)
+    up = Uploaded(lin)
+    up.run()
+    y, acc = up.results()
+    _long_k_check(y, acc, lin, "long K call M=%d" % M)
+    # the stack launch, y only (held outputs on the window kernel)
+    up2 = Uploaded(lin, with_acc=False)
+    ws = torch.empty(tern.tern_linear_stack_workspace_bytes(1, M), dtype=torch.uint8, device=DEV)
+    plan = tern.tern_linear_stack_prepare([up2.desc()], M, ws)
+    tern.tern_linear_stack(plan)
+    y2, _ = up2.results()
+    _long_k_check(y2, None, lin, "long K stack M=%d" % M)
+
+
 @pytest.mark.parametrize("ldy", [(1 << 29) - 64, 1 << 29])
 def test_outputs_near_32bit_offsets(ldy):
     """M = 2 outputs rows ldy apart: (M * ldy * 4) just below 2^32 keeps the
