@@ -237,6 +237,28 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
 int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream);
 
 /*
+ * tern_linear_stack_prepare_static -- tern_linear_stack_prepare for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The schedule goes to a
+ * workspace the library holds instead of a caller's: a file-scope device
+ * array of TERN_STATIC_WORKSPACE_BYTES, one on each device the library runs
+ * on, held until the process ends.  Arguments, plan and results are those of
+ * tern_linear_stack_prepare without the workspace pair; TERN_ERR_RANGE when
+ * the stack's schedule needs more than TERN_STATIC_WORKSPACE_BYTES (the
+ * full 8B-shaped stack of 252 linears needs about 1.2 MB at M = 1).  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine): like the other prepare it copies the schedule in and
+ * synchronises `stream`.  Every static plan of a device shares that
+ * device's array, which keeps the last prepare's schedule: preparing another
+ * static plan replaces it (an earlier static plan must not be launched
+ * again), and a prepare that overlaps a launch of a static plan on the same
+ * device races with it.
+ */
+#define TERN_STATIC_WORKSPACE_BYTES 4194304
+int tern_linear_stack_prepare_static(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
+                                     tern_stack_plan* plan, hipStream_t stream);
+
+/*
  * Block-wise scales along K.  The article ("What's actually ternary")
  * groups each row's weights into fixed-size blocks along the input
  * dimension, each block with its own higher-precision scale; one scale per

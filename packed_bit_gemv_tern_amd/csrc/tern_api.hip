@@ -4,12 +4,18 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "tern.h"
 #include "tern_internal.h"
 
 using namespace tern;
+
+// The workspace of tern_linear_stack_prepare_static: each device holds its
+// own copy of this array, at its own address.  Host code never uses the
+// name itself (a host-side stand-in) but the device address looked up below.
+static __device__ __align__(256) uint8_t scratch[TERN_STATIC_WORKSPACE_BYTES];
 
 namespace {
 
@@ -110,6 +116,32 @@ constexpr double kSplitRatio = 3.0;
 constexpr int64_t kValuWaveBytes = 24 << 10;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Device address of `scratch` on the current device, looked up (with that
+// device current) the first time a device asks and kept per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return TERN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!p) return hip_fail(hipErrorInvalidSymbol);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return TERN_OK;
+}
+
+int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path, void* workspace,
+                  int64_t workspace_bytes, bool static_ws, tern_stack_plan* plan, hipStream_t stream);
 
 // Schedule cost of one activation-window restage, in streamed bytes: a
 // restage stalls its workgroup about 2 us (the barriers wait for its
@@ -359,6 +391,27 @@ int64_t tern_linear_stack_workspace_bytes(int64_t L, int64_t M) {
 int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
                               void* workspace, int64_t workspace_bytes, tern_stack_plan* plan,
                               hipStream_t stream) {
+  return stack_prepare(descs, L, M, path, workspace, workspace_bytes, false, plan, stream);
+}
+
+int tern_linear_stack_prepare_static(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
+                                     tern_stack_plan* plan, hipStream_t stream) {
+  if (!plan || L < 0 || M < 0) return TERN_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != TERN_OK) return st;
+  return stack_prepare(descs, L, M, path, ws, TERN_STATIC_WORKSPACE_BYTES, true, plan, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The schedule of tern_linear_stack_prepare into `workspace` (with
+// static_ws, the library's own: a schedule too large for it is a range
+// error rather than a workspace error).
+int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path, void* workspace,
+                  int64_t workspace_bytes, bool static_ws, tern_stack_plan* plan, hipStream_t stream) {
   if (!plan || L < 0 || M < 0) return TERN_ERR_INVALID_ARG;
   if (L > kI32Max || M > kI32Max) return TERN_ERR_RANGE;
   if (L > 0 && !descs) return TERN_ERR_INVALID_ARG;
@@ -590,7 +643,7 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   while (wk <= workers) seg_start[(size_t)wk++] = (int32_t)segs.size();
 
   const Layout lay = layout_for((int64_t)lin.size(), workers, (int64_t)segs.size(), (int64_t)split.size());
-  if (workspace_bytes < lay.total) return TERN_ERR_WORKSPACE;
+  if (workspace_bytes < lay.total) return static_ws ? TERN_ERR_RANGE : TERN_ERR_WORKSPACE;
   std::vector<char> host((size_t)lay.total, 0);
   StackHeader h;
   memset(&h, 0, sizeof(h));
@@ -670,6 +723,10 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
   }
   return TERN_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int tern_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int blocks_per_cu, int unroll,
                     int nontemporal, hipStream_t stream) {

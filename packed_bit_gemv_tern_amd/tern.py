@@ -25,6 +25,7 @@ TERN_PATH_AUTO, TERN_PATH_VALU, TERN_PATH_MFMA = 0, 1, 2
 TERN_MAX_K = 5600000
 TERN_VALU_MAX_M = 8
 TERN_MAX_ROWS_PACK = 67108860
+TERN_STATIC_WORKSPACE_BYTES = 4194304
 TERN_BLOCK_MAX_K = 16384
 TERN_HEAD_MAX_M = 8
 TERN_HEAD_MAX_K = 43803
@@ -34,7 +35,7 @@ TERN5_MAX_K = 65520
 EXPORTS = (
     "tern_row_bytes", "tern_pack", "tern_unpack", "tern_validate", "tern_gemv",
     "tern_gemm_smallM", "tern_linear_stack_workspace_bytes", "tern_linear_stack_prepare",
-    "tern_linear_stack", "tern_block_rowsum", "tern_gemv_blocked", "tern_quantize_act",
+    "tern_linear_stack", "tern_linear_stack_prepare_static", "tern_block_rowsum", "tern_gemv_blocked", "tern_quantize_act",
     "tern_quantize_weights", "tern_head_rowsum", "tern_head_gemv", "tern_row_bytes5", "tern_pack5", "tern_gemv5",
     "tern_read_probe",
     "tern_status_string", "tern_last_hip_error",
@@ -101,6 +102,8 @@ def _declare(lib):
         "tern_linear_stack_prepare": (i32, [ctypes.POINTER(tern_linear_desc), i64, i64, i32,
                                             vp, i64, ctypes.POINTER(tern_stack_plan), vp]),
         "tern_linear_stack": (i32, [ctypes.POINTER(tern_stack_plan), vp]),
+        "tern_linear_stack_prepare_static": (i32, [ctypes.POINTER(tern_linear_desc), i64, i64, i32,
+                                                   ctypes.POINTER(tern_stack_plan), vp]),
         "tern_block_rowsum": (i32, [vp, i64, i64, i64, vp, vp]),
         "tern_gemv_blocked": (i32, [vp, vp, vp, i64, i64, i64, vp, vp, vp, vp, vp]),
         "tern_quantize_act": (i32, [vp, i64, i64, i64, vp, i64, vp, vp, vp]),
@@ -248,6 +251,18 @@ def tern_linear_stack_prepare(descs, M, workspace, path=TERN_PATH_AUTO, stream=N
     _check(_lib().tern_linear_stack_prepare(arr, len(descs), int(M), int(path), _ptr(workspace),
                                             nbytes, ctypes.byref(plan), _stream(stream)),
            "tern_linear_stack_prepare")
+    return plan
+
+
+def tern_linear_stack_prepare_static(descs, M, path=TERN_PATH_AUTO, stream=None):
+    """As tern_linear_stack_prepare, with the schedule in the library's own
+    device workspace (allocates nothing; the last static prepare on a device
+    replaces the schedule of the one before)."""
+    arr = (tern_linear_desc * max(1, len(descs)))(*descs)
+    plan = tern_stack_plan()
+    _check(_lib().tern_linear_stack_prepare_static(arr, len(descs), int(M), int(path), ctypes.byref(plan),
+                                                   _stream(stream)),
+           "tern_linear_stack_prepare_static")
     return plan
 
 
