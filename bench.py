@@ -86,9 +86,15 @@ def kernel_name(plan) -> str:
         return "valu_stack_kernel<1, %s>" % _VALU_SETS[k]
     if k in (4, 5, 6):
         return "valu_stack_kernel<%d, 0u>" % {4: 2, 5: 4, 6: 8}[k]
-    v = k - 8
+    if 8 <= k < 12:
+        return "valu_stack_blk_kernel<%s>" % _VALU_SETS[k - 8]
+    v = k - 16
     if v == 8:
         return "mfma_win_stack_kernel<%s>" % ("true" if getattr(plan, "splits", 0) else "false")
+    if v == 12:
+        return "mfma_win_stack_kernel<false, true>"
+    if v == 13:
+        return "mfma_win16_stack_kernel<false, true>"
     if v in (9, 10):
         return "gemm_stack_kernel<%d>" % (64 if v == 9 else 128)
     if v == 11:
@@ -553,8 +559,39 @@ def suite(args):
     emit({"suite": "stack8b_m16", "workload": "full 8B-shaped stack (252 linears) at M = 16, one stack launch",
           "M": 16, "kernel": kernel_name(b16.plan), **_stats(us, b16.bytes)})
     del b16
+
+    # --- per-layer input sharing: q/k/v read one activation buffer, gate/up
+    # another (a real layer's call layout), beside independent activations
+    for M in (1, 8):
+        rec = {"suite": "stack8b_shared_inputs", "workload": "full 8B-shaped stack (252 linears), M = %d: "
+               "q/k/v and gate/up sharing one input per layer, against independent inputs" % M, "M": M}
+        for share in (False, True):
+            b = st.bind(M, share_inputs=share)
+            us = _event_times(lambda i: b.run(), 40)
+            # algorithmic bytes: a shared input is read once per group
+            nb_ = b.bytes - (108 * (M * 4096 + 8 * M) if share else 0)  # 3 reads saved per layer
+            rec["shared" if share else "independent"] = {"kernel": kernel_name(b.plan),
+                                                         "restages_per_pass": int(b.plan.restages),
+                                                         **_stats(us, nb_)}
+            del b
+        emit(rec)
     del st, Whd, srhd, rshd
     torch.cuda.empty_cache()
+
+    # --- block-wise scales inside the stack launch: the full 8B-shaped stack
+    # with one fp32 scale and int32 row sum per block of B columns (8 bytes
+    # of metadata per row and block counted in the bytes)
+    for B in (128, 512):
+        stb = DeviceStack("8b", seed=6, threads=16, block=B)
+        for M in ((1, 8) if B == 512 else (1,)):
+            b = stb.bind(M)
+            us = _event_times(lambda i: b.run(), 20)
+            emit({"suite": "stack8b_blocked", "workload": "full 8B-shaped stack (252 linears), block scales "
+                  "every %d columns, M = %d, one stack launch" % (B, M), "B": B, "M": M,
+                  "kernel": kernel_name(b.plan), **_stats(us, b.bytes)})
+            del b
+        del stb
+        torch.cuda.empty_cache()
 
     # --- activation quantiser (launch-bound at decode sizes)
     for M in (1, 8, 512):

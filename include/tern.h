@@ -176,6 +176,16 @@ typedef struct {
   float* y;
   int64_t ldy;
   int32_t* acc; /* may be NULL */
+  /* Block-wise scales along K (see "Block-wise scales" below): block = 0
+   * keeps one scale per row (s_row, rowsum).  block = B > 0 (a power of two
+   * in [64, 4096]; a multiple of 512 on the MFMA path, M >= 2) gives row i
+   * the scale s_block[i * nb + b] and row sum rowsum_block[i * nb + b] of
+   * each block b of B columns (nb = ceil(K / B); from tern_block_rowsum);
+   * s_row and rowsum are then not read and may be NULL.  acc, when given,
+   * receives sum_b acc_b. */
+  int64_t block;
+  const float* s_block;
+  const int32_t* rowsum_block;
 } tern_linear_desc;
 
 /* Host-side handle filled by tern_linear_stack_prepare (plain data; copy it
@@ -227,6 +237,10 @@ int64_t tern_linear_stack_workspace_bytes(int64_t L, int64_t M);
  * the kernel and written when its work ends: as always, y is complete once
  * the launch has completed on the stream, and no other work may read or
  * write it in between.
+ * A block-scaled linear (block > 0) needs K a multiple of 64; at M = 1 on the
+ * VALU path K <= 16,384, on the MFMA path B a multiple of 512: otherwise
+ * TERN_ERR_UNSUPPORTED.  plan->bytes counts 8 bytes of block metadata per
+ * row and block in place of the 8 per row.
  */
 int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
                               void* workspace, int64_t workspace_bytes,
@@ -267,9 +281,10 @@ int tern_linear_stack_prepare_static(const tern_linear_desc* descs, int64_t L, i
  * token
  *     acc_b = sum_{j in b} w_ij q_j - z * rowsum_b[i][b]          (int32, exact)
  *     y_i   = (sum_b s_b[i][b] * acc_b) * s_act                    (fp32)
- * The fp32 sum over blocks is taken in the kernel's own order: it differs
- * from any other order by rounding only, within
- * (nb + 1) * 2^-24 * |s_act| * sum_b |s_b[i][b] * acc_b|.
+ * The fp32 sum over blocks is taken in block order from +0, each product
+ * s_b * (float)acc_b and each partial sum rounded to nearest (the order the
+ * definition is written in), so y has the bits of that left-to-right
+ * evaluation.
  * Weights use the packed layout above; B is a power of two in [64, 4096]
  * and K <= TERN_BLOCK_MAX_K.  Metadata rows have stride nb.
  */

@@ -28,6 +28,9 @@ CFLAGS = [
     "-I", INCLUDE, "-I", CSRC,
     # no packed fp32 instructions in the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every fp32 product and sum rounded as written: no fused multiply-adds
+    # formed from separate operations
+    "-ffp-contract=off",
 ]
 
 

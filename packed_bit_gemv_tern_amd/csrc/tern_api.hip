@@ -114,6 +114,9 @@ constexpr int kValuOversubscribe = 16;
 // partial sums' atomics cost more than the shorter tail saves.
 constexpr double kSplitRatio = 3.0;
 constexpr int64_t kValuWaveBytes = 24 << 10;
+// Tokens up to which the MFMA path takes block-scaled linears (the
+// activation-window kernels).
+constexpr int64_t kMfmaBlockedMaxM = 16;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -147,9 +150,12 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
 // restage stalls its workgroup about 2 us (the barriers wait for its
 // slowest wave), about what a workgroup streams in 50 KB at M = 8.
 constexpr double kRestageCost = 40000.0;
-// Units a window-major group is taken to hold, for the schedule's cost of
-// its restages (each window is staged once per group)
-constexpr double kWindowMajorGroup = 8.0;
+// A window-major unit is charged its windows' restages divided by this many
+// units (each window is staged once per group; its restages stall longer
+// than unit-by-unit ones, the waves having drifted apart over a whole pass):
+// the 8B stack at M = 8 took 277.8 / 277.8 / 274.3 / 279.4 us at 8 / 4 /
+// 2.4 / 1.6 on one box.
+constexpr double kWindowMajorGroup = 2.4;
 
 struct Layout {
   int64_t off_lin, off_seg_start, off_seg, off_split, total;
@@ -419,13 +425,26 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
   if (p < 0) return TERN_ERR_UNSUPPORTED;
   // every descriptor is checked before anything is written
   int64_t bytes = 0;
+  bool any_blocked = false;
   for (int64_t i = 0; i < L; ++i) {
     const tern_linear_desc& d = descs[i];
-    const int st = check_linear(d.packed, d.s_row, d.rowsum, d.N, d.K, M, d.q, d.ldq, d.s_act,
-                                d.z, d.y, d.ldy, d.acc);
+    const bool blk = d.block != 0;
+    if (blk && !block_size_ok(d.block)) return TERN_ERR_INVALID_ARG;
+    // a block-scaled linear's metadata arrays stand in for s_row / rowsum
+    const int st = check_linear(d.packed, blk ? d.s_block : d.s_row, blk ? d.rowsum_block : d.rowsum, d.N,
+                                d.K, M, d.q, d.ldq, d.s_act, d.z, d.y, d.ldy, d.acc);
     if (st != TERN_OK) return st;
-    if (d.N > 0 && M > 0)
-      bytes += d.N * row_bytes(d.K) + 8 * d.N + M * d.K + 8 * M + 4 * M * d.N;
+    if (d.N == 0 || M == 0) continue;
+    const int64_t nb = blk ? (d.K + d.block - 1) / d.block : 1;
+    if (blk) {
+      any_blocked = true;
+      if (d.K % 64 != 0) return TERN_ERR_UNSUPPORTED;
+      if (p == TERN_PATH_VALU && (M > 1 || valu_blocked_variant(d.K, d.block) < 0)) return TERN_ERR_UNSUPPORTED;
+      if (p == TERN_PATH_MFMA && (M > kMfmaBlockedMaxM || d.block % mfma_step_k() != 0))
+        return TERN_ERR_UNSUPPORTED;
+      if (d.N * nb > kI32Max) return TERN_ERR_RANGE;
+    }
+    bytes += d.N * row_bytes(d.K) + 8 * d.N * nb + M * d.K + 8 * M + 4 * M * d.N;
   }
   memset(plan, 0, sizeof(*plan));
   plan->workspace = workspace;
@@ -439,17 +458,24 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
   if (!workspace) return TERN_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return TERN_ERR_WORKSPACE;
 
+  // the VALU variant of each linear (block-scaled ones: a variant whose
+  // lanes per row hold whole blocks)
+  auto variant_of = [&](const tern_linear_desc& d) -> int32_t {
+    if (d.block != 0 && p == TERN_PATH_VALU) return valu_blocked_variant(d.K, d.block);
+    return d.K % 64 ? (int32_t)VGEN : valu_variant_for(d.K);
+  };
   uint32_t used = 0;
   bool big = false;
   for (int64_t i = 0; i < L; ++i) {
     if (descs[i].N == 0) continue;
-    const int32_t v = descs[i].K % 64 ? (int32_t)VGEN : valu_variant_for(descs[i].K);
-    used |= 1u << v;
+    used |= 1u << variant_of(descs[i]);
     big = big || !mfma_win_offsets_fit(descs[i].N, row_bytes(descs[i].K), M, descs[i].ldy);
   }
   const bool ragged = (used >> VGEN) & 1u;
-  int32_t kernel = p == TERN_PATH_VALU ? valu_stack_kernel_for((int32_t)M, used)
-                                       : (int32_t)SK_MFMA + mfma_stack_variant((int32_t)M, ragged, big);
+  int32_t kernel = p == TERN_PATH_VALU ? valu_stack_kernel_for((int32_t)M, used, any_blocked)
+                                       : (int32_t)SK_MFMA + mfma_stack_variant((int32_t)M, ragged, big, any_blocked);
+  // block-scaled linears on the MFMA path: the activation-window kernels
+  if (p == TERN_PATH_MFMA && any_blocked && !mfma_is_window(kernel - SK_MFMA)) return TERN_ERR_UNSUPPORTED;
   const int cus = device_cus();
   if (cus <= 0) return hip_fail(hipErrorNoDevice);
   auto mfma_per_cu = [&](int32_t v) {
@@ -461,7 +487,8 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
   // prefill GEMM, whose tiles end sooner and which may split long K, takes
   // the stack instead; deeper stacks keep their kernel, which streams them
   // faster.
-  if (p == TERN_PATH_MFMA && M > 8 && (mfma_is_lockstep(kernel - SK_MFMA) || mfma_is_window(kernel - SK_MFMA))) {
+  if (p == TERN_PATH_MFMA && M > 8 && !any_blocked &&
+      (mfma_is_lockstep(kernel - SK_MFMA) || mfma_is_window(kernel - SK_MFMA))) {
     const int32_t v = kernel - SK_MFMA;
     const int unit = mfma_unit_rows(v);
     const double workers_v = (double)std::max(8, cus * mfma_per_cu(v) / 8 * 8);
@@ -494,8 +521,17 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
   std::vector<LinearArgs> lin((size_t)L);
   for (int64_t i = 0; i < L; ++i) {
     const tern_linear_desc& d = descs[i];
-    lin[(size_t)i] = make_args(d.packed, d.s_row, d.rowsum, d.N, d.K, M, d.q, d.ldq, d.s_act, d.z,
-                               d.y, d.ldy, d.acc);
+    LinearArgs& a = lin[(size_t)i];
+    a = make_args(d.packed, d.s_row, d.rowsum, d.N, d.K, M, d.q, d.ldq, d.s_act, d.z, d.y, d.ldy, d.acc);
+    if (d.block != 0 && d.N > 0) {
+      a.s_b = d.s_block;
+      a.rowsum_b = d.rowsum_block;
+      a.nb = (int32_t)((d.K + d.block - 1) / d.block);
+      int lg = 0;
+      while ((64ll << lg) < d.block) ++lg;
+      a.blg = lg;
+      if (p == TERN_PATH_VALU) a.variant = variant_of(d);
+    }
   }
   struct Gran {
     int32_t lin, r0, r1, flags;
@@ -507,13 +543,15 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
   // 0: segments hold rows; else the prefill GEMM's token tiles per row unit
   // (its segments hold tile indices)
   const int32_t ntok = p == TERN_PATH_VALU ? 0 : mfma_token_tiles(kernel - SK_MFMA, (int32_t)M);
-  const bool splittable = p == TERN_PATH_MFMA && mfma_can_split(kernel - SK_MFMA);
+  // (block-scaled linears are never split)
+  const bool splittable = p == TERN_PATH_MFMA && mfma_can_split(kernel - SK_MFMA) && !any_blocked;
   const int64_t wk_k = mfma_window_k();
   auto add_units = [&](int32_t li, int32_t flags) {
     const LinearArgs& a = lin[(size_t)li];
-    const int unit = p == TERN_PATH_VALU ? valu_unit_rows(a.variant, (int32_t)M)
+    const int unit = p == TERN_PATH_VALU ? (a.s_b ? valu_blocked_unit_rows(a.variant) : valu_unit_rows(a.variant, (int32_t)M))
                                          : mfma_unit_rows(kernel - SK_MFMA);
-    const double ld = 16.0 * a.nch;  // packed bytes of a row the unit reads
+    // bytes of a row the unit reads: packed weights (and block metadata)
+    const double ld = 16.0 * a.nch + (a.s_b ? 8.0 * a.nb : 0.0);
     // a unit that restages the activation window stalls its workgroup for
     // about as long as streaming kRestageCost bytes takes
     // (a 16-token window, M > 8, is twice the activation bytes to restage:

@@ -15,9 +15,10 @@
 // VALU path the lane forms S = sum c qb over its chunk (codes c = w + 1,
 // biased activations qb = q + 128, zero past K); the group sums S with DPP,
 // subtracts the block's activation sum and (z + 128) * rowsum_b (exact), and
-// converts; the scaled block values are then summed in fp32 across the
-// groups.  That summation order differs from the oracle's reference order
-// by rounding only, within (blocks + 1) * 2^-24 * s_act * sum_b |s_b acc_b|.
+// converts.  The group's first lane puts s_b * acc_b (one rounding) into the
+// wave's LDS row, and lane u then adds row u's products in block order from
+// +0 (one rounding each) -- the order of the definition, so y has the bits
+// of its left-to-right evaluation.
 //
 // Two units of U rows are in flight per wave (next unit's weights, block
 // scales and block row sums loaded before the current unit is reduced), all
@@ -71,54 +72,6 @@ __device__ __forceinline__ uint32_t group_sum_int(uint32_t v, int g) {
   return v;
 }
 
-template <int D>
-__device__ __forceinline__ float fpartner(float v) {
-  return __uint_as_float(partner<D>(__float_as_uint(v)));
-}
-
-// Transposed butterfly step on floats: lanes with bit D clear keep
-// a + partner's a, lanes with bit D set keep b + partner's b.
-template <int D>
-__device__ __forceinline__ float fsplit(float a, float b, int lane) {
-  if constexpr (D == 32) {
-    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  } else if constexpr (D == 16) {
-    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  } else {
-    const bool hi = (lane & D) != 0;
-    return (hi ? b : a) + fpartner<D>(hi ? a : b);
-  }
-}
-
-// Sum over the 64 / G groups of U values per lane (each group of G lanes
-// holds the same U values), U * G <= 64: the first log2(U) levels split the
-// values (transposed), so lane l ends with the total of value
-// (l >> log2(G)) & (U - 1) and the wave does about one level per value
-// instead of six.
-template <int LG, int U>
-__device__ __forceinline__ float reduce_groups(float (&v)[U], int lane) {
-  constexpr int G = 1 << LG;
-  static_assert(U * G <= 64, "groups");
-  if constexpr (U == 4) {
-    v[0] = fsplit<G>(v[0], v[1], lane);
-    v[1] = fsplit<G>(v[2], v[3], lane);
-    v[0] = fsplit<2 * G>(v[0], v[1], lane);
-  } else if constexpr (U == 2) {
-    v[0] = fsplit<G>(v[0], v[1], lane);
-  }
-  constexpr int D0 = G * U;  // first plain level
-  float x = v[0];
-  if constexpr (D0 <= 1) x += fpartner<1>(x);
-  if constexpr (D0 <= 2) x += fpartner<2>(x);
-  if constexpr (D0 <= 4) x += fpartner<4>(x);
-  if constexpr (D0 <= 8) x += fpartner<8>(x);
-  if constexpr (D0 <= 16) x += fpartner<16>(x);
-  if constexpr (D0 <= 32) x += fpartner<32>(x);
-  return x;
-}
-
 struct BlkArgs {
   const uint8_t* packed;
   const float* s_b;
@@ -135,10 +88,18 @@ struct BlkU {
   static constexpr int U = CPL == 1 ? 4 : CPL == 2 ? 2 : 1;
 };
 
+// LDS floats per wave for the row products: U rows of up to K / 64 blocks
+// (K <= 64 * 64 * CPL), a pitch of a multiple of 4 plus 4
+constexpr int kBlkProdWave = 288;
+
 template <int CPL, int LG>
 __global__ __launch_bounds__(kBlkBlock) void blocked_gemv_kernel(BlkArgs a) {
   constexpr int U = BlkU<CPL>::U;
   constexpr int g = 1 << LG;
+  static_assert(U * (64 * CPL + 8) <= kBlkProdWave, "products per wave");
+  __shared__ __attribute__((aligned(16))) float prods[kBlkWaves][kBlkProdWave];
+  float* prow = prods[threadIdx.x >> 6];
+  const int pitch = (a.nb + 3) / 4 * 4 + 4;
   const int lane = threadIdx.x & 63;
   const int gw = (int)blockIdx.x * kBlkWaves + (int)(threadIdx.x >> 6);
   const int nw = (int)gridDim.x * kBlkWaves;
@@ -201,10 +162,8 @@ __global__ __launch_bounds__(kBlkBlock) void blocked_gemv_kernel(BlkArgs a) {
       }
   };
   auto finish = [&](const Unit& c, int base) {
-    float f[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      f[u] = 0.0f;
 #pragma unroll
       for (int t = 0; t < CPL; ++t) {
         uint32_t p[4] = {0, 0, 0, 0};
@@ -220,24 +179,20 @@ __global__ __launch_bounds__(kBlkBlock) void blocked_gemv_kernel(BlkArgs a) {
         const uint32_t sc = p[0] + (p[1] >> 2) + (p[2] >> 4) + (p[3] >> 6);
         const uint32_t sb = group_sum_int(sc, g);
         const int32_t accb = (int32_t)(sb - qbb[t] - zb * (uint32_t)c.r[u][t]);
-        f[u] += __fmul_rn(c.s[u][t], (float)accb);  // zero for chunks past the row
+        const int ch = lane + 64 * t;
+        if ((lane & (g - 1)) == 0 && ch < a.nch) prow[u * pitch + ch / g] = __fmul_rn(c.s[u][t], (float)accb);
       }
+    }
+    wait_lds();  // the wave's products are in LDS (its own accesses complete in order)
+    float tot = 0.0f;
+    if (lane < U) {
+      const float* pr = prow + lane * pitch;
+      for (int b = 0; b < a.nb; ++b) tot = __fadd_rn(tot, pr[b]);
     }
     const uint32_t rows = (uint32_t)min(U, a.N - base) * 4u;
-    const auto ry = buffer_rsrc(a.y + base, rows);
-    if constexpr (U * g <= 64) {
-      // lane l holds row (l >> LG) & (U - 1); one lane per row stores
-      const float tot = reduce_groups<LG, U>(f, lane);
-      const bool writer = lane < U * g && (lane & (g - 1)) == 0;
-      buffer_store_u32(__float_as_uint(__fmul_rn(tot, sa)), ry, writer ? 4u * (uint32_t)(lane >> LG) : kDropOffset);
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float one[1] = {f[u]};
-        const float tot = reduce_groups<LG, 1>(one, lane);
-        buffer_store_u32(__float_as_uint(__fmul_rn(tot, sa)), ry, lane == 0 ? 4u * (uint32_t)u : kDropOffset);
-      }
-    }
+    buffer_store_u32(__float_as_uint(__fmul_rn(tot, sa)), buffer_rsrc(a.y + base, rows),
+                     lane < U ? 4u * (uint32_t)lane : kDropOffset);
+    wait_lds();  // every row is read before the next unit's products go in
   };
 
   const int step = nw * U;

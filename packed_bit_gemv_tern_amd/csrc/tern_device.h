@@ -154,9 +154,20 @@ __device__ __forceinline__ uint32_t group_sum(uint32_t x) {
   return reduce_split<LPR, 1>(v, 0);
 }
 
+// Wait for the wave's LDS accesses; no memory access moves across it.
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // y = (s_row * acc) * s_act with two round-to-nearest products.
 __device__ __forceinline__ float epilogue(float s_row, int32_t acc, float s_act) {
   return __fmul_rn(__fmul_rn(s_row, (float)acc), s_act);
+}
+
+// run + s * a with the product and the sum each rounded to nearest: HIP's
+// __fmul_rn / __fadd_rn are the plain operators, which the compiler would
+// otherwise fuse into one FMA (one rounding instead of two).
+__device__ __forceinline__ float add_product_rn(float run, float s, float a) {
+#pragma clang fp contract(off)
+  return run + s * a;
 }
 
 }  // namespace tern

@@ -25,12 +25,12 @@ enum ValuVariant : int32_t {
   kNumValuVariants = 9
 };
 
-// Device-side view of one linear layer; 96 bytes, read by the kernels from
+// Device-side view of one linear layer; 128 bytes, read by the kernels from
 // kernel arguments (single-linear calls) or from the stack workspace.
 struct alignas(16) LinearArgs {
   const uint8_t* packed;  // N rows of ld bytes
-  const float* s_row;     // N
-  const int32_t* rowsum;  // N
+  const float* s_row;     // N (null with block scales)
+  const int32_t* rowsum;  // N (null with block scales)
   const int8_t* q;        // M rows of ldq bytes
   const float* s_act;     // M
   const int32_t* z;       // M
@@ -38,8 +38,15 @@ struct alignas(16) LinearArgs {
   int32_t* acc;           // M rows of ldy int32, or null
   int32_t N, K, ld, nch;  // rows, columns, row bytes, 16-byte chunks per row
   int32_t ldq, ldy, M, variant;
+  // block-wise scales along K: null for one scale per row; else row i's
+  // block b (columns [64 * 2^blg * b, 64 * 2^blg * (b + 1)) inside K) has
+  // scale s_b[i * nb + b] and row sum rowsum_b[i * nb + b]
+  const float* s_b;
+  const int32_t* rowsum_b;
+  int32_t blg, nb;  // log2(block / 64), blocks per row
+  int32_t pad[2];
 };
-static_assert(sizeof(LinearArgs) == 96, "LinearArgs layout");
+static_assert(sizeof(LinearArgs) == 128, "LinearArgs layout");
 
 // One schedule entry: rows [row_begin, row_end) of linear `lin` (all
 // tokens); for the prefill GEMM instead its tiles [row_begin, row_end) in
@@ -71,12 +78,15 @@ constexpr int32_t kStackMagic = 0x7e54a11;
 // Kernel selectors of a prepared stack.
 // SK_VALU_M1 .. SK_VALU_M1 + 3 are the M = 1 kernel compiled for growing
 // variant sets (8B shapes, 0.6B shapes, every register variant, all).
+// SK_VALU_M1_BLK .. + 3: the same sets for stacks holding block-scaled
+// linears.
 enum StackKernel : int32_t {
   SK_VALU_M1 = 0,
   SK_VALU_M2 = 4,
   SK_VALU_M4 = 5,
   SK_VALU_M8 = 6,
-  SK_MFMA = 8  // SK_MFMA + mfma_stack_variant(M, ragged)
+  SK_VALU_M1_BLK = 8,
+  SK_MFMA = 16  // SK_MFMA + mfma_stack_variant(M, ragged)
 };
 
 // Launch parameters chosen by the launchers below.
@@ -129,13 +139,17 @@ bool mfma_per_workgroup(int32_t variant);
 int32_t valu_variant_for(int64_t K);
 
 // Persistent stack launches over a prepared workspace.
-int32_t valu_stack_kernel_for(int32_t M, uint32_t used_variants);
+int32_t valu_stack_kernel_for(int32_t M, uint32_t used_variants, bool blocked);
+// block-scaled linears at M = 1: the register variant (-1: none takes K) and
+// its rows per unit
+int32_t valu_blocked_variant(int64_t K, int64_t B);
+int valu_blocked_unit_rows(int32_t variant);
 hipError_t launch_valu_stack(int32_t kernel, const void* ws, const LaunchShape& shp,
                              hipStream_t s);
 int valu_stack_blocks_per_cu(int32_t kernel);
 // big: some linear's weight or output offsets do not fit the 32-bit offsets
 // of the activation-window kernel (see mfma_win_offsets_fit)
-int32_t mfma_stack_variant(int32_t M, bool ragged, bool big);
+int32_t mfma_stack_variant(int32_t M, bool ragged, bool big, bool blocked);
 bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy);
 // the prefill GEMM's variant for M tokens (any M >= 1, any K), and whether
 // `variant` is the lockstep kernel (a workgroup takes whole rows over all K)
@@ -144,6 +158,9 @@ bool mfma_is_lockstep(int32_t variant);
 // the activation-window kernel: is `variant` it, and its window width in K
 bool mfma_is_window(int32_t variant);
 int mfma_window_k();
+// K columns of one step of the window kernels (block scales there come in
+// whole steps)
+int mfma_step_k();
 // kernels that take linears split along K (window kernel, prefill GEMM), and
 // the fill and finishing kernels of split linears
 bool mfma_can_split(int32_t variant);

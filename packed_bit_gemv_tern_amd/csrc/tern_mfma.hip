@@ -270,13 +270,27 @@ struct WinGeo {
 };
 constexpr int kWinTile = 16 * kWinR * kStepBytes;
 
+// Block-wise scales (BLK): the block scale and row sum of a wave's 32 rows
+// for one block, by 4-byte DMA (lanes 0..31 the scales, 32..63 the row sums
+// of rows 16 (l / 16 % 2) + l % 16), in a ring of kBlkSlots per wave; and
+// each staged token's activation sum per 512-column piece of the window.
+constexpr int kBlkSlots = 4;
+template <int T, bool BLK>
+struct WinBlk {
+  uint32_t meta[WinGeo<T>::WAVES][kBlkSlots][64];
+  int32_t qpiece[T][8];
+};
 template <int T>
+struct WinBlk<T, false> {};
+
+template <int T, bool BLK = false>
 struct WinTiles {
   uint8_t w[WinGeo<T>::WAVES][WinGeo<T>::DEPTH][kWinTile];
   uint8_t q[T][kWinPitch];  // each 64-byte chunk stored dword-transposed
   int32_t qsum[T];          // sum of the token's activations over all of K
   int32_t z[T];             // zero points and scales of the staged tokens
   float s_act[T];
+  WinBlk<T, BLK> blk;
 };
 
 // s_waitcnt on this wave's global loads (LDS DMA included): at most N still
@@ -346,6 +360,9 @@ static_assert(sizeof(OutMeta) == 32, "OutMeta");
 // units a wave holds: what each kernel leaves free at 256 VGPRs (96 and
 // 112 registers)
 constexpr int kOutUnits = 24, kOut16Units = 14;
+// the same for the kernels of stacks with block scales (their running sums
+// take registers)
+constexpr int kOutUnitsBlk = 12, kOut16UnitsBlk = 6;
 
 // value j of a held unit: with 8 tokens row block g >> 1, token
 // 4 (g & 1) + j; with 16, row block j >> 2, token 4 g + (j & 3)
@@ -373,9 +390,14 @@ __device__ __forceinline__ void flush_out(OutBuf<MAXU, NV>& ob, const OutMeta* m
 // SPLIT: segments may be windows of linears split along K (their flags say
 // so); compiled apart so that the kernel for unsplit stacks carries none of it.
 // T: tokens staged (8: activation rows 8..15 of the MFMA repeat 0..7; 16).
-template <bool SPLIT, int MAXU, int T>
+// BLK: linears may carry block-wise scales along K (blocks of whole K-steps,
+// B a multiple of 512): each block's exact sum is finished and scaled at the
+// block's last step and added to a running fp32 sum per output value, in
+// block order from +0 -- the order of the definition.  Compiled apart so
+// that kernels for stacks without block scales carry none of it.
+template <bool SPLIT, int MAXU, int T, bool BLK = false>
 __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, int row_hi, int unit0,
-                                               int ustride, int lane, int w, WinTiles<T>& L,
+                                               int ustride, int lane, int w, WinTiles<T, BLK>& L,
                                                WinStaged& staged, int flags, OutBuf<MAXU, T / 2>& ob,
                                                OutMeta* meta) {
   constexpr int R = kWinR;
@@ -384,12 +406,18 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   constexpr int D = WinGeo<T>::DEPTH;
   constexpr int NV = T / 2;  // held values per unit and lane
   static_assert(D >= 1 && D <= 3, "tile depth");
+  static_assert(!BLK || D == 2, "block metadata counts assume two tiles in flight");
   static_assert(kWinR == 2, "one row block per half-wave");
   const int r = lane & 15, g = lane >> 4;
   const int lrow = lane >> 3, lpos = lane & 7;
   const int nch = a.nch, K = a.K, M = a.M;
   const int nks = (nch + 7) / 8;
   const int nwin = (K + kWinK - 1) / kWinK;
+  // block scales: K-steps per block
+  const bool blk = BLK && a.s_b != nullptr;
+  const int bks = blk ? (1 << a.blg) / 8 : 1;
+  const int nb = a.nb;
+  int mb_issue = 0, mb_use = 0;  // block-metadata ring slots: next to fill, block being summed
   const bool partial = SPLIT && (flags & kSegPartial) != 0;
   const bool zpoint = !partial || (flags & kSegZeroPoint) != 0;
   // y-only outputs are held in registers until the worker's run ends (a
@@ -413,9 +441,20 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
 #pragma unroll
     for (int i = 0; i < NLD; ++i) src[i] = (uint32_t)min(base + 8 * i + lrow, row_hi - 1) * (uint32_t)a.ld;
   };
-  // K-step ks of a unit into the slot of tile number t (tiles are numbered
-  // in the order the wave consumes them, across units)
-  auto issue = [&](const uint32_t (&src)[NLD], int ks, int t) {
+  // K-step ks of unit `unit` into the slot of tile number t (tiles are
+  // numbered in the order the wave consumes them, across units); with block
+  // scales the block's scales and row sums go first when ks starts a block
+  // (one DMA instruction, counted by the waits below)
+  auto issue = [&](const uint32_t (&src)[NLD], int ks, int t, int unit) {
+    if constexpr (BLK) {
+      if (blk && ks % bks == 0) {
+        const int brow = min(row_lo + unit * ROWS + 16 * R * w + 16 * ((lane >> 4) & 1) + (lane & 15), row_hi - 1);
+        const int64_t o = (int64_t)brow * nb + ks / bks;
+        const void* msrc = lane < 32 ? (const void*)(a.s_b + o) : (const void*)(a.rowsum_b + o);
+        __builtin_amdgcn_global_load_lds(msrc, (lds_ptr)&L.blk.meta[w][mb_issue][0], 4, 0, 0);
+        mb_issue = (mb_issue + 1) & (kBlkSlots - 1);
+      }
+    }
     uint8_t* tile = L.w[w][t % D];
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
@@ -424,8 +463,10 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
                                        (lds_ptr)(tile + 1024 * i), 16, 0, 2 /* nt */);
     }
   };
-  // rowsum and s_row of a unit's rows, loaded one unit ahead
+  // rowsum and s_row of a unit's rows, loaded one unit ahead (a block-scaled
+  // linear has neither: its pointers may be null)
   auto load_rowops = [&](int unit, int32_t (&rs)[R], float (&sr)[R]) {
+    if (blk) return;
     const int base = row_lo + unit * ROWS + 16 * R * w;
 #pragma unroll
     for (int b = 0; b < R; ++b) {
@@ -447,7 +488,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
     unit_src(unit0, src);
 #pragma unroll
     for (int d = 0; d < D; ++d)
-      if (d < depth) issue(src, d, d);
+      if (d < depth) issue(src, d, d, unit0);
     load_rowops(unit0, nrs, nsr);
   }
 
@@ -489,6 +530,25 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
     i32x4 acc1[R], acc4[R], acc16[R];
 #pragma unroll
     for (int b = 0; b < R; ++b) acc1[b] = acc4[b] = acc16[b] = i32x4{0, 0, 0, 0};
+    // block scales: the lane's values (as held: with 8 tokens row block
+    // g >> 1, tokens 4 (g & 1) + v; with 16 both row blocks, tokens 4g + v)
+    // as running fp32 sums over the blocks so far, and their int32 totals;
+    // window-major, a later pass resumes from the sum held in the unit's slot
+    float bsum[BLK ? NV : 1];
+    int32_t bint[BLK ? NV : 1];
+    if constexpr (BLK) {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) bsum[j] = 0.0f, bint[j] = 0;
+      if (blk && wmajor && p > 0) {
+        const int slot = ob.n + (u - g0);
+#pragma unroll
+        for (int i = 0; i < MAXU; ++i)
+          if (i == slot) {
+#pragma unroll
+            for (int j = 0; j < NV; ++j) bsum[j] = ob.v[i][j];
+          }
+      }
+    }
     for (int ks = kb; ks < ke; ++ks) {
       const uint8_t* tile = L.w[w][(tb + ks - kb) % D];
       if ((ks & 7) == 0) {
@@ -537,10 +597,18 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
           // w + WAVES, ... so no two waves write one entry
           for (int tq = w; tq < T; tq += WAVES) {
             uint32_t part = 0;
-            for (int off = 16 * lane; off < kWinK; off += 16 * 64) {
-              const u32x4 v = *reinterpret_cast<const u32x4*>(&L.q[tq][off]);
 #pragma unroll
-              for (int k = 0; k < 4; ++k) part = (uint32_t)__builtin_amdgcn_sdot4((int)v[k], 0x01010101, (int)part, false);
+            for (int i = 0; i < kWinK / 1024; ++i) {
+              const u32x4 v = *reinterpret_cast<const u32x4*>(&L.q[tq][16 * lane + 1024 * i]);
+              uint32_t pi = 0;
+#pragma unroll
+              for (int k = 0; k < 4; ++k) pi = (uint32_t)__builtin_amdgcn_sdot4((int)v[k], 0x01010101, (int)pi, false);
+              part += pi;
+              if constexpr (BLK) {
+                // the window's 512-column piece 2i + (lane >= 32): a half-wave sum
+                const uint32_t ph = group_sum<32>(pi);
+                if ((lane & 31) == 0) L.blk.qpiece[tq][2 * i + (lane >> 5)] = (int32_t)ph;
+              }
             }
             const int32_t tot = (int32_t)group_sum<64>(part);
             if (lane == 0) L.qsum[tq] = (win == 0 ? 0 : L.qsum[tq]) + tot;
@@ -564,8 +632,13 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
       // and other loads and stores in between only add to the count)
       {
         const int after = has_next ? depth - 1 : min(depth - 1, ke - 1 - ks);
+        // (the tile after this one carries its block's metadata DMA first
+        // when it starts a block)
+        const bool meta_after = BLK && blk && after == 1 && (ks + 1 < ke ? ks + 1 : nkb) % bks == 0;
         if (after >= 2)
           wait_vm<2 * NLD>();
+        else if (meta_after)
+          wait_vm<NLD + 1>();
         else if (after == 1)
           wait_vm<NLD>();
         else
@@ -590,9 +663,9 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
               tile + (16 * b + r) * kStepBytes + 16 * ((2 * g + half) ^ (r & 7)));
       wait_lgkm();  // tile read: it may be overwritten
       if (ks + depth < ke)
-        issue(src, ks + depth, tb + ks - kb + depth);
+        issue(src, ks + depth, tb + ks - kb + depth, u);
       else if (has_next)
-        issue(nsrc, nkb + ks + depth - ke, tb + ks - kb + depth);  // the next pass's first tiles
+        issue(nsrc, nkb + ks + depth - ke, tb + ks - kb + depth, nu);  // the next pass's first tiles
       // activations come from the window, which the loads never overwrite
       const uint8_t* qrow = &L.q[r & (T - 1)][64 * (8 * (ks & 7) + 2 * g)];
 #pragma unroll
@@ -612,13 +685,84 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
           acc1[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_i32x4(qv[3]), p3, acc1[b], 0, 0, 0);
         }
       }
+      if constexpr (BLK) {
+        if (blk && ((ks + 1) % bks == 0 || ks + 1 == nks)) {
+          // the block ends: acc_b = sum(c*q) - sum(q) - z * rowsum_b, exact;
+          // then one rounding for s_b * acc_b and one for the running sum.
+          // Its metadata landed with the tile of its first step.
+          const uint32_t* ms = L.blk.meta[w][mb_use];
+          mb_use = (mb_use + 1) & (kBlkSlots - 1);
+          const int kw = (ks & 7) / bks;  // block within the window (blocks never span windows)
+#pragma unroll
+          for (int j = 0; j < NV; ++j) {
+            const int b = T == 8 ? (g >> 1) : (j >> 2);
+            const int v = j & 3;
+            const int m = T == 8 ? 4 * (g & 1) + v : 4 * g + v;
+            const int32_t c1 = b ? acc1[1][v] : acc1[0][v];
+            const int32_t c4 = b ? acc4[1][v] : acc4[0][v];
+            const int32_t c16 = b ? acc16[1][v] : acc16[0][v];
+            int32_t qb = 0;
+            for (int k = kw * bks; k < kw * bks + bks; ++k) qb += L.blk.qpiece[m][k];
+            const int32_t accb = (int32_t)((uint32_t)(c1 + (c4 >> 2) + (c16 >> 4)) - (uint32_t)qb -
+                                           (uint32_t)L.z[m] * ms[32 + 16 * b + r]);
+            bsum[j] = add_product_rn(bsum[j], __uint_as_float(ms[16 * b + r]), (float)accb);
+            bint[j] += accb;
+          }
+#pragma unroll
+          for (int b = 0; b < R; ++b) acc1[b] = acc4[b] = acc16[b] = i32x4{0, 0, 0, 0};
+        }
+      }
     }
 
     // epilogue: lane holds tokens 4g + v of row base + 16b + r.  A window of
     // a linear split along K adds its exact partial sums into y, viewed as
     // int32 (cleared before the launch, finished after it); the zero-point
     // term belongs to one window only.
-    if (held) {
+    if (BLK && blk && held) {
+      // block scales, y only: the running sums (window-major, an earlier
+      // pass's sum stays in the slot until the last pass scales it)
+      if (!wmajor && ob.n == MAXU) flush_out(ob, meta, lane);
+      const int slot = wmajor ? ob.n + (u - g0) : ob.n;
+      float vals[NV];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int m = T == 8 ? 4 * (g & 1) + (j & 3) : (4 * g + (j & 3)) & (T - 1);
+        vals[j] = last_pass ? __fmul_rn(bsum[j], L.s_act[m]) : bsum[j];
+      }
+#pragma unroll
+      for (int i = 0; i < MAXU; ++i)
+        if (i == slot) {
+#pragma unroll
+          for (int j = 0; j < NV; ++j) ob.v[i][j] = vals[j];
+        }
+      if (last_pass) {
+        OutMeta mt;
+        mt.y = a.y;
+        mt.ldy = a.ldy;
+        mt.M = M;
+        mt.base = row_lo + u * ROWS + 16 * R * w;
+        mt.row_hi = row_hi;
+        mt.pad[0] = mt.pad[1] = 0;
+        meta[slot] = mt;
+        if (!wmajor)
+          ob.n = ob.n + 1;
+        else if (u == g0 + gn - 1)
+          ob.n = ob.n + gn;
+      }
+    } else if (BLK && blk) {
+      // block scales, y and acc stored at once: the lane's values
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int b = T == 8 ? (g >> 1) : (j >> 2);
+        const int m = T == 8 ? 4 * (g & 1) + (j & 3) : 4 * g + (j & 3);
+        const int row = base + 16 * b + r;
+        if (m < M && row < row_hi) {
+          const uint32_t off = ((uint32_t)m * (uint32_t)a.ldy + (uint32_t)row) * 4u;
+          store_g(reinterpret_cast<float*>(reinterpret_cast<char*>(a.y) + off), __fmul_rn(bsum[j], L.s_act[m]));
+          if (a.acc) store_g(reinterpret_cast<int32_t*>(reinterpret_cast<char*>(a.acc) + off), bint[j]);
+        }
+      }
+    } else if (held) {
       // the lane's held values: with 8 tokens row block g >> 1, tokens
       // 4 (g & 1) + v (the MFMA result holds tokens 0..7 twice); with 16
       // both row blocks, tokens 4g + v
@@ -790,11 +934,13 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2)
 }
 
 // The stack kernel: a worker's segments in order, y-only outputs held in
-// registers (kOutUnits units per wave) and stored at the end of the run.
-template <bool SPLIT>
+// registers (kOutUnits units per wave, kOutUnitsBlk in the kernel for stacks
+// with block scales) and stored at the end of the run.
+template <bool SPLIT, bool BLK = false>
 __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_win_stack_kernel(const StackHeader* __restrict__ h) {
-  __shared__ __attribute__((aligned(16))) WinTiles<8> L;
-  __shared__ OutMeta meta[kWinWaves][kOutUnits];
+  constexpr int MAXU = BLK ? kOutUnitsBlk : kOutUnits;
+  __shared__ __attribute__((aligned(16))) WinTiles<8, BLK> L;
+  __shared__ OutMeta meta[kWinWaves][MAXU];
   const int worker = xcd_logical_block();
   if (worker >= h->workers) return;  // the same for the whole workgroup
   const int lane = threadIdx.x & 63;
@@ -805,24 +951,26 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2)
   const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
   const int s1 = seg_start[worker + 1];
   WinStaged staged;
-  OutBuf<kOutUnits, 4> ob;
+  OutBuf<MAXU, 4> ob;
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
-    mfma_win_range<SPLIT, kOutUnits, 8>(a, sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged, SPLIT ? sg.flags : 0,
-                                     ob, meta[w]);
+    mfma_win_range<SPLIT, MAXU, 8, BLK>(a, sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged,
+                                        SPLIT ? sg.flags : 0, ob, meta[w]);
   }
   flush_out(ob, meta[w], lane);
 }
 
 // 9 <= M <= 16 tokens, every K a multiple of 64: the same window kernel with
 // all 16 activation rows staged, one 8-wave workgroup per CU, y-only outputs
-// held (kOut16Units units per wave).  (Only SPLIT = false is launched.)
-template <bool SPLIT>
+// held (kOut16Units units per wave, kOut16UnitsBlk with block scales).
+// (Only SPLIT = false is launched.)
+template <bool SPLIT, bool BLK = false>
 __global__ __launch_bounds__(WinGeo<16>::BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_win16_stack_kernel(
     const StackHeader* __restrict__ h) {
-  __shared__ __attribute__((aligned(16))) WinTiles<16> L;
-  __shared__ OutMeta meta[WinGeo<16>::WAVES][kOut16Units];
+  constexpr int MAXU = BLK ? kOut16UnitsBlk : kOut16Units;
+  __shared__ __attribute__((aligned(16))) WinTiles<16, BLK> L;
+  __shared__ OutMeta meta[WinGeo<16>::WAVES][MAXU];
   const int worker = xcd_logical_block();
   if (worker >= h->workers) return;  // the same for the whole workgroup
   const int lane = threadIdx.x & 63;
@@ -833,11 +981,11 @@ __global__ __launch_bounds__(WinGeo<16>::BLOCK) __attribute__((amdgpu_waves_per_
   const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
   const int s1 = seg_start[worker + 1];
   WinStaged staged;
-  OutBuf<kOut16Units, 8> ob;
+  OutBuf<MAXU, 8> ob;
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
-    mfma_win_range<SPLIT, kOut16Units, 16>(lin[sg.lin], sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged,
-                                           SPLIT ? sg.flags : 0, ob, meta[w]);
+    mfma_win_range<SPLIT, MAXU, 16, BLK>(lin[sg.lin], sg.row_begin, sg.row_end, 0, 1, lane, w, L, staged,
+                                         SPLIT ? sg.flags : 0, ob, meta[w]);
   }
   flush_out(ob, meta[w], lane);
 }
@@ -881,13 +1029,19 @@ constexpr int32_t kWinVariant = 8;
 constexpr int32_t kGemm64Variant = 9;
 constexpr int32_t kGemm128Variant = 10;
 constexpr int32_t kWin16Variant = 11;  // the window kernel for 9 <= M <= 16
+// the window kernels compiled for stacks with block scales
+constexpr int32_t kWinBlkVariant = 12;
+constexpr int32_t kWin16BlkVariant = 13;
 
 bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy) {
   // weight row offsets and output byte offsets are 32-bit in that kernel
   return N * ld < (1ll << 32) && M * ldy * 4 < (1ll << 32);
 }
 
-bool mfma_is_window(int32_t variant) { return variant == kWinVariant || variant == kWin16Variant; }
+bool mfma_is_window(int32_t variant) {
+  return variant == kWinVariant || variant == kWin16Variant || variant == kWinBlkVariant ||
+         variant == kWin16BlkVariant;
+}
 
 // (the 16-token window kernel never splits: stacks small enough to want it
 // take the prefill GEMM at 9..16 tokens)
@@ -909,16 +1063,18 @@ hipError_t launch_split_finish(const void* ws, const LaunchShape& shp, hipStream
 
 int mfma_window_k() { return kWinK; }
 
+int mfma_step_k() { return 8 * 64; }
+
 int32_t mfma_gemm_variant(int32_t M) {
   return gemm_tile_tokens(M) == 128 ? kGemm128Variant : kGemm64Variant;
 }
 
 bool mfma_is_lockstep(int32_t variant) { return variant >= 0 && variant < kWinVariant; }
 
-int32_t mfma_stack_variant(int32_t M, bool ragged, bool big) {
+int32_t mfma_stack_variant(int32_t M, bool ragged, bool big, bool blocked) {
   if (M > 16) return mfma_gemm_variant(M);
-  if (M <= kWinTokens && !ragged && !big) return kWinVariant;
-  if (M <= 16 && !ragged && !big) return kWin16Variant;
+  if (M <= kWinTokens && !ragged && !big) return blocked ? kWinBlkVariant : kWinVariant;
+  if (M <= 16 && !ragged && !big) return blocked ? kWin16BlkVariant : kWin16Variant;
   return (ragged ? 2 : 0) | (M > 8 ? 4 : 0);
 }
 
@@ -931,8 +1087,8 @@ int32_t mfma_token_tiles(int32_t variant, int32_t M) {
 bool mfma_per_workgroup(int32_t) { return true; }
 
 int mfma_unit_rows(int32_t variant) {
-  if (variant == kWinVariant) return kWinRows;
-  if (variant == kWin16Variant) return WinGeo<16>::ROWS;
+  if (variant == kWinVariant || variant == kWinBlkVariant) return kWinRows;
+  if (variant == kWin16Variant || variant == kWin16BlkVariant) return WinGeo<16>::ROWS;
   if (variant == kGemm64Variant || variant == kGemm128Variant)
     return gemm_unit_rows(variant == kGemm128Variant ? 128 : 64);
   return kWgRows;
@@ -943,7 +1099,13 @@ int mfma_unit_restages(int32_t variant, int64_t K) {
 }
 
 int mfma_held_units(int32_t variant) {
-  return variant == kWinVariant ? kOutUnits : variant == kWin16Variant ? kOut16Units : 0;
+  switch (variant) {
+    case kWinVariant: return kOutUnits;
+    case kWin16Variant: return kOut16Units;
+    case kWinBlkVariant: return kOutUnitsBlk;
+    case kWin16BlkVariant: return kOut16UnitsBlk;
+    default: return 0;
+  }
 }
 
 bool mfma_window_major(int32_t variant, int64_t K, bool y_only) {
@@ -959,12 +1121,14 @@ static hipError_t with_mfma_stack_kernel(int32_t variant, F&& f) {
     case 6: return f(mfma_wg_stack_kernel<16, true>);
     case kWinVariant: return f(mfma_win_stack_kernel<false>);
     case kWin16Variant: return f(mfma_win16_stack_kernel<false>);
+    case kWinBlkVariant: return f(mfma_win_stack_kernel<false, true>);
+    case kWin16BlkVariant: return f(mfma_win16_stack_kernel<false, true>);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
-  int32_t v = mfma_stack_variant(a.M, (a.K & 63) != 0, !mfma_win_offsets_fit(a.N, a.ld, a.M, a.ldy));
+  int32_t v = mfma_stack_variant(a.M, (a.K & 63) != 0, !mfma_win_offsets_fit(a.N, a.ld, a.M, a.ldy), false);
   if (v == kGemm64Variant || v == kGemm128Variant) return launch_gemm_linear(a, s);
   if (v == kWin16Variant) v = 4;  // one linear at 9..16 tokens: the lockstep kernel
   const int64_t units = (a.N + mfma_unit_rows(v) - 1) / mfma_unit_rows(v);
@@ -987,9 +1151,9 @@ hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape&
   if (variant == kGemm64Variant || variant == kGemm128Variant)
     return launch_gemm_stack(variant == kGemm128Variant ? 128 : 64, ws, shp, s);
   const StackHeader* h = static_cast<const StackHeader*>(ws);
-  const dim3 grid(shp.grid), block(variant == kWinVariant     ? kWinBlock
-                                    : variant == kWin16Variant ? WinGeo<16>::BLOCK
-                                                               : shp.block);
+  const dim3 grid(shp.grid), block(variant == kWinVariant || variant == kWinBlkVariant       ? kWinBlock
+                                    : variant == kWin16Variant || variant == kWin16BlkVariant ? WinGeo<16>::BLOCK
+                                                                                            : shp.block);
   const bool split = variant == kWinVariant && shp.splits > 0;
   if (split) {
     const hipError_t e = launch_split_clear(ws, shp, s);
@@ -1013,7 +1177,9 @@ int mfma_stack_blocks_per_cu(int32_t variant) {
   if (variant == kGemm64Variant || variant == kGemm128Variant)
     return gemm_stack_blocks_per_cu(variant == kGemm128Variant ? 128 : 64);
   int n = 0;
-  const int block = variant == kWinVariant ? kWinBlock : variant == kWin16Variant ? WinGeo<16>::BLOCK : kBlock;
+  const int block = variant == kWinVariant || variant == kWinBlkVariant       ? kWinBlock
+                    : variant == kWin16Variant || variant == kWin16BlkVariant ? WinGeo<16>::BLOCK
+                                                                            : kBlock;
   const hipError_t e = with_mfma_stack_kernel(variant, [&](auto kern) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, block, 0);
   });

@@ -218,6 +218,163 @@ __device__ __forceinline__ void valu_range_reg(const LinearArgs& a, int row_lo, 
 }
 
 // ---------------------------------------------------------------------------
+// Block-wise scales along K, one token (article "Neutrino-1: quantization is
+// a training decision, not a deployment one", "What's actually ternary": a
+// scale per fixed-size block of the input dimension).  Blocks of
+// B = 64 * 2^blg columns; lane (sub, r) holds chunk r + LPR t of its rows,
+// so a block is an aligned group of G = 2^blg lanes of one slice t (G <= LPR).
+// The group sums its lanes' exact sum(c * qb) into S_b and forms
+//     acc_b = S_b - QB_b - (z + 128) * rowsum_b        (exact, wrapping int32)
+// (QB_b: the block's biased activations); the first lane of the group puts
+// s_b * (float)acc_b (one rounding) into the wave's LDS row, and lane j then
+// adds row j's products in block order b = 0, 1, ... (one rounding each,
+// from +0) and multiplies by s_act: the order of the definition, so y has
+// the bits of its left-to-right evaluation.  acc, when asked for, is
+// sum_b acc_b.
+constexpr int kBlkLdsWave = 8192;  // LDS bytes per wave for the row products
+
+// sum over aligned groups of 2^lg lanes (lg <= 6), in every lane
+__device__ __forceinline__ uint32_t group_sum_lg(uint32_t x, int lg) {
+  if (lg >= 1) x = pair_sum<1>(x);
+  if (lg >= 2) x = pair_sum<2>(x);
+  if (lg >= 3) x = pair_sum<4>(x);
+  if (lg >= 4) x = pair_sum<8>(x);
+  if (lg >= 5) x = pair_sum<16>(x);
+  if (lg >= 6) x = pair_sum<32>(x);
+  return x;
+}
+
+template <int LPR, int CPL, int U>
+__device__ __forceinline__ void valu_range_blk(const LinearArgs& a, int row_lo, int row_hi, int unit0,
+                                               int ustride, int lane, float* prow, int pitch) {
+  constexpr int RPW = 64 / LPR;
+  constexpr int UNIT = U * RPW;
+  const int sub = lane / LPR, r = lane % LPR;
+  const int nch = a.nch, lg = a.blg, nb = a.nb;
+  int32_t* arow = reinterpret_cast<int32_t*>(prow + UNIT * pitch);  // block accs, when acc is asked for
+
+  // activations in registers (as the per-row path), and per slice the
+  // block's biased activation sum
+  uint32_t qc[CPL][16];
+  uint32_t qbb[CPL];
+#pragma unroll
+  for (int t = 0; t < CPL; ++t) {
+    const int ch = r + LPR * t;
+    if (ch < nch) {
+      load_q_chunk<false>(a.q, a.K, ch, qc[t]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qc[t][i] = 0;
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s = udot4(qc[t][i], kOnes, s);
+    qbb[t] = group_sum_lg(s, lg);
+  }
+  const float sa = load_g(a.s_act);
+  const uint32_t zb = (uint32_t)(load_g(a.z) + 128);
+  const bool first = (r & ((1 << lg) - 1)) == 0;
+
+  // one unit's loads: weight chunks, and the scale and row sum of the block
+  // of each (row, slice), through range-checked buffer loads over the
+  // unit's rows (rows past row_hi read as zero and are never stored; a
+  // unit with live == false reads nothing)
+  struct Unit {
+    u32x4 w[U][CPL];
+    int32_t rs[U][CPL];
+    float sb[U][CPL];
+  };
+  uint32_t woff[U][CPL], boff[U][CPL];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int t = 0; t < CPL; ++t) {
+      const int ch = r + LPR * t;
+      woff[u][t] = (uint32_t)(u * RPW + sub) * (uint32_t)a.ld + 16u * (uint32_t)min(ch, nch - 1);
+      boff[u][t] = ((uint32_t)(u * RPW + sub) * (uint32_t)nb + (uint32_t)min(ch >> lg, nb - 1)) * 4u;
+    }
+  auto issue = [&](int base, bool live, Unit& b) {
+    const uint32_t n = live ? (uint32_t)min(UNIT, row_hi - base) : 0u;
+    const auto rw = buffer_rsrc(const_cast<uint8_t*>(a.packed) + (int64_t)base * a.ld, n * (uint32_t)a.ld);
+    const auto rr = buffer_rsrc(const_cast<int32_t*>(a.rowsum_b) + (int64_t)base * nb, n * (uint32_t)nb * 4u);
+    const auto rsb = buffer_rsrc(const_cast<float*>(a.s_b) + (int64_t)base * nb, n * (uint32_t)nb * 4u);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < CPL; ++t) {
+        b.w[u][t] = buffer_load_weights16(rw, woff[u][t]);
+        b.rs[u][t] = (int32_t)buffer_load_u32(rr, boff[u][t]);
+        b.sb[u][t] = __uint_as_float(buffer_load_u32(rsb, boff[u][t]));
+      }
+  };
+  auto finish = [&](const Unit& c, int base) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int t = 0; t < CPL; ++t) {
+        uint32_t p[4] = {0, 0, 0, 0};
+        dot_chunk(c.w[u][t], qc[t], p);
+        const uint32_t sbk = group_sum_lg(combine_exact(p), lg);
+        const int32_t accb = (int32_t)(sbk - qbb[t] - zb * (uint32_t)c.rs[u][t]);
+        const int ch = r + LPR * t;
+        if (first && ch < nch) {
+          const int o = (u * RPW + sub) * pitch + (ch >> lg);
+          prow[o] = __fmul_rn(c.sb[u][t], (float)accb);
+          if (a.acc) arow[o] = accb;
+        }
+      }
+    }
+    wait_lds();  // the wave's products are in LDS (its own accesses complete in order)
+    // lane j < UNIT: row j of the unit, its blocks in order
+    const int j = lane;
+    const int row = base + j;
+    float tot = 0.0f;
+    int32_t isum = 0;
+    if (j < UNIT && row < row_hi) {
+      const float* pr = prow + j * pitch;
+      int b = 0;
+      for (; b + 4 <= nb; b += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(pr + b);
+        tot = __fadd_rn(tot, v.x);
+        tot = __fadd_rn(tot, v.y);
+        tot = __fadd_rn(tot, v.z);
+        tot = __fadd_rn(tot, v.w);
+      }
+      for (; b < nb; ++b) tot = __fadd_rn(tot, pr[b]);
+      if (a.acc) {
+        const int32_t* ar = arow + j * pitch;
+        for (int k = 0; k < nb; ++k) isum += ar[k];
+      }
+    }
+    const uint32_t rows = (uint32_t)min(UNIT, row_hi - base) * 4u;
+    const uint32_t off = j < UNIT ? 4u * (uint32_t)j : kDropOffset;
+    buffer_store_u32(__float_as_uint(__fmul_rn(tot, sa)), buffer_rsrc(a.y + base, rows), off);
+    buffer_store_u32((uint32_t)isum, buffer_rsrc(a.acc ? a.acc + base : nullptr, a.acc ? rows : 0u), off);
+    wait_lds();  // every lane has read its row before the next unit's products go in
+  };
+  const int step = ustride * UNIT;
+  if ((int64_t)row_lo + (int64_t)unit0 * UNIT >= row_hi) return;
+  int base = row_lo + unit0 * UNIT;
+  Unit ua, ub;
+  issue(base, true, ua);
+#pragma unroll 1
+  for (;;) {
+    bool more = (int64_t)base + step < row_hi;
+    issue(more ? base + step : base, more, ub);
+    __builtin_amdgcn_sched_barrier(0);  // the next unit's loads go out first
+    finish(ua, base);
+    if (!more) break;
+    base += step;
+    more = (int64_t)base + step < row_hi;
+    issue(more ? base + step : base, more, ua);
+    __builtin_amdgcn_sched_barrier(0);
+    finish(ub, base);
+    if (!more) break;
+    base += step;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Any K, MT tokens (rows of q streamed through registers one 64-weight chunk
 // at a time).  One row per 64 lanes, U rows per unit.
 template <int U, int MT>
@@ -314,6 +471,50 @@ __device__ __forceinline__ void run_reg(const LinearArgs& a, int lo, int hi, int
   valu_range_reg<C::LPR, C::CPL, C::U, RAGGED>(a, lo, hi, u0, us, lane);
 }
 
+// Units of the block-scaled path: fewer rows than the per-row path (each
+// (row, slice) also loads its block's scale and row sum).
+template <int V> struct BlkU;
+template <> struct BlkU<V8x1>  { static constexpr int U = 2; };
+template <> struct BlkU<V16x1> { static constexpr int U = 2; };
+template <> struct BlkU<V32x1> { static constexpr int U = 2; };
+template <> struct BlkU<V16x3> { static constexpr int U = 1; };
+template <> struct BlkU<V64x1> { static constexpr int U = 4; };
+template <> struct BlkU<V64x2> { static constexpr int U = 2; };
+template <> struct BlkU<V64x3> { static constexpr int U = 2; };
+template <> struct BlkU<V64x4> { static constexpr int U = 1; };
+
+template <int V>
+__device__ __forceinline__ void run_blk(const LinearArgs& a, int lo, int hi, int u0, int us, int lane,
+                                        float* prow) {
+  using C = ValuCfg<V>;
+  // a row pitch of the products that is a multiple of 4 floats and 4 more
+  // than needed, so that lanes reading rows side by side use other banks
+  const int pitch = (a.nb + 3) / 4 * 4 + 4;
+  valu_range_blk<C::LPR, C::CPL, BlkU<V>::U>(a, lo, hi, u0, us, lane, prow, pitch);
+}
+
+// A block-scaled linear of the M = 1 stack (register variants in VSET; the
+// host picks one whose lanes per row hold whole blocks).
+template <uint32_t VSET>
+__device__ __forceinline__ void valu_m1_segment_blk(const LinearArgs& a, int lo, int hi, int lane, float* prow) {
+#define TERN_BLK_CASE(V)                                                 \
+  case V:                                                                \
+    if constexpr ((VSET >> V) & 1u) run_blk<V>(a, lo, hi, 0, 1, lane, prow); \
+    break;
+  switch (a.variant) {
+    TERN_BLK_CASE(V8x1)
+    TERN_BLK_CASE(V16x1)
+    TERN_BLK_CASE(V32x1)
+    TERN_BLK_CASE(V16x3)
+    TERN_BLK_CASE(V64x1)
+    TERN_BLK_CASE(V64x2)
+    TERN_BLK_CASE(V64x3)
+    TERN_BLK_CASE(V64x4)
+    default: break;
+  }
+#undef TERN_BLK_CASE
+}
+
 // M = 1, one segment of a prepared stack.  VSET is the set of variants the
 // kernel is compiled for (bit V for register variant V, bit VGEN for the
 // streaming one, which also takes K not a multiple of 64): each extra
@@ -359,6 +560,16 @@ __device__ __forceinline__ int xcd_logical_block() {
   return (n % 8 == 0) ? (b % 8) * (n / 8) + b / 8 : b;
 }
 
+// Variant sets the persistent M = 1 kernel is compiled for.
+constexpr uint32_t bit(int v) { return 1u << v; }
+constexpr uint32_t kSet8B = bit(V64x1) | bit(V64x3);
+constexpr uint32_t kSet06B = bit(V16x1) | bit(V32x1) | bit(V16x3);
+constexpr uint32_t kSetReg = bit(V8x1) | bit(V16x1) | bit(V32x1) | bit(V16x3) | bit(V64x1) |
+                             bit(V64x2) | bit(V64x3) | bit(V64x4);
+constexpr uint32_t kSetAll = kSetReg | bit(VGEN);
+constexpr uint32_t kSets[] = {kSet8B, kSet06B, kSetReg, kSetAll};
+constexpr uint32_t kNone = 0;
+
 }  // namespace
 
 template <int V, bool RAGGED>
@@ -399,7 +610,64 @@ __global__ __launch_bounds__(kBlock) void valu_stack_kernel(const StackHeader* _
   }
 }
 
+// M = 1 stacks holding block-scaled linears: those take the block path,
+// the others the per-row path (both compiled for the variant set VSET).
+template <uint32_t VSET>
+__global__ __launch_bounds__(kBlock) void valu_stack_blk_kernel(const StackHeader* __restrict__ h) {
+  __shared__ __attribute__((aligned(16))) float prods[kWavesPerBlock][kBlkLdsWave / 4];
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id_uniform();
+  const int worker = xcd_logical_block() * kWavesPerBlock + w;
+  if (worker >= h->workers) return;
+  const LinearArgs* lin = reinterpret_cast<const LinearArgs*>(
+      reinterpret_cast<const char*>(h) + h->off_lin);
+  const int32_t* seg_start = reinterpret_cast<const int32_t*>(
+      reinterpret_cast<const char*>(h) + h->off_seg_start);
+  const Segment* seg = reinterpret_cast<const Segment*>(
+      reinterpret_cast<const char*>(h) + h->off_seg);
+  const int s1 = seg_start[worker + 1];
+  for (int s = seg_start[worker]; s < s1; ++s) {
+    const Segment sg = seg[s];
+    const LinearArgs a = lin[sg.lin];
+    if (a.s_b)
+      valu_m1_segment_blk<VSET>(a, sg.row_begin, sg.row_end, lane, prods[w]);
+    else
+      valu_m1_segment<VSET>(a, sg.row_begin, sg.row_end, lane);
+  }
+}
+
 // ------------------------------------------------------------- launchers --
+
+// The register variant of a block-scaled linear: the per-row one when its
+// lanes per row hold whole blocks (B <= 64 * LPR), else the 64-lane one for
+// K; -1 when no register variant takes K (K > 16,384 or not a multiple of 64).
+int32_t valu_blocked_variant(int64_t K, int64_t B) {
+  if (K % 64 != 0 || K > 16384) return -1;
+  const int32_t v = valu_variant_for(K);
+  int lpr = 64;
+  switch (v) {
+    case V8x1: lpr = ValuCfg<V8x1>::LPR; break;
+    case V16x1: lpr = ValuCfg<V16x1>::LPR; break;
+    case V32x1: lpr = ValuCfg<V32x1>::LPR; break;
+    case V16x3: lpr = ValuCfg<V16x3>::LPR; break;
+    default: break;
+  }
+  if (B <= 64 * lpr) return v;
+  return K <= 4096 ? V64x1 : K <= 8192 ? V64x2 : K <= 12288 ? V64x3 : V64x4;
+}
+
+int valu_blocked_unit_rows(int32_t variant) {
+  switch (variant) {
+    case V8x1: return BlkU<V8x1>::U * 64 / ValuCfg<V8x1>::LPR;
+    case V16x1: return BlkU<V16x1>::U * 64 / ValuCfg<V16x1>::LPR;
+    case V32x1: return BlkU<V32x1>::U * 64 / ValuCfg<V32x1>::LPR;
+    case V16x3: return BlkU<V16x3>::U * 64 / ValuCfg<V16x3>::LPR;
+    case V64x1: return BlkU<V64x1>::U;
+    case V64x2: return BlkU<V64x2>::U;
+    case V64x3: return BlkU<V64x3>::U;
+    default: return BlkU<V64x4>::U;
+  }
+}
 
 int32_t valu_variant_for(int64_t K) {
   if (K <= 512) return V8x1;
@@ -473,21 +741,13 @@ hipError_t launch_valu_linear(const LinearArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Variant sets the persistent M = 1 kernel is compiled for.
-constexpr uint32_t bit(int v) { return 1u << v; }
-constexpr uint32_t kSet8B = bit(V64x1) | bit(V64x3);
-constexpr uint32_t kSet06B = bit(V16x1) | bit(V32x1) | bit(V16x3);
-constexpr uint32_t kSetReg = bit(V8x1) | bit(V16x1) | bit(V32x1) | bit(V16x3) | bit(V64x1) |
-                             bit(V64x2) | bit(V64x3) | bit(V64x4);
-constexpr uint32_t kSetAll = kSetReg | bit(VGEN);
-constexpr uint32_t kSets[] = {kSet8B, kSet06B, kSetReg, kSetAll};
-constexpr uint32_t kNone = 0;
 
-int32_t valu_stack_kernel_for(int32_t M, uint32_t used_variants) {
+int32_t valu_stack_kernel_for(int32_t M, uint32_t used_variants, bool blocked) {
   if (M == 1) {
+    const int32_t k0 = blocked ? SK_VALU_M1_BLK : SK_VALU_M1;
     for (int i = 0; i < 4; ++i)
-      if ((used_variants & ~kSets[i]) == 0) return SK_VALU_M1 + i;
-    return SK_VALU_M1 + 3;
+      if ((used_variants & ~kSets[i]) == 0) return k0 + i;
+    return k0 + 3;
   }
   if (M == 2) return SK_VALU_M2;
   if (M <= 4) return SK_VALU_M4;
@@ -504,6 +764,10 @@ static hipError_t with_valu_stack_kernel(int32_t kernel, F&& f) {
     case SK_VALU_M2: return f(valu_stack_kernel<2, kNone>);
     case SK_VALU_M4: return f(valu_stack_kernel<4, kNone>);
     case SK_VALU_M8: return f(valu_stack_kernel<8, kNone>);
+    case SK_VALU_M1_BLK + 0: return f(valu_stack_blk_kernel<kSets[0]>);
+    case SK_VALU_M1_BLK + 1: return f(valu_stack_blk_kernel<kSets[1]>);
+    case SK_VALU_M1_BLK + 2: return f(valu_stack_blk_kernel<kSets[2]>);
+    case SK_VALU_M1_BLK + 3: return f(valu_stack_blk_kernel<kSets[3]>);
     default: return hipErrorInvalidValue;
   }
 }

@@ -27,6 +27,10 @@ class PackedLinear:
     packed: torch.Tensor
     rowsum: torch.Tensor
     s_row: torch.Tensor
+    # block-wise scales (block > 0): N x ceil(K / block) scales and row sums
+    block: int = 0
+    s_block: torch.Tensor | None = None
+    rowsum_block: torch.Tensor | None = None
     # host copies of a few rows, for sampled checks (row index -> weights)
     sample_rows: np.ndarray | None = None
     sample_w: np.ndarray | None = None
@@ -41,8 +45,11 @@ class DeviceStack:
     """Packed weights and metadata of every linear of a synthetic stack."""
 
     def __init__(self, model: str = "8b", layers: int | None = None, seed: int = 0,
-                 threads: int = 8, device: str = "cuda:0", sample_rows: int = 0):
-        self.model, self.seed, self.device = model, seed, device
+                 threads: int = 8, device: str = "cuda:0", sample_rows: int = 0, block: int = 0):
+        """block > 0: every linear also gets block-wise scales along K (one per
+        `block` columns, ``synth.make_block_scales``) and their block row
+        sums (``tern_block_rowsum`` on the packed weights)."""
+        self.model, self.seed, self.device, self.block = model, seed, device, block
         self.specs = synth.stack_specs(model, layers)
         self.linears: list[PackedLinear] = []
         bad_total = torch.zeros(1, dtype=torch.int32, device=device)
@@ -70,6 +77,12 @@ class DeviceStack:
                 del wd
                 pl = PackedLinear(layer, idx, "L%d.%s" % (layer, name), N, K, packed, rowsum,
                                   torch.from_numpy(s_row).to(device))
+                if block:
+                    nb = -(-K // block)
+                    pl.block = block
+                    pl.s_block = torch.from_numpy(synth.make_block_scales(seed, layer, idx, N, K, block)).to(device)
+                    pl.rowsum_block = torch.empty((N, nb), dtype=torch.int32, device=device)
+                    tern.tern_block_rowsum(packed, N, K, block, pl.rowsum_block)
                 if sample_rows:
                     rows = np.unique(np.concatenate([
                         [0, N - 1], rng.choice(N, min(N, sample_rows), replace=False)]))
@@ -135,7 +148,7 @@ class StackBinding:
             if pl.sample_rows is not None:
                 self.host_act.append((q, s_act, z))
             descs.append(tern.make_desc(pl.packed, pl.s_row, pl.rowsum, pl.N, pl.K, qd, ldq, sd,
-                                        zd, yd, pl.N, ad))
+                                        zd, yd, pl.N, ad, pl.block, pl.s_block, pl.rowsum_block))
         self.descs = descs
         L = len(descs)
         self.workspace = torch.empty(tern.tern_linear_stack_workspace_bytes(L, M),

@@ -32,7 +32,9 @@ and its M tokens of activations from ``default_rng([seed, layer, idx, M])``:
   3. q: ``integers(-128, 127, (M, K), int8, endpoint=True)``;
   4. per-token parameters: for M = 1, s_act = 0.02 and z = 3; for M > 1,
      s_act = ``uniform(0.01, 0.03, M)`` (float32) then z = ``integers(-8, 9, M)``.
-The same weights therefore serve every M.
+The same weights therefore serve every M.  Block-wise scales (one per block
+of B columns) come from ``default_rng([seed, layer, idx, 2**20, B])``:
+``uniform(0.01, 0.1, (N, ceil(K / B)))`` rounded to float32.
 """
 from __future__ import annotations
 
@@ -159,6 +161,12 @@ def make_linear(seed, layer: int, idx: int, N: int, K: int, p_zero: float, M: in
     w, s_row = make_weights(seed, layer, idx, N, K, p_zero)
     q, s_act, z = make_activations(seed, layer, idx, K, M)
     return Linear(name, w, s_row, q, s_act, z)
+
+
+def make_block_scales(seed, layer: int, idx: int, N: int, K: int, B: int) -> np.ndarray:
+    """float32 (N, ceil(K / B)) block scales of one linear."""
+    rng = np.random.default_rng([seed, layer, idx, 1 << 20, B])
+    return rng.uniform(0.01, 0.1, (N, -(-K // B))).astype(np.float32)
 
 
 def single_gemv_case() -> Linear:

@@ -58,6 +58,7 @@ class tern_linear_desc(ctypes.Structure):
         ("q", ctypes.c_void_p), ("ldq", ctypes.c_int64),
         ("s_act", ctypes.c_void_p), ("z", ctypes.c_void_p),
         ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64), ("acc", ctypes.c_void_p),
+        ("block", ctypes.c_int64), ("s_block", ctypes.c_void_p), ("rowsum_block", ctypes.c_void_p),
     ]
 
 
@@ -231,9 +232,18 @@ def tern_linear_stack_workspace_bytes(L: int, M: int) -> int:
     return int(_lib().tern_linear_stack_workspace_bytes(int(L), int(M)))
 
 
-def make_desc(packed, s_row, rowsum, N, K, q, ldq, s_act, z, y, ldy, acc=None) -> tern_linear_desc:
+def make_desc(packed, s_row, rowsum, N, K, q, ldq, s_act, z, y, ldy, acc=None, block=0, s_block=None,
+              rowsum_block=None) -> tern_linear_desc:
+    """One linear of a stack.  With block > 0 (block-wise scales along K),
+    s_block / rowsum_block are N x ceil(K / block) and s_row / rowsum may be
+    None."""
     d = tern_linear_desc()
-    d.packed, d.s_row, d.rowsum = packed.data_ptr(), s_row.data_ptr(), rowsum.data_ptr()
+    d.packed = packed.data_ptr()
+    d.s_row = None if s_row is None else s_row.data_ptr()
+    d.rowsum = None if rowsum is None else rowsum.data_ptr()
+    d.block = int(block)
+    d.s_block = None if s_block is None else s_block.data_ptr()
+    d.rowsum_block = None if rowsum_block is None else rowsum_block.data_ptr()
     d.N, d.K = int(N), int(K)
     d.q, d.ldq = q.data_ptr(), int(ldq)
     d.s_act, d.z = s_act.data_ptr(), z.data_ptr()
