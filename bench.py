@@ -24,8 +24,11 @@ M = 16, 64, 512 on four layers; the int8 output head (151,936 x 4,096) at
 M = 1 and 8; block-wise scales on the 8B's stacked gate projections; the
 same gate projections in 2-bit and in 1.6-bit rows; the weight quantiser;
 one decode step (quantiser, stack, head) eager and replayed from a HIP
-graph; and the activation quantiser.  Most lines carry the oracle timed on
-a bounded sample of the same workload.
+graph, with the quantiser fused into the stack launch (two launches) and as
+a launch of its own (three); the whole 8B stack at M = 16; q/k/v and gate/up
+sharing inputs; block-wise scales inside the stack; and the activation
+quantiser.  Most lines carry the oracle timed on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -522,7 +525,11 @@ def suite(args):
     torch.cuda.empty_cache()
 
     # --- one decode step's linears, eager and replayed from a HIP graph:
-    # quantise the token (fp32 4,096), the 252-linear 8B stack, the int8 head
+    # the token's fp32 hidden state quantised, the 252-linear 8B stack (layer
+    # 0's q/k/v read that token; each layer's q/k/v and gate/up share one
+    # input), the int8 head reading the same quantised token.  Fused: the
+    # stack launch quantises its fp32 input itself (two launches); separate:
+    # the quantiser is a launch of its own (three).
     st = DeviceStack("8b", seed=5, threads=16)
     Wh, srh_ = synth.make_head(0)
     Nh, Kh = Wh.shape
@@ -531,28 +538,38 @@ def suite(args):
     rshd = torch.empty(Nh, dtype=torch.int32, device=dev)
     tern.tern_head_rowsum(Whd, Nh, Kh, Kh, rshd)
     for M in (1, 8):
-        b = st.bind(M)
-        ldq = b.q[0].shape[1]
-        xd = torch.from_numpy(np.random.default_rng([M, 6]).normal(0, 1, (M, Kh)).astype(np.float32)).to(dev)
-        logits = torch.empty((M, Nh), dtype=torch.float32, device=dev)
+        rec = {"suite": "decode_step", "workload": "one decode step's linears at M = %d: quantise the fp32 "
+               "token(s), the 252-linear 8B stack (one launch; q/k/v and gate/up share inputs), the int8 head "
+               "151,936 x 4,096 reading the quantised token(s)" % M, "M": M}
+        head_bytes = Nh * Kh + 8 * Nh + M * Kh + 8 * M + 4 * M * Nh
+        for mode in ("fused", "separate"):
+            b = st.bind(M, share_inputs=True, quantise="first" if mode == "fused" else "none")
+            ldq = b.q[0].shape[1]
+            xd = b.x[0] if mode == "fused" else torch.from_numpy(
+                synth.make_hidden(5, 0, 0, Kh, M)).to(dev)
+            logits = torch.empty((M, Nh), dtype=torch.float32, device=dev)
 
-        def dstep(i=0, b=b, xd=xd, logits=logits, M=M, ldq=ldq):
-            tern.tern_quantize_act(xd, M, Kh, Kh, b.q[0], ldq, b.s_act[0], b.z[0])
-            b.run()
-            tern.tern_head_gemv(Whd, srhd, rshd, Nh, Kh, Kh, M, b.q[0], ldq, b.s_act[0], b.z[0], logits, Nh)
-        eager = _event_times(dstep, 20)
-        g = torch.cuda.CUDAGraph()
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            dstep()
-        torch.cuda.synchronize()
-        replay = _event_times(lambda i: g.replay(), 20)
-        db = b.bytes + Nh * Kh + 8 * Nh + M * Kh + 8 * M + 4 * M * Nh + 5 * M * Kh
-        emit({"suite": "decode_step", "workload": "one decode step's linears at M = %d: quantise the "
-              "token(s), the 252-linear 8B stack (one launch), the int8 head 151,936 x 4,096" % M,
-              "M": M, "eager": _stats(eager, db), "graph_replay": _stats(replay, db),
-              "note": "three kernel launches; the stack's linears take independent synthetic activations"})
-        del b, g, xd, logits
+            def dstep(i=0, b=b, xd=xd, logits=logits, M=M, ldq=ldq, mode=mode):
+                if mode == "separate":
+                    tern.tern_quantize_act(xd, M, Kh, Kh, b.q[0], ldq, b.s_act[0], b.z[0])
+                b.run()
+                tern.tern_head_gemv(Whd, srhd, rshd, Nh, Kh, Kh, M, b.q[0], ldq, b.s_act[0], b.z[0], logits, Nh)
+            eager = _event_times(dstep, 20)
+            g = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                dstep()
+            torch.cuda.synchronize()
+            replay = _event_times(lambda i: g.replay(), 20)
+            # (fused: the stack's bytes include its input's 5*M*K + 8*M)
+            db = b.bytes + head_bytes + (5 * M * Kh + 8 * M if mode == "separate" else 0)
+            rec[mode] = {"launches": 2 if mode == "fused" else 3, "eager": _stats(eager, db),
+                         "graph_replay": _stats(replay, db)}
+            if mode == "fused":
+                tern.tern_linear_stack_status(b.plan)
+            del b, g, xd, logits
+        rec["note"] = "the other linears take independent synthetic activations (one per shared group)"
+        emit(rec)
     # --- the same 252-linear stack at 16 tokens (a longer verify pass), one launch
     b16 = st.bind(16)
     us = _event_times(lambda i: b16.run(), 20)

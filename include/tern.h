@@ -78,7 +78,8 @@ typedef enum {
   TERN_ERR_RANGE = 3,       /* K > TERN_MAX_K, or a size beyond int32 rows */
   TERN_ERR_UNSUPPORTED = 4, /* a path hint the shape cannot take */
   TERN_ERR_WORKSPACE = 5,   /* workspace missing, too small or misaligned */
-  TERN_ERR_HIP = 6          /* a HIP runtime call failed */
+  TERN_ERR_HIP = 6,         /* a HIP runtime call failed */
+  TERN_ERR_TIMEOUT = 7      /* see tern_linear_stack_status */
 } tern_status;
 
 /* Path hints for tern_gemm_smallM and tern_linear_stack_prepare. */
@@ -186,6 +187,18 @@ typedef struct {
   int64_t block;
   const float* s_block;
   const int32_t* rowsum_block;
+  /* fp32 input quantised by the launch itself (NULL: q, s_act and z are
+   * the caller's, ready before the launch).  x holds M rows of K finite
+   * floats (row stride ldx >= K, 4-byte aligned); the launch writes q (row
+   * stride ldq; columns < K), s_act and z from it exactly as
+   * tern_quantize_act does, before any linear of the launch reads them.
+   * Each distinct q buffer is quantised once: linears naming the same q
+   * must name the same x, ldx, K, ldq, s_act and z (and every linear
+   * naming such a q reads the quantised values, with or without x);
+   * otherwise TERN_ERR_INVALID_ARG.  q, s_act and z are outputs of the
+   * launch, complete when it is; x must not overlap them. */
+  const float* x;
+  int64_t ldx;
 } tern_linear_desc;
 
 /* Host-side handle filled by tern_linear_stack_prepare (plain data; copy it
@@ -247,8 +260,25 @@ int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t 
                               tern_stack_plan* plan, hipStream_t stream);
 
 /* tern_linear_stack -- one launch over the prepared stack (three when
- * plan->splits > 0: clear, main, finish). */
+ * plan->splits > 0: clear, main, finish).  Launches on one plan (or on
+ * plans sharing a workspace) must not overlap: enqueue them on one stream,
+ * or order them. */
 int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream);
+
+/*
+ * Fused activation quantisation (descriptors with x): inside the launch,
+ * before the linears, the launch's workgroups claim token rows of the
+ * distinct inputs from a counter in the workspace, quantise them and flag
+ * each one finished; a wave about to read a quantised input waits for its
+ * rows' flags.  Every row is claimed by a workgroup already running, so the
+ * waits end; they are bounded all the same (about a second), and a wait
+ * that gives up is recorded in the workspace.  plan->bytes adds, per
+ * distinct input, 4*M*K bytes read, M*K + 8*M written.
+ * tern_linear_stack_status -- synchronises `stream` and returns
+ * TERN_ERR_TIMEOUT if any launch of the plan since its prepare gave up such
+ * a wait (its outputs are then not to be used), else TERN_OK.
+ */
+int tern_linear_stack_status(const tern_stack_plan* plan, hipStream_t stream);
 
 /*
  * tern_linear_stack_prepare_static -- tern_linear_stack_prepare for callers

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -73,6 +74,7 @@ LinearArgs make_args(const uint8_t* packed, const float* s_row, const int32_t* r
   a.ldy = (int32_t)(M > 1 ? ldy : 0);
   a.M = (int32_t)M;
   a.variant = valu_variant_for(K);
+  a.qjob = -1;
   return a;
 }
 
@@ -158,18 +160,24 @@ constexpr double kRestageCost = 40000.0;
 constexpr double kWindowMajorGroup = 2.4;
 
 struct Layout {
-  int64_t off_lin, off_seg_start, off_seg, off_split, total;
+  int64_t off_lin, off_seg_start, off_seg, off_split, off_job, off_sync, off_flag, off_part, total;
 };
 
 // nlin LinearArgs entries, `workers` schedule heads, nseg segments, nsplit
-// split linears
-Layout layout_for(int64_t nlin, int64_t workers, int64_t nseg, int64_t nsplit) {
+// split linears, njobs quantisation jobs with nitems rows, npart words of
+// claiming-workgroup bits
+Layout layout_for(int64_t nlin, int64_t workers, int64_t nseg, int64_t nsplit, int64_t njobs,
+                  int64_t nitems, int64_t npart) {
   Layout l;
-  l.off_lin = (int64_t)sizeof(StackHeader);
+  l.off_sync = kStackSyncOffset;
+  l.off_flag = l.off_sync + (int64_t)sizeof(StackSync);
+  l.off_lin = align_up(l.off_flag + nitems * 4, 64);
   l.off_seg_start = align_up(l.off_lin + nlin * (int64_t)sizeof(LinearArgs), 16);
   l.off_seg = align_up(l.off_seg_start + (workers + 1) * 4, 16);
   l.off_split = align_up(l.off_seg + nseg * (int64_t)sizeof(Segment), 16);
-  l.total = l.off_split + nsplit * 4;
+  l.off_job = align_up(l.off_split + nsplit * 4, 64);
+  l.off_part = l.off_job + njobs * (int64_t)sizeof(QuantJob);
+  l.total = l.off_part + npart * 4;
   return l;
 }
 
@@ -188,6 +196,7 @@ const char* tern_status_string(int status) {
     case TERN_ERR_UNSUPPORTED: return "unsupported path for this shape";
     case TERN_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case TERN_ERR_HIP: return "HIP runtime error";
+    case TERN_ERR_TIMEOUT: return "a stack launch gave up waiting for a quantised input";
     default: return "unknown status";
   }
 }
@@ -391,7 +400,10 @@ int64_t tern_linear_stack_workspace_bytes(int64_t L, int64_t M) {
   // every linear may be split into kMaxSplitWindows windows, each with its
   // own LinearArgs entry and segments
   const int64_t nlin = L * (1 + kMaxSplitWindows);
-  return layout_for(nlin, workers, workers + nlin, L).total;
+  // every linear may carry its own fp32 input: L jobs of M rows (at most
+  // kMaxQuantItems rows in all)
+  const int64_t items = M > 0 && L > kMaxQuantItems / M ? kMaxQuantItems : std::min(kMaxQuantItems, L * M);
+  return layout_for(nlin, workers, workers + nlin, L, L, items, workers / 32 + 1).total;
 }
 
 int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
@@ -426,6 +438,58 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
   // every descriptor is checked before anything is written
   int64_t bytes = 0;
   bool any_blocked = false;
+  // fp32 inputs the launch quantises: one job per distinct q buffer, named
+  // by the linears that give x (and read by every linear naming that q)
+  std::vector<QuantJob> jobs;
+  std::vector<int32_t> qjob((size_t)L, -1);
+  std::map<const void*, int32_t> job_of_q;
+  for (int64_t i = 0; i < L; ++i) {
+    const tern_linear_desc& d = descs[i];
+    if (!d.x) continue;
+    // (checked here as well as below: a linear with no rows still has its
+    // input quantised)
+    if (d.K < 1 || d.ldx < d.K || !d.q || !d.s_act || !d.z) return TERN_ERR_INVALID_ARG;
+    if (d.K > TERN_MAX_K || d.ldx > kI32Max || d.ldq > kI32Max) return TERN_ERR_RANGE;
+    if (M > 1 && d.ldq < d.K) return TERN_ERR_INVALID_ARG;
+    if (!aligned(d.x, 4) || !aligned(d.q, 16) || !aligned(d.s_act, 4) || !aligned(d.z, 4) ||
+        (M > 1 && d.ldq % 16 != 0))
+      return TERN_ERR_ALIGNMENT;
+    const int64_t ldq = M > 1 ? d.ldq : d.K;
+    auto it = job_of_q.find(d.q);
+    if (it == job_of_q.end()) {
+      QuantJob j;
+      memset(&j, 0, sizeof(j));
+      j.x = d.x;
+      j.q = const_cast<int8_t*>(d.q);
+      j.s_act = const_cast<float*>(d.s_act);
+      j.z = const_cast<int32_t*>(d.z);
+      j.ldx = d.ldx;
+      j.ldq = ldq;
+      j.K = (int32_t)std::min<int64_t>(d.K, kI32Max);
+      job_of_q[d.q] = (int32_t)jobs.size();
+      jobs.push_back(j);
+      continue;
+    }
+    const QuantJob& j = jobs[(size_t)it->second];
+    if (j.x != d.x || j.ldx != d.ldx || j.K != d.K || j.ldq != ldq || j.s_act != d.s_act || j.z != d.z)
+      return TERN_ERR_INVALID_ARG;
+  }
+  if (!jobs.empty()) {
+    for (int64_t i = 0; i < L; ++i) {
+      const tern_linear_desc& d = descs[i];
+      auto it = job_of_q.find(d.q);
+      if (it == job_of_q.end()) continue;
+      // a linear reading a buffer the launch writes reads all of it, as
+      // written: the same activations, scales and zero points
+      const QuantJob& j = jobs[(size_t)it->second];
+      if (j.K != d.K || j.ldq != (M > 1 ? d.ldq : d.K) || j.s_act != d.s_act || j.z != d.z)
+        return TERN_ERR_INVALID_ARG;
+      qjob[(size_t)i] = it->second;
+    }
+    if (M > 0 && (int64_t)jobs.size() > kMaxQuantItems / M) return TERN_ERR_RANGE;
+    for (const QuantJob& j : jobs) bytes += 5 * M * (int64_t)j.K + 8 * M;  // fp32 in, int8 out, s_act and z
+  }
+  const int64_t nitems = (int64_t)jobs.size() * M;
   for (int64_t i = 0; i < L; ++i) {
     const tern_linear_desc& d = descs[i];
     const bool blk = d.block != 0;
@@ -523,6 +587,7 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
     const tern_linear_desc& d = descs[i];
     LinearArgs& a = lin[(size_t)i];
     a = make_args(d.packed, d.s_row, d.rowsum, d.N, d.K, M, d.q, d.ldq, d.s_act, d.z, d.y, d.ldy, d.acc);
+    a.qjob = qjob[(size_t)i];
     if (d.block != 0 && d.N > 0) {
       a.s_b = d.s_block;
       a.rowsum_b = d.rowsum_block;
@@ -680,7 +745,32 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
   }
   while (wk <= workers) seg_start[(size_t)wk++] = (int32_t)segs.size();
 
-  const Layout lay = layout_for((int64_t)lin.size(), workers, (int64_t)segs.size(), (int64_t)split.size());
+  // Workgroups that claim rows to quantise (launches with jobs): the first
+  // few of the grid (one per row, at least 8: spread over the XCDs, and
+  // dispatched first), and every workgroup whose run reads a quantised input
+  // (its waves wait for that input only after their own claims have run
+  // out).  The others skip the prologue.
+  std::vector<uint32_t> part;
+  int32_t claimers = 0;
+  if (nitems > 0) {
+    part.assign((size_t)(grid + 31) / 32, 0u);
+    auto set = [&](int64_t b) { part[(size_t)(b >> 5)] |= 1u << (b & 31); };
+    const int64_t first = std::min<int64_t>(grid, std::max<int64_t>(8, nitems));
+    for (int64_t b = 0; b < first; ++b) set(b);
+    const int64_t per = grid / 8;  // (the grid is a multiple of 8: XCD-aware numbering)
+    for (int64_t wr = 0; wr < workers; ++wr) {
+      bool reads = false;
+      for (int32_t sx = seg_start[(size_t)wr]; sx < seg_start[(size_t)wr + 1] && !reads; ++sx)
+        reads = lin[(size_t)segs[(size_t)sx].lin].qjob >= 0;
+      if (!reads) continue;
+      // the worker's logical workgroup, and the workgroup index it runs as
+      const int64_t lb = per_wg ? wr : wr / kWavesPerBlock;
+      set((lb % per) * 8 + lb / per);
+    }
+    for (uint32_t wd : part) claimers += __builtin_popcount(wd);
+  }
+  const Layout lay = layout_for((int64_t)lin.size(), workers, (int64_t)segs.size(), (int64_t)split.size(),
+                               (int64_t)jobs.size(), nitems, (int64_t)part.size());
   if (workspace_bytes < lay.total) return static_ws ? TERN_ERR_RANGE : TERN_ERR_WORKSPACE;
   std::vector<char> host((size_t)lay.total, 0);
   StackHeader h;
@@ -697,7 +787,17 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
   h.off_seg_start = lay.off_seg_start;
   h.off_seg = lay.off_seg;
   h.off_split = lay.off_split;
+  h.njobs = (int32_t)jobs.size();
+  h.nitems = (int32_t)nitems;
+  h.off_job = lay.off_job;
+  h.off_sync = lay.off_sync;
+  h.off_flag = lay.off_flag;
+  h.claimers = claimers;
+  h.off_part = lay.off_part;
   memcpy(host.data(), &h, sizeof(h));
+  if (!part.empty()) memcpy(host.data() + lay.off_part, part.data(), part.size() * 4);
+  // (the claim counter, the error word and the flags start at zero)
+  if (!jobs.empty()) memcpy(host.data() + lay.off_job, jobs.data(), jobs.size() * sizeof(QuantJob));
   memcpy(host.data() + lay.off_lin, lin.data(), lin.size() * sizeof(LinearArgs));
   memcpy(host.data() + lay.off_seg_start, seg_start.data(), seg_start.size() * 4);
   if (!segs.empty()) memcpy(host.data() + lay.off_seg, segs.data(), segs.size() * sizeof(Segment));
@@ -777,6 +877,23 @@ int tern_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int blocks_p
   const hipError_t e =
       launch_read_probe(buf, bytes, sink, cus * blocks_per_cu, unroll, nontemporal != 0, stream);
   return e == hipSuccess ? TERN_OK : hip_fail(e);
+}
+
+int tern_linear_stack_status(const tern_stack_plan* plan, hipStream_t stream) {
+  if (!plan) return TERN_ERR_INVALID_ARG;
+  if (plan->L == 0 || plan->M == 0) return TERN_OK;
+  if (!plan->workspace || !aligned(plan->workspace, 256)) return TERN_ERR_WORKSPACE;
+  StackHeader h;
+  hipError_t e = hipMemcpyAsync(&h, plan->workspace, sizeof(h), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e);
+  if (h.magic != kStackMagic) return TERN_ERR_WORKSPACE;
+  StackSync sy;
+  e = hipMemcpyAsync(&sy, static_cast<const char*>(plan->workspace) + h.off_sync, sizeof(sy),
+                     hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return sy.err ? TERN_ERR_TIMEOUT : TERN_OK;
 }
 
 int tern_linear_stack(const tern_stack_plan* plan, hipStream_t stream) {

@@ -37,7 +37,7 @@
 //    never stored.
 #include <algorithm>
 
-#include "tern_device.h"
+#include "tern_prologue.h"
 
 namespace tern {
 
@@ -317,8 +317,11 @@ void gemm_linear_kernel(LinearArgs a) {
 
 template <int BM, bool SPLIT>
 __global__ __launch_bounds__(64 * GemmShape<BM>::WAVES) __attribute__((amdgpu_waves_per_eu(BM == 128 ? 2 : 4)))
-void gemm_stack_kernel(const StackHeader* __restrict__ h) {
+void gemm_stack_kernel(const StackHeader* __restrict__ h,
+                                  StackSync* __restrict__ sy) {
   __shared__ __attribute__((aligned(16))) GemmTiles<BM> L;
+  __shared__ PrologueLds prol;
+  const uint32_t launch1 = stack_prologue(h, sy, prol);
   const int worker = gemm_xcd_block();
   if (worker >= h->workers) return;  // the same for the whole workgroup
   const int lane = threadIdx.x & 63;
@@ -328,6 +331,7 @@ void gemm_stack_kernel(const StackHeader* __restrict__ h) {
   const int32_t* seg_start = reinterpret_cast<const int32_t*>(base + h->off_seg_start);
   const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
   const int s1 = seg_start[worker + 1];
+  wait_segment_inputs(h, sy, lin, seg, seg_start[worker], s1, launch1);
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
@@ -370,7 +374,7 @@ hipError_t launch_gemm_stack(int bm, const void* ws, const LaunchShape& shp, hip
     if (e != hipSuccess) return e;
   }
   const hipError_t e = with_gemm_stack_kernel(bm, split, [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(shp.grid), dim3(gemm_block(bm)), 0, s, h);
+    hipLaunchKernelGGL(kern, dim3(shp.grid), dim3(gemm_block(bm)), 0, s, h, stack_sync(ws));
     return hipGetLastError();
   });
   if (e != hipSuccess || !split) return e;

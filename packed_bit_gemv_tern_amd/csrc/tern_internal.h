@@ -44,7 +44,10 @@ struct alignas(16) LinearArgs {
   const float* s_b;
   const int32_t* rowsum_b;
   int32_t blg, nb;  // log2(block / 64), blocks per row
-  int32_t pad[2];
+  // the launch's quantisation job that writes q, s_act and z (-1: the
+  // caller's activations, ready before the launch)
+  int32_t qjob;
+  int32_t pad;
 };
 static_assert(sizeof(LinearArgs) == 128, "LinearArgs layout");
 
@@ -63,16 +66,62 @@ constexpr int32_t kSegPartial = 1, kSegZeroPoint = 2;
 constexpr int kMaxSplitWindows = 4;
 
 // Stack workspace layout (device memory, 256-byte aligned):
-//   StackHeader | LinearArgs[nlin] | int32 seg_start[workers + 1] |
-//   Segment[nseg] | int32 split[nsplit]
+//   StackHeader | StackSync | uint32 flag[njobs * M] | LinearArgs[nlin] |
+//   int32 seg_start[workers + 1] | Segment[nseg] | int32 split[nsplit] |
+//   QuantJob[njobs] | uint32 part[ceil(grid / 32)]
 // The first L entries of LinearArgs are the caller's linears; a linear split
 // along K adds one entry per window after them, and split[] lists the split
 // linears (their outputs are cleared before and finished after the main
-// kernel).
+// kernel).  QuantJob lists the fp32 inputs the launch quantises itself
+// (each distinct q buffer once); its items are (job, token) rows, item
+// i = job * M + m, and flag[i] says which launch has finished item i.
 struct alignas(256) StackHeader {
   int32_t magic, L, M, workers, nseg, kernel, nlin, nsplit;
   int64_t off_lin, off_seg_start, off_seg, off_split;
+  int32_t njobs, nitems;  // quantisation jobs, and their rows (njobs * M)
+  int64_t off_job, off_sync, off_flag;
+  // workgroups that claim rows: their number, and one bit per workgroup of
+  // the grid (uint32 words at off_part)
+  int32_t claimers, pad0;
+  int64_t off_part;
 };
+static_assert(sizeof(StackHeader) == 256, "StackHeader layout");
+
+// One fp32 input quantised inside the launch: M rows of K floats (stride
+// ldx) into M rows of int8 codes (stride ldq), a scale and a zero point per
+// row -- the arithmetic of tern_quantize_act.
+struct alignas(16) QuantJob {
+  const float* x;
+  int8_t* q;
+  float* s_act;
+  int32_t* z;
+  int64_t ldx, ldq;
+  int32_t K;
+  int32_t pad[3];
+};
+static_assert(sizeof(QuantJob) == 64, "QuantJob layout");
+
+// Words the launch updates: claim counts the rows claimed by workgroups over
+// every launch of the plan (each launch advances it by a fixed amount, which
+// numbers the launches); err is set when a wait for a quantised input gave
+// up.  They sit at a fixed offset after the header, with the flags right
+// after them, and reach the kernels as an argument of their own: everything
+// the kernels read through the header pointer stays read-only for the whole
+// launch, so the compiler keeps those reads in scalar loads (written through
+// the same pointer, they would become vector loads whose waits also wait for
+// the weight tiles in flight).
+struct alignas(64) StackSync {
+  unsigned long long claim;
+  uint32_t err;
+  uint32_t pad[13];
+};
+static_assert(sizeof(StackSync) == 64, "StackSync layout");
+constexpr int64_t kStackSyncOffset = sizeof(StackHeader);
+inline StackSync* stack_sync(const void* ws) {
+  return reinterpret_cast<StackSync*>(static_cast<char*>(const_cast<void*>(ws)) + kStackSyncOffset);
+}
+// Rows of quantisation jobs one plan may hold.
+constexpr int64_t kMaxQuantItems = 1ll << 22;
 constexpr int32_t kStackMagic = 0x7e54a11;
 
 // Kernel selectors of a prepared stack.

@@ -22,7 +22,7 @@
 //
 // Two kernels: the lockstep workgroup kernel (9 <= M <= 16, or any K) and
 // the activation-window kernel (M <= 8, K a multiple of 64).
-#include "tern_device.h"
+#include "tern_prologue.h"
 
 namespace tern {
 
@@ -902,8 +902,11 @@ __global__ __launch_bounds__(kBlock) void mfma_wg_linear_kernel(LinearArgs a) {
 }
 
 template <int MQ, bool RAGGED>
-__global__ __launch_bounds__(kBlock) void mfma_wg_stack_kernel(const StackHeader* __restrict__ h) {
+__global__ __launch_bounds__(kBlock) void mfma_wg_stack_kernel(const StackHeader* __restrict__ h,
+                                  StackSync* __restrict__ sy) {
   __shared__ __attribute__((aligned(16))) WgTiles<MQ> L;
+  __shared__ PrologueLds prol;
+  const uint32_t launch1 = stack_prologue(h, sy, prol);
   const int worker = xcd_logical_block();
   if (worker >= h->workers) return;  // the same for the whole workgroup
   clear_zero_row(L);
@@ -914,6 +917,7 @@ __global__ __launch_bounds__(kBlock) void mfma_wg_stack_kernel(const StackHeader
   const int32_t* seg_start = reinterpret_cast<const int32_t*>(base + h->off_seg_start);
   const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
   const int s1 = seg_start[worker + 1];
+  wait_segment_inputs(h, sy, lin, seg, seg_start[worker], s1, launch1);
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
@@ -937,10 +941,13 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2)
 // registers (kOutUnits units per wave, kOutUnitsBlk in the kernel for stacks
 // with block scales) and stored at the end of the run.
 template <bool SPLIT, bool BLK = false>
-__global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_win_stack_kernel(const StackHeader* __restrict__ h) {
+__global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_win_stack_kernel(const StackHeader* __restrict__ h,
+                                  StackSync* __restrict__ sy) {
   constexpr int MAXU = BLK ? kOutUnitsBlk : kOutUnits;
   __shared__ __attribute__((aligned(16))) WinTiles<8, BLK> L;
   __shared__ OutMeta meta[kWinWaves][MAXU];
+  __shared__ PrologueLds prol;
+  const uint32_t launch1 = stack_prologue(h, sy, prol);
   const int worker = xcd_logical_block();
   if (worker >= h->workers) return;  // the same for the whole workgroup
   const int lane = threadIdx.x & 63;
@@ -950,6 +957,7 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int32_t* seg_start = reinterpret_cast<const int32_t*>(base + h->off_seg_start);
   const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
   const int s1 = seg_start[worker + 1];
+  wait_segment_inputs(h, sy, lin, seg, seg_start[worker], s1, launch1);
   WinStaged staged;
   OutBuf<MAXU, 4> ob;
   for (int s = seg_start[worker]; s < s1; ++s) {
@@ -967,10 +975,12 @@ __global__ __launch_bounds__(kWinBlock) __attribute__((amdgpu_waves_per_eu(2, 2)
 // (Only SPLIT = false is launched.)
 template <bool SPLIT, bool BLK = false>
 __global__ __launch_bounds__(WinGeo<16>::BLOCK) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_win16_stack_kernel(
-    const StackHeader* __restrict__ h) {
+    const StackHeader* __restrict__ h, StackSync* __restrict__ sy) {
   constexpr int MAXU = BLK ? kOut16UnitsBlk : kOut16Units;
   __shared__ __attribute__((aligned(16))) WinTiles<16, BLK> L;
   __shared__ OutMeta meta[WinGeo<16>::WAVES][MAXU];
+  __shared__ PrologueLds prol;
+  const uint32_t launch1 = stack_prologue(h, sy, prol);
   const int worker = xcd_logical_block();
   if (worker >= h->workers) return;  // the same for the whole workgroup
   const int lane = threadIdx.x & 63;
@@ -980,6 +990,7 @@ __global__ __launch_bounds__(WinGeo<16>::BLOCK) __attribute__((amdgpu_waves_per_
   const int32_t* seg_start = reinterpret_cast<const int32_t*>(base + h->off_seg_start);
   const Segment* seg = reinterpret_cast<const Segment*>(base + h->off_seg);
   const int s1 = seg_start[worker + 1];
+  wait_segment_inputs(h, sy, lin, seg, seg_start[worker], s1, launch1);
   WinStaged staged;
   OutBuf<MAXU, 8> ob;
   for (int s = seg_start[worker]; s < s1; ++s) {
@@ -1161,11 +1172,11 @@ hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape&
   }
   hipError_t e;
   if (split) {
-    hipLaunchKernelGGL(mfma_win_stack_kernel<true>, grid, block, 0, s, h);
+    hipLaunchKernelGGL(mfma_win_stack_kernel<true>, grid, block, 0, s, h, stack_sync(ws));
     e = hipGetLastError();
   } else {
     e = with_mfma_stack_kernel(variant, [&](auto kern) {
-      hipLaunchKernelGGL(kern, grid, block, 0, s, h);
+      hipLaunchKernelGGL(kern, grid, block, 0, s, h, stack_sync(ws));
       return hipGetLastError();
     });
   }

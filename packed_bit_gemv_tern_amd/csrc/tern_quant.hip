@@ -14,24 +14,13 @@
 // Every division is one correctly rounded fp32 division and rint rounds half
 // to even, so the integer codes are a function of the fp32 inputs alone.
 // One workgroup per token: a min/max pass over the row, then the codes.
-#include "tern_device.h"
+#include "tern_prologue.h"
 
 namespace tern {
 
 namespace {
 
 constexpr int kQuantBlock = 256;
-
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = fminf(v, __shfl_xor(v, d, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
-  return v;
-}
 
 __global__ __launch_bounds__(kQuantBlock) void quant_kernel(const float* x, int64_t K, int64_t ldx,
                                                             int8_t* q, int64_t ldq, float* s_act,
@@ -45,22 +34,18 @@ __global__ __launch_bounds__(kQuantBlock) void quant_kernel(const float* x, int6
     lo = fminf(lo, v);
     hi = fmaxf(hi, v);
   }
-  lo = wave_min(lo);
-  hi = wave_max(hi);
+  lo = wave_min_f(lo);
+  hi = wave_max_f(hi);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[0][w] = lo, red[1][w] = hi;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kQuantBlock / 64; ++i) lo = fminf(lo, red[0][i]), hi = fmaxf(hi, red[1][i]);
-  float s = __fdiv_rn(hi - lo, 255.0f);
-  if (s == 0.0f) s = 1.0f;
-  const int32_t zm = -128 - (int32_t)__builtin_rintf(__fdiv_rn(lo, s));
+  float s;
+  int32_t zm;
+  act_params(lo, hi, s, zm);
   int8_t* out = q + m * ldq;
-  for (int64_t j = threadIdx.x; j < K; j += kQuantBlock) {
-    int32_t v = (int32_t)__builtin_rintf(__fdiv_rn(load_g(r + j), s)) + zm;
-    v = min(127, max(-128, v));
-    out[j] = (int8_t)v;
-  }
+  for (int64_t j = threadIdx.x; j < K; j += kQuantBlock) out[j] = (int8_t)act_code(load_g(r + j), s, zm);
   if (threadIdx.x == 0) {
     s_act[m] = s;
     z[m] = zm;

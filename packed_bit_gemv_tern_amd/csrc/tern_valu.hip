@@ -23,7 +23,7 @@
 // A row is split over LPR lanes; each wave reduces U rows at once with a
 // transposed butterfly (v_permlane32/16_swap and DPP), so the cross-lane cost
 // is about two operations per row instead of six.
-#include "tern_device.h"
+#include "tern_prologue.h"
 
 namespace tern {
 
@@ -589,7 +589,10 @@ __global__ __launch_bounds__(kBlock) void valu_stream_kernel(LinearArgs a) {
 }
 
 template <int MT, uint32_t VSET>
-__global__ __launch_bounds__(kBlock) void valu_stack_kernel(const StackHeader* __restrict__ h) {
+__global__ __launch_bounds__(kBlock) void valu_stack_kernel(const StackHeader* __restrict__ h,
+                                  StackSync* __restrict__ sy) {
+  __shared__ PrologueLds prol;
+  const uint32_t launch1 = stack_prologue(h, sy, prol);
   const int lane = threadIdx.x & 63;
   const int worker = xcd_logical_block() * kWavesPerBlock + wave_id_uniform();
   if (worker >= h->workers) return;
@@ -600,6 +603,7 @@ __global__ __launch_bounds__(kBlock) void valu_stack_kernel(const StackHeader* _
   const Segment* seg = reinterpret_cast<const Segment*>(
       reinterpret_cast<const char*>(h) + h->off_seg);
   const int s1 = seg_start[worker + 1];
+  wait_segment_inputs(h, sy, lin, seg, seg_start[worker], s1, launch1);
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
@@ -613,8 +617,11 @@ __global__ __launch_bounds__(kBlock) void valu_stack_kernel(const StackHeader* _
 // M = 1 stacks holding block-scaled linears: those take the block path,
 // the others the per-row path (both compiled for the variant set VSET).
 template <uint32_t VSET>
-__global__ __launch_bounds__(kBlock) void valu_stack_blk_kernel(const StackHeader* __restrict__ h) {
+__global__ __launch_bounds__(kBlock) void valu_stack_blk_kernel(const StackHeader* __restrict__ h,
+                                  StackSync* __restrict__ sy) {
   __shared__ __attribute__((aligned(16))) float prods[kWavesPerBlock][kBlkLdsWave / 4];
+  __shared__ PrologueLds prol;
+  const uint32_t launch1 = stack_prologue(h, sy, prol);
   const int lane = threadIdx.x & 63;
   const int w = wave_id_uniform();
   const int worker = xcd_logical_block() * kWavesPerBlock + w;
@@ -626,6 +633,7 @@ __global__ __launch_bounds__(kBlock) void valu_stack_blk_kernel(const StackHeade
   const Segment* seg = reinterpret_cast<const Segment*>(
       reinterpret_cast<const char*>(h) + h->off_seg);
   const int s1 = seg_start[worker + 1];
+  wait_segment_inputs(h, sy, lin, seg, seg_start[worker], s1, launch1);
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
@@ -776,7 +784,7 @@ hipError_t launch_valu_stack(int32_t kernel, const void* ws, const LaunchShape& 
   const StackHeader* h = static_cast<const StackHeader*>(ws);
   const dim3 grid(shp.grid), block(shp.block);
   return with_valu_stack_kernel(kernel, [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, block, 0, s, h);
+    hipLaunchKernelGGL(kern, grid, block, 0, s, h, stack_sync(ws));
     return hipGetLastError();
   });
 }

@@ -97,13 +97,18 @@ class DeviceStack:
         return sum(pl.N * pl.K for pl in self.linears)
 
     def bind(self, M: int, path: int = tern.TERN_PATH_AUTO, with_acc: bool = False,
-             act_seed: int | None = None, share_inputs: bool = False) -> "StackBinding":
+             act_seed: int | None = None, share_inputs: bool = False,
+             quantise: str = "none") -> "StackBinding":
         """Buffers and a prepared launch for M tokens.  With ``share_inputs``
         the linears of a layer that read one input (``synth.INPUT_LEADER``:
         q/k/v, gate/up) are given one activation buffer, drawn for the
-        group's first linear; otherwise every linear has its own."""
+        group's first linear; otherwise every linear has its own.
+        ``quantise``: "none" (int8 activations drawn directly), "first" (the
+        first input is fp32, ``synth.make_hidden``, quantised by the launch
+        itself) or "all" (every input is)."""
+        assert quantise in ("none", "first", "all")
         return StackBinding(self, M, path, with_acc, self.seed if act_seed is None else act_seed,
-                            share_inputs)
+                            share_inputs, quantise)
 
 
 @dataclass
@@ -115,12 +120,15 @@ class StackBinding:
     with_acc: bool
     act_seed: int
     share_inputs: bool = False
+    quantise: str = "none"
     q: list = field(default_factory=list)
     s_act: list = field(default_factory=list)
     z: list = field(default_factory=list)
     y: list = field(default_factory=list)
     acc: list = field(default_factory=list)
     host_act: list = field(default_factory=list)
+    x: list = field(default_factory=list)       # fp32 inputs (device) or None
+    host_x: list = field(default_factory=list)  # their host copies or None
 
     def __post_init__(self):
         dev, M = self.stack.device, self.M
@@ -130,14 +138,26 @@ class StackBinding:
             src = synth.INPUT_LEADER[pl.idx] if self.share_inputs else pl.idx
             key = (pl.layer, src)
             if key not in shared:
-                q, s_act, z = synth.make_activations(self.act_seed, pl.layer, src, pl.K, M)
                 ldq = _pad16(pl.K)
-                qp = np.zeros((M, ldq), np.int8)
-                qp[:, : pl.K] = q
-                shared[key] = ((q, s_act, z), torch.from_numpy(qp).to(dev), torch.from_numpy(s_act).to(dev),
-                               torch.from_numpy(z).to(dev))
-            (q, s_act, z), qd, sd, zd = shared[key]
+                if self.quantise == "all" or (self.quantise == "first" and not shared):
+                    # an fp32 input: q, s_act and z are written by the launch
+                    x = synth.make_hidden(self.act_seed, pl.layer, src, pl.K, M)
+                    shared[key] = (None, torch.zeros((M, ldq), dtype=torch.int8, device=dev),
+                                   torch.zeros(M, dtype=torch.float32, device=dev),
+                                   torch.zeros(M, dtype=torch.int32, device=dev), x, torch.from_numpy(x).to(dev))
+                else:
+                    q, s_act, z = synth.make_activations(self.act_seed, pl.layer, src, pl.K, M)
+                    qp = np.zeros((M, ldq), np.int8)
+                    qp[:, : pl.K] = q
+                    shared[key] = ((q, s_act, z), torch.from_numpy(qp).to(dev), torch.from_numpy(s_act).to(dev),
+                                   torch.from_numpy(z).to(dev), None, None)
+            host, qd, sd, zd, hx, xd = shared[key]
             ldq = qd.shape[1]
+            self.x.append(xd)
+            self.host_x.append(hx)
+            # (an fp32 input has no host int8 activations: its q, s_act and z
+            # exist only once the launch has run)
+            q, s_act, z = host if host is not None else (None, None, None)
             yd = torch.empty((M, pl.N), dtype=torch.float32, device=dev)
             ad = torch.empty((M, pl.N), dtype=torch.int32, device=dev) if self.with_acc else None
             self.q.append(qd)
@@ -148,7 +168,8 @@ class StackBinding:
             if pl.sample_rows is not None:
                 self.host_act.append((q, s_act, z))
             descs.append(tern.make_desc(pl.packed, pl.s_row, pl.rowsum, pl.N, pl.K, qd, ldq, sd,
-                                        zd, yd, pl.N, ad, pl.block, pl.s_block, pl.rowsum_block))
+                                        zd, yd, pl.N, ad, pl.block, pl.s_block, pl.rowsum_block,
+                                        x=xd, ldx=pl.K))
         self.descs = descs
         L = len(descs)
         self.workspace = torch.empty(tern.tern_linear_stack_workspace_bytes(L, M),

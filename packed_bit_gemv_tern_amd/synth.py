@@ -156,6 +156,17 @@ def make_activations(seed, layer: int, idx: int, K: int, M: int):
     return q, s_act, z
 
 
+def make_hidden(seed, layer: int, idx: int, K: int, M: int) -> np.ndarray:
+    """float32 (M, K) token rows before quantisation, the input of a linear
+    that quantises its own activations: standard normal values with one
+    column in 256 (the same columns for every token) twenty times larger,
+    the outlier channels of a normalised hidden state."""
+    rng = np.random.default_rng([seed, layer, idx, 2 << 20, M])
+    x = rng.normal(0.0, 1.0, (M, K))
+    x[:, rng.permutation(K)[: max(1, K // 256)]] *= 20.0
+    return x.astype(np.float32)
+
+
 def make_linear(seed, layer: int, idx: int, N: int, K: int, p_zero: float, M: int,
                 name: str = "") -> Linear:
     w, s_row = make_weights(seed, layer, idx, N, K, p_zero)

@@ -21,6 +21,7 @@ TERN_ERR_RANGE = 3
 TERN_ERR_UNSUPPORTED = 4
 TERN_ERR_WORKSPACE = 5
 TERN_ERR_HIP = 6
+TERN_ERR_TIMEOUT = 7
 TERN_PATH_AUTO, TERN_PATH_VALU, TERN_PATH_MFMA = 0, 1, 2
 TERN_MAX_K = 5600000
 TERN_VALU_MAX_M = 8
@@ -35,7 +36,7 @@ TERN5_MAX_K = 65520
 EXPORTS = (
     "tern_row_bytes", "tern_pack", "tern_unpack", "tern_validate", "tern_gemv",
     "tern_gemm_smallM", "tern_linear_stack_workspace_bytes", "tern_linear_stack_prepare",
-    "tern_linear_stack", "tern_linear_stack_prepare_static", "tern_block_rowsum", "tern_gemv_blocked", "tern_quantize_act",
+    "tern_linear_stack", "tern_linear_stack_status", "tern_linear_stack_prepare_static", "tern_block_rowsum", "tern_gemv_blocked", "tern_quantize_act",
     "tern_quantize_weights", "tern_head_rowsum", "tern_head_gemv", "tern_row_bytes5", "tern_pack5", "tern_gemv5",
     "tern_read_probe",
     "tern_status_string", "tern_last_hip_error",
@@ -59,6 +60,7 @@ class tern_linear_desc(ctypes.Structure):
         ("s_act", ctypes.c_void_p), ("z", ctypes.c_void_p),
         ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64), ("acc", ctypes.c_void_p),
         ("block", ctypes.c_int64), ("s_block", ctypes.c_void_p), ("rowsum_block", ctypes.c_void_p),
+        ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64),
     ]
 
 
@@ -103,6 +105,7 @@ def _declare(lib):
         "tern_linear_stack_prepare": (i32, [ctypes.POINTER(tern_linear_desc), i64, i64, i32,
                                             vp, i64, ctypes.POINTER(tern_stack_plan), vp]),
         "tern_linear_stack": (i32, [ctypes.POINTER(tern_stack_plan), vp]),
+        "tern_linear_stack_status": (i32, [ctypes.POINTER(tern_stack_plan), vp]),
         "tern_linear_stack_prepare_static": (i32, [ctypes.POINTER(tern_linear_desc), i64, i64, i32,
                                                    ctypes.POINTER(tern_stack_plan), vp]),
         "tern_block_rowsum": (i32, [vp, i64, i64, i64, vp, vp]),
@@ -233,11 +236,14 @@ def tern_linear_stack_workspace_bytes(L: int, M: int) -> int:
 
 
 def make_desc(packed, s_row, rowsum, N, K, q, ldq, s_act, z, y, ldy, acc=None, block=0, s_block=None,
-              rowsum_block=None) -> tern_linear_desc:
+              rowsum_block=None, x=None, ldx=0) -> tern_linear_desc:
     """One linear of a stack.  With block > 0 (block-wise scales along K),
     s_block / rowsum_block are N x ceil(K / block) and s_row / rowsum may be
-    None."""
+    None.  With x (fp32, M x K, row stride ldx) the launch quantises x into
+    q, s_act and z itself."""
     d = tern_linear_desc()
+    d.x = None if x is None else x.data_ptr()
+    d.ldx = int(ldx)
     d.packed = packed.data_ptr()
     d.s_row = None if s_row is None else s_row.data_ptr()
     d.rowsum = None if rowsum is None else rowsum.data_ptr()
@@ -278,6 +284,12 @@ def tern_linear_stack_prepare_static(descs, M, path=TERN_PATH_AUTO, stream=None)
 
 def tern_linear_stack(plan, stream=None):
     _check(_lib().tern_linear_stack(ctypes.byref(plan), _stream(stream)), "tern_linear_stack")
+
+
+def tern_linear_stack_status(plan, stream=None):
+    """Synchronises the stream; raises TernError (TERN_ERR_TIMEOUT) if a
+    launch of the plan gave up waiting for a quantised input."""
+    _check(_lib().tern_linear_stack_status(ctypes.byref(plan), _stream(stream)), "tern_linear_stack_status")
 
 
 def tern_read_probe(buf, nbytes, sink, blocks_per_cu=4, unroll=8, nontemporal=True, stream=None):

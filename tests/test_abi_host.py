@@ -52,8 +52,9 @@ def test_row_bytes(lib):
 
 
 def test_status_strings(lib):
-    for st in range(7):
-        assert tern.status_string(st)
+    for st in range(8):
+        assert tern.status_string(st) != "unknown status"
+
     assert tern.status_string(99) == "unknown status"
     assert lib.tern_last_hip_error() == 0
 
@@ -148,6 +149,30 @@ def test_stack_prepare_errors(lib):
     assert lib.tern_linear_stack(None, S) == tern.TERN_ERR_INVALID_ARG
 
 
+def test_stack_fused_input_errors(lib):
+    # descriptors naming an fp32 input x: checked before anything is launched
+    plan = tern.tern_stack_plan()
+    X = 0x20000
+
+    def prep(*descs, M=2):
+        arr = (tern.tern_linear_desc * len(descs))(*descs)
+        return lib.tern_linear_stack_prepare(arr, len(descs), M, 0, A16, 1 << 20, ctypes.byref(plan), S)
+
+    assert prep(_desc(x=X, ldx=63)) == tern.TERN_ERR_INVALID_ARG           # rows shorter than K
+    assert prep(_desc(x=X + 2, ldx=64)) == tern.TERN_ERR_ALIGNMENT
+    assert prep(_desc(x=X, ldx=2 ** 31)) == tern.TERN_ERR_RANGE
+    assert prep(_desc(x=X, ldx=64, ldq=72)) == tern.TERN_ERR_ALIGNMENT     # q rows of 16-byte multiples
+    # a linear without rows still has its input written, so its q is checked
+    assert prep(_desc(x=X, ldx=64, N=0, q=None)) == tern.TERN_ERR_INVALID_ARG
+    assert prep(_desc(x=X, ldx=64, N=0, q=A16 + 8)) == tern.TERN_ERR_ALIGNMENT
+    # one q buffer, two different inputs or scales
+    assert prep(_desc(x=X, ldx=64), _desc(x=X + 1024, ldx=64)) == tern.TERN_ERR_INVALID_ARG
+    assert prep(_desc(x=X, ldx=64), _desc(x=X, ldx=80)) == tern.TERN_ERR_INVALID_ARG
+    assert prep(_desc(x=X, ldx=64), _desc(s_act=A16 + 64)) == tern.TERN_ERR_INVALID_ARG
+    assert prep(_desc(x=X, ldx=64), _desc(K=128, ldq=128)) == tern.TERN_ERR_INVALID_ARG
+    assert lib.tern_linear_stack_status(None, S) == tern.TERN_ERR_INVALID_ARG
+
+
 def test_stack_empty_plan(lib):
     plan = tern.tern_stack_plan()
     arr = (tern.tern_linear_desc * 1)(_desc())
@@ -156,6 +181,7 @@ def test_stack_empty_plan(lib):
     assert lib.tern_linear_stack(ctypes.byref(plan), S) == tern.TERN_OK
     assert lib.tern_linear_stack_prepare(arr, 1, 0, 0, None, 0, ctypes.byref(plan), S) == tern.TERN_OK
     assert lib.tern_linear_stack(ctypes.byref(plan), S) == tern.TERN_OK
+    assert lib.tern_linear_stack_status(ctypes.byref(plan), S) == tern.TERN_OK
 
 
 def test_read_probe_argument_errors(lib):

@@ -1,7 +1,9 @@
 """A decode step captured in a HIP graph: activation quantiser -> stack of
 ternary linears -> int8 head, replayed with new activations between eager
 work and synchronisations; every replay must equal the eager run bit for
-bit (the calls enqueue kernels only: no allocation, copy or memset)."""
+bit (the calls enqueue kernels only: no allocation, copy or memset).  The
+same step with the quantiser fused into the stack launch (two launches)
+gives the same bits as the three-launch step."""
 import numpy as np
 import pytest
 
@@ -61,3 +63,57 @@ def test_decode_step_graph_replays(M):
             torch.cuda.synchronize()
             for a, e in zip(outputs(), eager[i]):
                 assert torch.equal(a.view(torch.uint8), e.view(torch.uint8)), (M, rep, i)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_fused_decode_step_graph_replays(M):
+    # layer 0's q/k/v read one fp32 token row that the stack launch quantises
+    # itself; the head reads the quantised row after it: two launches
+    st = DeviceStack("8b", layers=1, seed=12, threads=8)
+    fused = st.bind(M, share_inputs=True, quantise="first")
+    sep = st.bind(M, share_inputs=True)
+    K = st.linears[0].K
+    ldq = sep.q[0].shape[1]
+    Wh, srh = synth.make_head(4, 2000, K)
+    Whd, srhd = to_dev(Wh), to_dev(srh)
+    rsh = torch.empty(2000, dtype=torch.int32, device=DEV)
+    tern.tern_head_rowsum(Whd, 2000, K, K, rsh)
+    x = fused.x[0]
+    assert x is not None and fused.x[1] is x and fused.x[2] is x and fused.x[3] is None
+    lf = torch.empty((M, 2000), dtype=torch.float32, device=DEV)
+    ls = torch.empty((M, 2000), dtype=torch.float32, device=DEV)
+
+    def step_fused():
+        fused.run()
+        tern.tern_head_gemv(Whd, srhd, rsh, 2000, K, K, M, fused.q[0], ldq, fused.s_act[0], fused.z[0], lf, 2000)
+
+    def step_sep():
+        tern.tern_quantize_act(x, M, K, K, sep.q[0], ldq, sep.s_act[0], sep.z[0])
+        sep.run()
+        tern.tern_head_gemv(Whd, srhd, rsh, 2000, K, K, M, sep.q[0], ldq, sep.s_act[0], sep.z[0], ls, 2000)
+
+    rng = np.random.default_rng(M + 100)
+    xs = [rng.normal(0, 1 + i, (M, K)).astype(np.float32) for i in range(4)]
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step_fused()
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for xi in xs:
+            x.copy_(torch.from_numpy(xi))
+            for y in fused.y:
+                y.fill_(float("nan"))
+            lf.zero_()
+            torch.cuda.synchronize()
+            if rep == 0:
+                step_fused()
+            else:
+                g.replay()
+            step_sep()
+            torch.cuda.synchronize()
+            for a, b_ in zip(fused.y + [lf, fused.q[0], fused.s_act[0], fused.z[0]],
+                             sep.y + [ls, sep.q[0], sep.s_act[0], sep.z[0]]):
+                assert torch.equal(a.view(torch.int8) if a.dtype != torch.int8 else a,
+                                   b_.view(torch.int8) if b_.dtype != torch.int8 else b_), (M, rep)
+    tern.tern_linear_stack_status(fused.plan)
