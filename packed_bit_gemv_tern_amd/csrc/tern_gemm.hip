@@ -49,15 +49,17 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Tile shapes.  BM = 128: 256 rows x 128 tokens, eight waves in a 4 x 2 grid
 // of 64 rows x 64 tokens each.  BM = 64: 128 rows x 64 tokens, four waves of
-// 32 rows x 64 tokens.  Every wave brings 32 weight rows and BM / 16 / WAVES
-// activation instructions per step, so all waves issue the same count.
+// 32 rows x 64 tokens.  Every wave brings ROWS / WAVES weight rows and
+// BM / 16 / WAVES activation instructions per step, so all waves issue the
+// same count.
 template <int BM>
 struct GemmShape {
   static constexpr int ROWS = BM == 128 ? 256 : 128;
   static constexpr int WAVES = BM == 128 ? 8 : 4;
-  static constexpr int RGROUPS = BM == 128 ? 4 : 4;  // row groups of the wave grid
+  static constexpr int RGROUPS = 4;                  // row groups of the wave grid
   static constexpr int WT = 4;                       // token blocks of 16 per wave
   static constexpr int WR = ROWS / RGROUPS / 16;     // row blocks of 16 per wave
+  static constexpr int RPW = ROWS / WAVES;           // weight rows each wave brings (one lane each)
   static constexpr int QLD = BM / 16 / WAVES;        // activation DMA instructions per wave
   static constexpr int PER = QLD + 1;                // DMA instructions per wave per step
   // LDS ring depth and K-steps per barrier.  The 64-token tile waits and
@@ -68,7 +70,8 @@ struct GemmShape {
   static constexpr int STAGES = BM == 128 ? 6 : 12;
   static constexpr int SS = BM == 128 ? 1 : 6;
   static constexpr int META = (2 * ROWS + 2 * BM) / 64;  // operand DMA instructions per tile
-  static_assert(WAVES * 32 == ROWS && QLD * WAVES * 16 == BM, "tile shape");
+  static_assert(RPW <= 64 && RGROUPS * WR * 16 == ROWS && (WAVES / RGROUPS) * WT * 16 == BM &&
+                QLD * WAVES * 16 == BM, "tile shape");
   static_assert(PER * (STAGES - 2 * SS) < 64 && STAGES % SS == 0, "vmcnt field");
 };
 
@@ -136,10 +139,10 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
   const int nks = a.nch;  // K-steps: one 16-byte packed chunk (64 weights) per row each
   // this wave's place in the tile
   const int wr = w % S::RGROUPS, wt = w / S::RGROUPS;
-  const int rbase = wr * 16 * S::WR, tbase = wt * 64;
+  const int rbase = wr * 16 * S::WR, tbase = wt * 16 * S::WT;
 
   // DMA sources: activation rows for this wave's QLD instructions, and the
-  // weight row of lane l < 32 (rows 32w + l of the tile)
+  // weight row of lane l < RPW (rows RPW w + l of the tile)
   const int8_t* qsrc[S::QLD];
   int qchunk[S::QLD];
 #pragma unroll
@@ -149,7 +152,7 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
     qchunk[j] = (lane & 3) ^ gemm_qswz(t);        // source chunk of this LDS slot
     qsrc[j] = a.q + (int64_t)min(tok0 + t, M - 1) * a.ldq;
   }
-  const uint8_t* wsrc = a.packed + (int64_t)min(row0 + 32 * w + (lane & 31), N - 1) * a.ld;
+  const uint8_t* wsrc = a.packed + (int64_t)min(row0 + S::RPW * w + (lane & (S::RPW - 1)), N - 1) * a.ld;
   const int qmax = a.ldq - 16;  // last in-row 16-byte activation chunk
 
   // row and token operands of the tile, 64 values (4 bytes per lane) per
@@ -182,8 +185,8 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
       __builtin_amdgcn_global_load_lds((const void*)(qsrc[j] + off),
                                        (lds_ptr_t)(&L.q[s][1024 * (w * S::QLD + j)]), 16, 0, 0);
     }
-    if (lane < 32)
-      __builtin_amdgcn_global_load_lds((const void*)(wsrc + 16 * k), (lds_ptr_t)(&L.w[s][512 * w]),
+    if (lane < S::RPW)
+      __builtin_amdgcn_global_load_lds((const void*)(wsrc + 16 * k), (lds_ptr_t)(&L.w[s][16 * S::RPW * w]),
                                        16, 0, 0);
   };
 
@@ -228,8 +231,6 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
 #pragma unroll
   for (int s = 0; s < S::STAGES - S::SS; ++s)
     if (s < nks) issue(s);
-  // step k: my loads landed (later steps may still fly), then everybody's;
-  // the barrier also frees the buffer the next issue reuses
   // steps k0 .. k0 + SS - 1 landed (mine, then everybody's); the barrier
   // also frees the SS buffers the next issues reuse, read in the previous
   // round
@@ -252,33 +253,33 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
     }
   }
 
-  // epilogue: lane holds tokens tok0 + tbase + 16t + 4g + v of row row0 + rbase + 16b + r
+  // epilogue: lane holds tokens tok0 + tbase + 16t + 4g + v of row row0 +
+  // rbase + 16b + r; token by token (its zero point and scale read once),
+  // the rows' operands read from LDS where used
   const bool partial = SPLIT && (flags & kSegPartial) != 0;
   const bool zpoint = !partial || (flags & kSegZeroPoint) != 0;
 #pragma unroll
-  for (int b = 0; b < S::WR; ++b) {
-    const int rl = rbase + 16 * b + r;
-    const int row = row0 + rl;
-    if (row >= N) continue;
-    const int32_t rs = L.rowsum[rl];
-    const float sr = L.s_row[rl];
+  for (int t = 0; t < S::WT; ++t) {
 #pragma unroll
-    for (int t = 0; t < S::WT; ++t) {
+    for (int v = 0; v < 4; ++v) {
+      const int ml = tbase + 16 * t + 4 * g + v;
+      const int m = tok0 + ml;
+      if (m >= M) continue;
+      const int32_t zz = zpoint ? L.z[ml] : 0;
+      const float sa = L.s_act[ml];
+      const int64_t o0 = (int64_t)m * a.ldy + row0 + rbase + r;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int ml = tbase + 16 * t + 4 * g + v;
-        const int m = tok0 + ml;
-        if (m < M) {
-          const int32_t zz = zpoint ? L.z[ml] : 0;
-          const int32_t accv = (int32_t)((uint32_t)acc[b][t][v] - (uint32_t)zz * (uint32_t)rs);
-          const int64_t o = (int64_t)m * a.ldy + row;
-          if (partial) {
-            __hip_atomic_fetch_add((int32_t __attribute__((address_space(1)))*)(reinterpret_cast<int32_t*>(a.y) + o),
-                                   accv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          } else {
-            store_g(a.y + o, epilogue(sr, accv, L.s_act[ml]));
-            if (a.acc) store_g(a.acc + o, accv);
-          }
+      for (int b = 0; b < S::WR; ++b) {
+        const int rl = rbase + 16 * b + r;
+        if (row0 + rl >= N) continue;
+        const int32_t accv = (int32_t)((uint32_t)acc[b][t][v] - (uint32_t)zz * (uint32_t)L.rowsum[rl]);
+        const int64_t o = o0 + 16 * b;
+        if (partial) {
+          __hip_atomic_fetch_add((int32_t __attribute__((address_space(1)))*)(reinterpret_cast<int32_t*>(a.y) + o),
+                                 accv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          store_g(a.y + o, epilogue(L.s_row[rl], accv, sa));
+          if (a.acc) store_g(a.acc + o, accv);
         }
       }
     }
