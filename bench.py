@@ -51,16 +51,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# The sources that define the stack kernels' device code and schedule: the
-# committed HBM counters hold only while none of them has changed.
-STACK_KERNEL_SOURCES = ("tern_api.hip", "tern_device.h", "tern_gemm.hip", "tern_internal.h",
-                        "tern_mfma.hip", "tern_valu.hip")
+# The sources that define the stack kernels' device code and schedule, and
+# the compile flags: the committed HBM counters hold only while none of them
+# has changed.
+STACK_KERNEL_SOURCES = ("csrc/tern_api.hip", "csrc/tern_device.h", "csrc/tern_gemm.hip",
+                        "csrc/tern_internal.h", "csrc/tern_mfma.hip", "csrc/tern_prologue.h",
+                        "csrc/tern_valu.hip", "build.py")
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for name in STACK_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "packed_bit_gemv_tern_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(ROOT, "packed_bit_gemv_tern_amd", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
