@@ -415,7 +415,8 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   const int nwin = (K + kWinK - 1) / kWinK;
   // block scales: K-steps per block
   const bool blk = BLK && a.s_b != nullptr;
-  const int bks = blk ? (1 << a.blg) / 8 : 1;
+  // K-steps per block, a power of two (B = 512 << lbks)
+  const int lbks = blk ? a.blg - 3 : 0, bks = 1 << lbks, bmask = bks - 1;
   const int nb = a.nb;
   int mb_issue = 0, mb_use = 0;  // block-metadata ring slots: next to fill, block being summed
   const bool partial = SPLIT && (flags & kSegPartial) != 0;
@@ -445,12 +446,20 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   // numbered in the order the wave consumes them, across units); with block
   // scales the block's scales and row sums go first when ks starts a block
   // (one DMA instruction, counted by the waits below)
-  auto issue = [&](const uint32_t (&src)[NLD], int ks, int t, int unit) {
+  // (block scales: lanes 0..31 bring the scales, 32..63 the row sums of the
+  // wave's rows; mo = the lane's row times nb, below 2^31: checked by the host)
+  const char* mptr = BLK && blk ? (lane < 32 ? reinterpret_cast<const char*>(a.s_b)
+                                             : reinterpret_cast<const char*>(a.rowsum_b))
+                                : nullptr;
+  auto unit_meta = [&](int unit) -> uint32_t {
+    if (!(BLK && blk)) return 0;
+    const int brow = min(row_lo + unit * ROWS + 16 * R * w + 16 * ((lane >> 4) & 1) + (lane & 15), row_hi - 1);
+    return (uint32_t)brow * (uint32_t)nb;
+  };
+  auto issue = [&](const uint32_t (&src)[NLD], uint32_t mo, int ks, int t) {
     if constexpr (BLK) {
-      if (blk && ks % bks == 0) {
-        const int brow = min(row_lo + unit * ROWS + 16 * R * w + 16 * ((lane >> 4) & 1) + (lane & 15), row_hi - 1);
-        const int64_t o = (int64_t)brow * nb + ks / bks;
-        const void* msrc = lane < 32 ? (const void*)(a.s_b + o) : (const void*)(a.rowsum_b + o);
+      if (blk && (ks & bmask) == 0) {
+        const void* msrc = mptr + 4 * (uint64_t)(mo + (uint32_t)(ks >> lbks));
         __builtin_amdgcn_global_load_lds(msrc, (lds_ptr)&L.blk.meta[w][mb_issue][0], 4, 0, 0);
         mb_issue = (mb_issue + 1) & (kBlkSlots - 1);
       }
@@ -484,11 +493,13 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   // unit's (a window's, window-major) K-steps, so a lookahead reaches at
   // most into the next unit
   const int depth = min(D, nks);
+  uint32_t mo = 0;
   if (ufirst < row_hi) {
     unit_src(unit0, src);
+    mo = unit_meta(unit0);
 #pragma unroll
     for (int d = 0; d < D; ++d)
-      if (d < depth) issue(src, d, d, unit0);
+      if (d < depth) issue(src, mo, d, d);
     load_rowops(unit0, nrs, nsr);
   }
 
@@ -524,7 +535,8 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
     const bool has_next = nu >= 0;
     const int nkb = wmajor ? 8 * np : 0;
     uint32_t nsrc[NLD];
-    if (has_next) unit_src(nu, nsrc);
+    uint32_t nmo = 0;
+    if (has_next) unit_src(nu, nsrc), nmo = unit_meta(nu);
     int32_t rs[R];
     float sr[R];
     i32x4 acc1[R], acc4[R], acc16[R];
@@ -536,9 +548,13 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
     // window-major, a later pass resumes from the sum held in the unit's slot
     float bsum[BLK ? NV : 1];
     int32_t bint[BLK ? NV : 1];
+    // (the plane accumulators run on over the blocks of the pass: each block's
+    // sum(c*q) is the difference of their combined value from the previous
+    // block's end, exact in int32)
+    int32_t cprev[BLK ? NV : 1];
     if constexpr (BLK) {
 #pragma unroll
-      for (int j = 0; j < NV; ++j) bsum[j] = 0.0f, bint[j] = 0;
+      for (int j = 0; j < NV; ++j) bsum[j] = 0.0f, bint[j] = 0, cprev[j] = 0;
       if (blk && wmajor && p > 0) {
         const int slot = ob.n + (u - g0);
 #pragma unroll
@@ -634,7 +650,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
         const int after = has_next ? depth - 1 : min(depth - 1, ke - 1 - ks);
         // (the tile after this one carries its block's metadata DMA first
         // when it starts a block)
-        const bool meta_after = BLK && blk && after == 1 && (ks + 1 < ke ? ks + 1 : nkb) % bks == 0;
+        const bool meta_after = BLK && blk && after == 1 && ((ks + 1 < ke ? ks + 1 : nkb) & bmask) == 0;
         if (after >= 2)
           wait_vm<2 * NLD>();
         else if (meta_after)
@@ -663,9 +679,9 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
               tile + (16 * b + r) * kStepBytes + 16 * ((2 * g + half) ^ (r & 7)));
       wait_lgkm();  // tile read: it may be overwritten
       if (ks + depth < ke)
-        issue(src, ks + depth, tb + ks - kb + depth, u);
+        issue(src, mo, ks + depth, tb + ks - kb + depth);
       else if (has_next)
-        issue(nsrc, nkb + ks + depth - ke, tb + ks - kb + depth, nu);  // the next pass's first tiles
+        issue(nsrc, nmo, nkb + ks + depth - ke, tb + ks - kb + depth);  // the next pass's first tiles
       // activations come from the window, which the loads never overwrite
       const uint8_t* qrow = &L.q[r & (T - 1)][64 * (8 * (ks & 7) + 2 * g)];
 #pragma unroll
@@ -686,13 +702,13 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
         }
       }
       if constexpr (BLK) {
-        if (blk && ((ks + 1) % bks == 0 || ks + 1 == nks)) {
+        if (blk && (((ks + 1) & bmask) == 0 || ks + 1 == nks)) {
           // the block ends: acc_b = sum(c*q) - sum(q) - z * rowsum_b, exact;
           // then one rounding for s_b * acc_b and one for the running sum.
           // Its metadata landed with the tile of its first step.
           const uint32_t* ms = L.blk.meta[w][mb_use];
           mb_use = (mb_use + 1) & (kBlkSlots - 1);
-          const int kw = (ks & 7) / bks;  // block within the window (blocks never span windows)
+          const int kw = (ks & 7) >> lbks;  // block within the window (blocks never span windows)
 #pragma unroll
           for (int j = 0; j < NV; ++j) {
             const int b = T == 8 ? (g >> 1) : (j >> 2);
@@ -702,14 +718,14 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
             const int32_t c4 = b ? acc4[1][v] : acc4[0][v];
             const int32_t c16 = b ? acc16[1][v] : acc16[0][v];
             int32_t qb = 0;
-            for (int k = kw * bks; k < kw * bks + bks; ++k) qb += L.blk.qpiece[m][k];
-            const int32_t accb = (int32_t)((uint32_t)(c1 + (c4 >> 2) + (c16 >> 4)) - (uint32_t)qb -
+            for (int k = kw << lbks; k < (kw + 1) << lbks; ++k) qb += L.blk.qpiece[m][k];
+            const int32_t cq = c1 + (c4 >> 2) + (c16 >> 4);
+            const int32_t accb = (int32_t)((uint32_t)cq - (uint32_t)cprev[j] - (uint32_t)qb -
                                            (uint32_t)L.z[m] * ms[32 + 16 * b + r]);
+            cprev[j] = cq;
             bsum[j] = add_product_rn(bsum[j], __uint_as_float(ms[16 * b + r]), (float)accb);
             bint[j] += accb;
           }
-#pragma unroll
-          for (int b = 0; b < R; ++b) acc1[b] = acc4[b] = acc16[b] = i32x4{0, 0, 0, 0};
         }
       }
     }
@@ -874,6 +890,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
     }
 #pragma unroll
     for (int i = 0; i < NLD; ++i) src[i] = nsrc[i];
+    mo = nmo;
     tb += ke - kb;
     if (!has_next) break;
     u = nu;
