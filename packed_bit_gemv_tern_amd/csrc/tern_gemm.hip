@@ -5,10 +5,10 @@
 // "Neutrino-1", model card "Overview": the weights stay packed and are
 // decoded inside the matrix kernels), so the work is a dense contraction and
 // the tile below is the usual one: a workgroup owns ROWS output rows x BM
-// tokens (256 x 128 with eight waves, or 128 x 64 with four) and walks K in
-// steps of 64.
+// tokens (512 x 128 with eight waves, or 128 x 64 with four) and walks K in
+// steps of 64.  The two tiles stage their operands differently (below).
 //
-//  * Each K-step's operands go HBM/L2 -> LDS by DMA (global_load_lds): the
+//  * 64-token tile: each K-step's operands go HBM/L2 -> LDS by DMA (global_load_lds): the
 //    BM x 64 activation tile and the ROWS x 16-byte packed weight tile, in a
 //    ring of STAGES buffers, so that later steps are in flight while the
 //    current ones are used (the loads take several steps of MFMA work to
@@ -36,6 +36,7 @@
 //    well); tokens past M and rows past N are read at clamped addresses and
 //    never stored.
 #include <algorithm>
+#include <type_traits>
 
 #include "tern_prologue.h"
 
@@ -47,32 +48,62 @@ constexpr uint32_t kGCodeTable = 0x000100FFu;  // code byte 0, 1, 2 -> -1, 0, +1
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Tile shapes.  BM = 128: 256 rows x 128 tokens, eight waves in a 4 x 2 grid
-// of 64 rows x 64 tokens each.  BM = 64: 128 rows x 64 tokens, four waves of
-// 32 rows x 64 tokens.  Every wave brings ROWS / WAVES weight rows and
-// BM / 16 / WAVES activation instructions per step, so all waves issue the
-// same count.
+// The 64-token tile: 128 rows x 64 tokens, four waves of 32 rows x 64 tokens.
+// Every wave brings ROWS / WAVES weight rows and BM / 16 / WAVES activation
+// instructions per step, so all waves issue the same count.
 template <int BM>
 struct GemmShape {
-  static constexpr int ROWS = BM == 128 ? 256 : 128;
-  static constexpr int WAVES = BM == 128 ? 8 : 4;
+  static_assert(BM == 64, "the 128-token tile is LineShape");
+  static constexpr int ROWS = 128;
+  static constexpr int WAVES = 4;
   static constexpr int RGROUPS = 4;                  // row groups of the wave grid
   static constexpr int WT = 4;                       // token blocks of 16 per wave
   static constexpr int WR = ROWS / RGROUPS / 16;     // row blocks of 16 per wave
   static constexpr int RPW = ROWS / WAVES;           // weight rows each wave brings (one lane each)
   static constexpr int QLD = BM / 16 / WAVES;        // activation DMA instructions per wave
   static constexpr int PER = QLD + 1;                // DMA instructions per wave per step
-  // LDS ring depth and K-steps per barrier.  The 64-token tile waits and
-  // synchronises once per 6 steps (a barrier per step kept its four waves in
-  // the same phase, LDS reads and MFMAs never overlapping: 133 -> 84 us per
-  // four 8B layers at M = 64); the eight-wave 128-token tile, which is bound
-  // by LDS bandwidth, was slower that way and keeps one barrier per step.
-  static constexpr int STAGES = BM == 128 ? 6 : 12;
-  static constexpr int SS = BM == 128 ? 1 : 6;
+  // LDS ring depth and K-steps per barrier: the tile waits and synchronises
+  // once per 6 steps (a barrier per step kept its four waves in the same
+  // phase, LDS reads and MFMAs never overlapping: 133 -> 84 us per four 8B
+  // layers at M = 64)
+  static constexpr int STAGES = 12;
+  static constexpr int SS = 6;
   static constexpr int META = (2 * ROWS + 2 * BM) / 64;  // operand DMA instructions per tile
   static_assert(RPW <= 64 && RGROUPS * WR * 16 == ROWS && (WAVES / RGROUPS) * WT * 16 == BM &&
                 QLD * WAVES * 16 == BM, "tile shape");
   static_assert(PER * (STAGES - 2 * SS) < 64 && STAGES % SS == 0, "vmcnt field");
+};
+
+// The 128-token tile: 512 rows x 128 tokens, eight waves of 64 rows x 128
+// tokens (two waves per SIMD; the decode of one weight dword serves eight
+// MFMAs).  Its operands are staged in runs of whole cache lines: a weight
+// stage holds WS = 4 K-steps of every row (64 contiguous bytes), an
+// activation stage AS = 2 K-steps of every token (128 bytes), each in a ring
+// of RING stages.  Staged one K-step at a time, every row's 16 bytes and
+// every token's 64 were an L2 request of their own (640 per step for four 8B
+// layers at M = 512), and the requests in flight per CU, not bytes or MFMAs,
+// set the pace.
+struct LineShape {
+  static constexpr int ROWS = 512, BM = 128, WAVES = 8;
+  static constexpr int RGROUPS = 8, WR = 4, WT = 8;  // wave grid 8 x 1
+  static constexpr int WS = 4, AS = 2, RING = 3;
+  static constexpr int WPW = ROWS * 16 * WS / 1024 / WAVES;  // weight DMA instructions per wave per stage
+  static constexpr int APW = BM * 64 * AS / 1024 / WAVES;    // activation DMA instructions per wave per stage
+  static constexpr int META = (2 * ROWS + 2 * BM) / 64;
+  static_assert(WPW * WAVES * 1024 == ROWS * 16 * WS && APW * WAVES * 1024 == BM * 64 * AS, "stage split");
+  static_assert(RGROUPS * WR * 16 == ROWS && (WAVES / RGROUPS) * WT * 16 == BM, "wave grid");
+  static_assert(WS == 2 * AS && AS == 2 && RING == 3, "the boundary logic below assumes these");
+  static_assert(WPW + APW < 64, "vmcnt field");
+};
+
+struct LineTiles {
+  using S = LineShape;
+  uint8_t q[S::RING][S::BM * 64 * S::AS];    // [stage][token][8 pieces of 16 B], swizzled
+  uint8_t w[S::RING][S::ROWS * 16 * S::WS];  // [stage][row][4 chunks of 16 B], swizzled
+  int32_t rowsum[S::ROWS];
+  float s_row[S::ROWS];
+  int32_t z[S::BM];
+  float s_act[S::BM];
 };
 
 template <int BM>
@@ -289,16 +320,247 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
   gemm_barrier();
 }
 
+// swizzles of 16-byte pieces in the line-staged rings: activation piece p of
+// token t (8 per token) sits at position p ^ line_fa(t), weight chunk c of row
+// rho (4 per row) at c ^ line_fw(rho).  A 128-bit activation read of 16 tokens
+// (t % 16 = 0..15, one piece each) and a 32-bit weight read of 16 rows x 4
+// dwords then touch every bank once per 128 bytes, whether the LDS serves
+// 8 or 16 lanes (128 or 256 bytes) per cycle.
+__device__ __forceinline__ int line_fa(int t) { return ((t >> 1) & 7) ^ ((t & 1) << 2); }
+__device__ __forceinline__ int line_fw(int rho) { return ((rho >> 1) & 3) ^ ((rho >> 2) & 3); }
+
+// One 512 x 128 tile over all of K (see LineShape): rows row0.., tokens
+// tok0..; SPLIT and flags as for gemm_tile.
+//  * Weight stage J (K-steps 4J .. 4J+3) and activation stage j (K-steps 2j,
+//    2j+1) live in ring slots J % 3 and j % 3.  At the boundary of K-step
+//    k = 2j the wave waits for activation stage j (and, with it, weight stage
+//    k / 4, issued earlier), then a barrier publishes them and frees the slots
+//    of weight stage k / 4 - 1 and activation stage j - 1, which take weight
+//    stage k / 4 + 2 (when k % 4 == 0) and activation stage j + 2: weights
+//    arrive 8 K-steps ahead, activations 4.
+//  * A weight DMA instruction brings 16 rows x 64 B (lane l: row l / 4, its
+//    chunk (l % 4) ^ line_fw(row)), an activation one 8 tokens x 128 B (lane
+//    l: token l / 8, piece (l % 8) ^ line_fa(token)); lane l lands at byte
+//    16 l of the instruction's 1 KB block, so the pieces arrive swizzled.
+//    Chunks past the row's last are read at the last (never used), pieces
+//    past ldq at the row's last 16 bytes (they meet zero weights or are
+//    masked), rows past N and tokens past M at the last one (never stored).
+template <bool SPLIT>
+__device__ __forceinline__ void gemm_tile_lines(const LinearArgs& a, int row0, int tok0, int lane, int w,
+                                                LineTiles& L, int flags) {
+  using S = LineShape;
+  const int r = lane & 15, g = lane >> 4;
+  const int K = a.K, M = a.M, N = a.N;
+  const int nks = a.nch;
+  const int nas = (nks + S::AS - 1) / S::AS, nws = (nks + S::WS - 1) / S::WS;
+  const int wr = w % S::RGROUPS, wt = w / S::RGROUPS;
+  const int rbase = wr * 16 * S::WR, tbase = wt * 16 * S::WT;
+
+  // DMA sources: the token / row index of each instruction's lane (clamped)
+  // and its swizzled piece; the 64-bit addresses are formed at each issue
+  // (held across the loop, twelve more registers made the kernel spill)
+  int atok[S::APW], apc[S::APW];
+#pragma unroll
+  for (int i = 0; i < S::APW; ++i) {
+    const int t = 8 * (w * S::APW + i) + (lane >> 3);
+    atok[i] = min(tok0 + t, M - 1);
+    apc[i] = 16 * ((lane & 7) ^ line_fa(t));
+  }
+  int wrow[S::WPW], wpc[S::WPW];
+#pragma unroll
+  for (int i = 0; i < S::WPW; ++i) {
+    const int rho = 16 * (w * S::WPW + i) + (lane >> 2);
+    wrow[i] = min(row0 + rho, N - 1);
+    wpc[i] = (lane & 3) ^ line_fw(rho);
+  }
+  const int qmax = a.ldq - 16;
+
+  auto issue_meta = [&]() {
+    for (int j = w; j < S::META; j += S::WAVES) {
+      const void* src;
+      void* dst;
+      int k = j;
+      if (k < S::ROWS / 64) {
+        src = a.rowsum + min(row0 + 64 * k + lane, N - 1), dst = &L.rowsum[64 * k];
+      } else if ((k -= S::ROWS / 64) < S::ROWS / 64) {
+        src = a.s_row + min(row0 + 64 * k + lane, N - 1), dst = &L.s_row[64 * k];
+      } else if ((k -= S::ROWS / 64) < S::BM / 64) {
+        src = a.z + min(tok0 + 64 * k + lane, M - 1), dst = &L.z[64 * k];
+      } else {
+        k -= S::BM / 64;
+        src = a.s_act + min(tok0 + 64 * k + lane, M - 1), dst = &L.s_act[64 * k];
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 4, 0, 0);
+    }
+  };
+  auto issue_w = [&](int J) {
+    uint8_t* dst = L.w[J % S::RING];
+#pragma unroll
+    for (int i = 0; i < S::WPW; ++i) {
+      int row = wrow[i];
+      asm volatile("" : "+v"(row));  // keep the address computation here
+      const int ch = min(S::WS * J + wpc[i], nks - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(a.packed + (int64_t)row * a.ld + 16 * ch),
+                                       (lds_ptr_t)(dst + 1024 * (w * S::WPW + i)), 16, 0, 0);
+    }
+  };
+  auto issue_a = [&](int j) {
+    uint8_t* dst = L.q[j % S::RING];
+#pragma unroll
+    for (int i = 0; i < S::APW; ++i) {
+      int tok = atok[i];
+      asm volatile("" : "+v"(tok));
+      const int off = min(64 * S::AS * j + apc[i], qmax);
+      __builtin_amdgcn_global_load_lds((const void*)(a.q + (int64_t)tok * a.ldq + off),
+                                       (lds_ptr_t)(dst + 1024 * (w * S::APW + i)), 16, 0, 0);
+    }
+  };
+
+  i32x4 acc[S::WR][S::WT];
+#pragma unroll
+  for (int b = 0; b < S::WR; ++b)
+#pragma unroll
+    for (int t = 0; t < S::WT; ++t) acc[b][t] = i32x4{0, 0, 0, 0};
+
+  // this lane's read offsets within a stage: weight chunk c of row block b at
+  // wofs[b] + 16 (c ^ fw), activation piece p of token block t at qofs[t] +
+  // 16 (p ^ fa); fw and fa depend on the row / token only through r
+  const int fw = line_fw(r), fa = line_fa(r);
+  auto step = [&](const uint8_t* qs, const uint8_t* ws, int k, auto last) {
+    uint32_t wd[S::WR];
+    i32x4 qa[S::WT];
+#pragma unroll
+    for (int b = 0; b < S::WR; ++b)
+      wd[b] = *reinterpret_cast<const uint32_t*>(ws + 64 * (rbase + 16 * b + r) + 16 * ((k & 3) ^ fw) + 4 * g);
+#pragma unroll
+    for (int t = 0; t < S::WT; ++t) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qs + 128 * (tbase + 16 * t + r) +
+                                                      16 * ((4 * (k & 1) + g) ^ fa));
+      qa[t] = i32x4{(int32_t)v.x, (int32_t)v.y, (int32_t)v.z, (int32_t)v.w};
+    }
+    if constexpr (decltype(last)::value) {  // the tail of K lies in the last stage
+#pragma unroll
+      for (int t = 0; t < S::WT; ++t) qa[t] = gemm_mask_tail(qa[t], 64 * k + 16 * g, K);
+    }
+#pragma unroll
+    for (int b = 0; b < S::WR; ++b) {
+      const i32x4 wb = gemm_decode(wd[b]);
+#pragma unroll
+      for (int t = 0; t < S::WT; ++t)
+        acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[t], wb, acc[b][t], 0, 0, 0);
+    }
+    // issue order: the LDS reads, the first row block's decode, then each
+    // MFMA followed by a share of the next row block's decode, so that the
+    // VALU works while the matrix core does (in program order the decode of
+    // block b + 1 waited for block b's MFMAs to release its registers)
+    constexpr int kDecode = 11;                               // VALU per decoded dword
+    constexpr int kShare = (kDecode + S::WT - 1) / S::WT + 1;  // VALU after each MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, S::WR / 2 + S::WT, 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x002, kDecode + 1, 0);       // VALU
+#pragma unroll
+    for (int i = 0; i < S::WR * S::WT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, kShare, 0);
+    }
+  };
+
+  issue_meta();  // older than every stage's loads, so the first wait covers it
+  issue_w(0);
+  issue_a(0);
+  if (nws > 1) issue_w(1);
+  if (nas > 1) issue_a(1);
+  auto stage = [&](int j, auto last) {
+    const int k = S::AS * j;
+    // loads issued after activation stage j: those of the previous boundary
+    // (or, for j = 0, of the prologue), weights before activations
+    const bool w_after = j == 0 ? nws > 1 : ((k - 2) & 3) == 0 && (k - 2) / 4 + 2 < nws;
+    const bool a_after = j + 1 < nas;
+    if (w_after) {
+      if (a_after)
+        gemm_wait_vm<S::WPW + S::APW>();
+      else
+        gemm_wait_vm<S::WPW>();
+    } else {
+      if (a_after)
+        gemm_wait_vm<S::APW>();
+      else
+        gemm_wait_vm<0>();
+    }
+    gemm_barrier();
+    if ((k & 3) == 0 && k / 4 + 2 < nws) issue_w(k / 4 + 2);
+    if (j + 2 < nas) issue_a(j + 2);
+    const uint8_t* qs = L.q[j % S::RING];
+    const uint8_t* ws = L.w[(k / 4) % S::RING];
+    step(qs, ws, k, last);
+    __builtin_amdgcn_sched_barrier(0);  // one step's operands in registers at a time
+    if (k + 1 < nks) step(qs, ws, k + 1, last);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int j = 0; j + 1 < nas; ++j) stage(j, std::false_type{});
+  stage(nas - 1, std::true_type{});
+
+  // epilogue: lane holds tokens tok0 + tbase + 16t + 4g + v of row row0 +
+  // rbase + 16b + r; token by token, as in gemm_tile.  (The lane's row and
+  // token offsets are taken here, where the compiler cannot lift the
+  // addresses derived from them above the loop and hold them through it.)
+  const bool partial = SPLIT && (flags & kSegPartial) != 0;
+  const bool zpoint = !partial || (flags & kSegZeroPoint) != 0;
+  int rl0 = rbase + r, ml0 = tbase + 4 * g;
+  asm volatile("" : "+v"(rl0), "+v"(ml0));
+#pragma unroll
+  for (int t = 0; t < S::WT; ++t) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int ml = ml0 + 16 * t + v;
+      const int m = tok0 + ml;
+      if (m >= M) continue;
+      const int32_t zz = zpoint ? L.z[ml] : 0;
+      const float sa = L.s_act[ml];
+      const int64_t o0 = (int64_t)m * a.ldy + row0 + rl0;
+#pragma unroll
+      for (int b = 0; b < S::WR; ++b) {
+        const int rl = rl0 + 16 * b;
+        if (row0 + rl >= N) continue;
+        const int32_t accv = (int32_t)((uint32_t)acc[b][t][v] - (uint32_t)zz * (uint32_t)L.rowsum[rl]);
+        const int64_t o = o0 + 16 * b;
+        if (partial) {
+          __hip_atomic_fetch_add((int32_t __attribute__((address_space(1)))*)(reinterpret_cast<int32_t*>(a.y) + o),
+                                 accv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          store_g(a.y + o, epilogue(L.s_row[rl], accv, sa));
+          if (a.acc) store_g(a.acc + o, accv);
+        }
+      }
+    }
+  }
+  gemm_barrier();
+}
+
 // Tiles tile0, tile0 + tstride, ... below tile1 of a linear, numbered in
 // (row tile, token tile) order: tile = row_tile * token_tiles + token_tile,
 // so the token tiles of one row tile are adjacent.
+template <int BM>
+struct GemmTile {
+  using Shape = GemmShape<BM>;
+  using Tiles = GemmTiles<BM>;
+};
+template <>
+struct GemmTile<128> {
+  using Shape = LineShape;
+  using Tiles = LineTiles;
+};
+
 template <int BM, bool SPLIT>
 __device__ __forceinline__ void gemm_range(const LinearArgs& a, int tile0, int tile1, int tstride,
-                                           int lane, int w, GemmTiles<BM>& L, int flags) {
+                                           int lane, int w, typename GemmTile<BM>::Tiles& L, int flags) {
   const int ntok = (int)(((int64_t)a.M + BM - 1) / BM);
+  constexpr int ROWS = GemmTile<BM>::Shape::ROWS;
   for (int tile = tile0; tile < tile1; tile += tstride) {
     const int rt = tile / ntok, tt = tile - rt * ntok;
-    gemm_tile<BM, SPLIT>(a, rt * GemmShape<BM>::ROWS, tt * BM, lane, w, L, flags);
+    if constexpr (BM == 128)
+      gemm_tile_lines<SPLIT>(a, rt * ROWS, tt * BM, lane, w, L, flags);
+    else
+      gemm_tile<BM, SPLIT>(a, rt * ROWS, tt * BM, lane, w, L, flags);
   }
 }
 
@@ -308,21 +570,28 @@ __device__ __forceinline__ int gemm_xcd_block() {
 }
 
 template <int BM>
-__global__ __launch_bounds__(64 * GemmShape<BM>::WAVES) __attribute__((amdgpu_waves_per_eu(BM == 128 ? 2 : 4)))
+__global__ __launch_bounds__(64 * GemmTile<BM>::Shape::WAVES) __attribute__((amdgpu_waves_per_eu(BM == 128 ? 2 : 4)))
 void gemm_linear_kernel(LinearArgs a) {
-  __shared__ __attribute__((aligned(16))) GemmTiles<BM> L;
-  constexpr int ROWS = GemmShape<BM>::ROWS;
+  __shared__ __attribute__((aligned(16))) typename GemmTile<BM>::Tiles L;
+  constexpr int ROWS = GemmTile<BM>::Shape::ROWS;
   const int ntiles = (int)((((int64_t)a.N + ROWS - 1) / ROWS) * (((int64_t)a.M + BM - 1) / BM));
   gemm_range<BM, false>(a, gemm_xcd_block(), ntiles, gridDim.x, threadIdx.x & 63, gemm_wave_id(), L, 0);
 }
 
 template <int BM, bool SPLIT>
-__global__ __launch_bounds__(64 * GemmShape<BM>::WAVES) __attribute__((amdgpu_waves_per_eu(BM == 128 ? 2 : 4)))
+__global__ __launch_bounds__(64 * GemmTile<BM>::Shape::WAVES) __attribute__((amdgpu_waves_per_eu(BM == 128 ? 2 : 4)))
 void gemm_stack_kernel(const StackHeader* __restrict__ h,
                                   StackSync* __restrict__ sy) {
-  __shared__ __attribute__((aligned(16))) GemmTiles<BM> L;
-  __shared__ PrologueLds prol;
-  const uint32_t launch1 = stack_prologue(h, sy, prol);
+  // one LDS object: with two, the compiler tags every LDS access with its
+  // object's alias scope and then makes the first LDS read after a tile DMA
+  // wait for that DMA (the tag says "may alias"), which drained the rings
+  struct Lds {
+    typename GemmTile<BM>::Tiles tiles;
+    PrologueLds prol;
+  };
+  __shared__ __attribute__((aligned(16))) Lds lds;
+  auto& L = lds.tiles;
+  const uint32_t launch1 = stack_prologue(h, sy, lds.prol);
   const int worker = gemm_xcd_block();
   if (worker >= h->workers) return;  // the same for the whole workgroup
   const int lane = threadIdx.x & 63;
@@ -350,9 +619,9 @@ static hipError_t with_gemm_stack_kernel(int bm, bool split, F&& f) {
 
 int gemm_tile_tokens(int32_t M) { return M > 64 ? 128 : 64; }
 
-int gemm_unit_rows(int bm) { return bm == 128 ? GemmShape<128>::ROWS : GemmShape<64>::ROWS; }
+int gemm_unit_rows(int bm) { return bm == 128 ? LineShape::ROWS : GemmShape<64>::ROWS; }
 
-static int gemm_block(int bm) { return 64 * (bm == 128 ? GemmShape<128>::WAVES : GemmShape<64>::WAVES); }
+static int gemm_block(int bm) { return 64 * (bm == 128 ? LineShape::WAVES : GemmShape<64>::WAVES); }
 
 hipError_t launch_gemm_linear(const LinearArgs& a, hipStream_t s) {
   const int bm = gemm_tile_tokens(a.M);
