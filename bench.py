@@ -100,8 +100,8 @@ def kernel_name(plan) -> str:
         return "mfma_win_stack_kernel<false, true>"
     if v == 13:
         return "mfma_win16_stack_kernel<false, true>"
-    if v in (9, 10):
-        return "gemm_stack_kernel<%d>" % (64 if v == 9 else 128)
+    if v in (9, 10, 14):
+        return {9: "gemm_stack_kernel<64, 128>", 10: "gemm_stack_kernel<128, 512>", 14: "gemm_stack_kernel<128, 256>"}[v]
     if v == 11:
         return "mfma_win16_stack_kernel<false>"
     ragged = "true" if v & 2 else "false"

@@ -255,7 +255,7 @@ int tern_gemm_smallM(const uint8_t* packed, const float* s_row, const int32_t* r
   if (N == 0 || M == 0) return TERN_OK;
   const LinearArgs a = make_args(packed, s_row, rowsum, N, K, M, q, ldq, s_act, z, y, ldy, acc);
   const hipError_t e = p == TERN_PATH_VALU ? launch_valu_linear(a, stream)
-                                           : launch_mfma_linear(a, stream);
+                                           : launch_mfma_linear(a, device_cus(), stream);
   return e == hipSuccess ? TERN_OK : hip_fail(e);
 }
 
@@ -565,6 +565,14 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
       gm = std::max(gm, (double)std::min<int64_t>(unit, d.N) * ld + 256.0);
     }
     if (gm > kSplitRatio * tot / workers_v) kernel = (int32_t)SK_MFMA + mfma_gemm_variant((int32_t)M);
+  }
+  // the prefill GEMM's row tile: 512 rows for stacks of a few such tiles per
+  // CU or more, else 256
+  if (p == TERN_PATH_MFMA) {
+    int64_t tiles512 = 0;
+    for (int64_t i = 0; i < L; ++i)
+      if (descs[i].N > 0) tiles512 += (descs[i].N + 511) / 512 * ((M + 127) / 128);
+    kernel = (int32_t)SK_MFMA + mfma_gemm_refine(kernel - SK_MFMA, (int32_t)M, tiles512, cus);
   }
   int per_cu = p == TERN_PATH_VALU ? valu_stack_blocks_per_cu(kernel) : mfma_per_cu(kernel - SK_MFMA);
   per_cu = std::min(per_cu, kMaxWavesPerCu / kWavesPerBlock);

@@ -74,18 +74,22 @@ struct GemmShape {
   static_assert(PER * (STAGES - 2 * SS) < 64 && STAGES % SS == 0, "vmcnt field");
 };
 
-// The 128-token tile: 512 rows x 128 tokens, eight waves of 64 rows x 128
-// tokens (two waves per SIMD; the decode of one weight dword serves eight
-// MFMAs).  Its operands are staged in runs of whole cache lines: a weight
+// The 128-token tiles: ROWS = 512 or 256 rows x 128 tokens, eight waves of
+// ROWS / 8 rows x 128 tokens (two waves per SIMD; the decode of one weight
+// dword serves eight MFMAs).  512-row tiles read each activation tile half
+// as often; 256-row tiles give a stack twice as many, for stacks too small
+// to fill the chip evenly with the larger ones (one 8B layer at M = 512:
+// 304 of them for 256 workgroups).  Their operands are staged in runs of whole cache lines: a weight
 // stage holds WS = 4 K-steps of every row (64 contiguous bytes), an
 // activation stage AS = 2 K-steps of every token (128 bytes), each in a ring
 // of RING stages.  Staged one K-step at a time, every row's 16 bytes and
 // every token's 64 were an L2 request of their own (640 per step for four 8B
 // layers at M = 512), and the requests in flight per CU, not bytes or MFMAs,
 // set the pace.
+template <int ROWS_>
 struct LineShape {
-  static constexpr int ROWS = 512, BM = 128, WAVES = 8;
-  static constexpr int RGROUPS = 8, WR = 4, WT = 8;  // wave grid 8 x 1
+  static constexpr int ROWS = ROWS_, BM = 128, WAVES = 8;
+  static constexpr int RGROUPS = 8, WR = ROWS / 128, WT = 8;  // wave grid 8 x 1
   static constexpr int WS = 4, AS = 2, RING = 3;
   static constexpr int WPW = ROWS * 16 * WS / 1024 / WAVES;  // weight DMA instructions per wave per stage
   static constexpr int APW = BM * 64 * AS / 1024 / WAVES;    // activation DMA instructions per wave per stage
@@ -96,8 +100,9 @@ struct LineShape {
   static_assert(WPW + APW < 64, "vmcnt field");
 };
 
+template <int ROWS>
 struct LineTiles {
-  using S = LineShape;
+  using S = LineShape<ROWS>;
   uint8_t q[S::RING][S::BM * 64 * S::AS];    // [stage][token][8 pieces of 16 B], swizzled
   uint8_t w[S::RING][S::ROWS * 16 * S::WS];  // [stage][row][4 chunks of 16 B], swizzled
   int32_t rowsum[S::ROWS];
@@ -329,7 +334,7 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
 __device__ __forceinline__ int line_fa(int t) { return ((t >> 1) & 7) ^ ((t & 1) << 2); }
 __device__ __forceinline__ int line_fw(int rho) { return ((rho >> 1) & 3) ^ ((rho >> 2) & 3); }
 
-// One 512 x 128 tile over all of K (see LineShape): rows row0.., tokens
+// One ROWS x 128 tile over all of K (see LineShape): rows row0.., tokens
 // tok0..; SPLIT and flags as for gemm_tile.
 //  * Weight stage J (K-steps 4J .. 4J+3) and activation stage j (K-steps 2j,
 //    2j+1) live in ring slots J % 3 and j % 3.  At the boundary of K-step
@@ -345,10 +350,10 @@ __device__ __forceinline__ int line_fw(int rho) { return ((rho >> 1) & 3) ^ ((rh
 //    Chunks past the row's last are read at the last (never used), pieces
 //    past ldq at the row's last 16 bytes (they meet zero weights or are
 //    masked), rows past N and tokens past M at the last one (never stored).
-template <bool SPLIT>
+template <int ROWS, bool SPLIT>
 __device__ __forceinline__ void gemm_tile_lines(const LinearArgs& a, int row0, int tok0, int lane, int w,
-                                                LineTiles& L, int flags) {
-  using S = LineShape;
+                                                LineTiles<ROWS>& L, int flags) {
+  using S = LineShape<ROWS>;
   const int r = lane & 15, g = lane >> 4;
   const int K = a.K, M = a.M, N = a.N;
   const int nks = a.nch;
@@ -536,29 +541,32 @@ __device__ __forceinline__ void gemm_tile_lines(const LinearArgs& a, int row0, i
   gemm_barrier();
 }
 
+// Tile kinds: BM = 64 with 128 rows (gemm_tile), BM = 128 with 256 or 512
+// rows (gemm_tile_lines).
+template <int BM, int ROWS>
+struct GemmTile;
+template <>
+struct GemmTile<64, 128> {
+  using Shape = GemmShape<64>;
+  using Tiles = GemmTiles<64>;
+};
+template <int ROWS>
+struct GemmTile<128, ROWS> {
+  using Shape = LineShape<ROWS>;
+  using Tiles = LineTiles<ROWS>;
+};
+
 // Tiles tile0, tile0 + tstride, ... below tile1 of a linear, numbered in
 // (row tile, token tile) order: tile = row_tile * token_tiles + token_tile,
 // so the token tiles of one row tile are adjacent.
-template <int BM>
-struct GemmTile {
-  using Shape = GemmShape<BM>;
-  using Tiles = GemmTiles<BM>;
-};
-template <>
-struct GemmTile<128> {
-  using Shape = LineShape;
-  using Tiles = LineTiles;
-};
-
-template <int BM, bool SPLIT>
+template <int BM, int ROWS, bool SPLIT>
 __device__ __forceinline__ void gemm_range(const LinearArgs& a, int tile0, int tile1, int tstride,
-                                           int lane, int w, typename GemmTile<BM>::Tiles& L, int flags) {
+                                           int lane, int w, typename GemmTile<BM, ROWS>::Tiles& L, int flags) {
   const int ntok = (int)(((int64_t)a.M + BM - 1) / BM);
-  constexpr int ROWS = GemmTile<BM>::Shape::ROWS;
   for (int tile = tile0; tile < tile1; tile += tstride) {
     const int rt = tile / ntok, tt = tile - rt * ntok;
     if constexpr (BM == 128)
-      gemm_tile_lines<SPLIT>(a, rt * ROWS, tt * BM, lane, w, L, flags);
+      gemm_tile_lines<ROWS, SPLIT>(a, rt * ROWS, tt * BM, lane, w, L, flags);
     else
       gemm_tile<BM, SPLIT>(a, rt * ROWS, tt * BM, lane, w, L, flags);
   }
@@ -569,24 +577,23 @@ __device__ __forceinline__ int gemm_xcd_block() {
   return (n % 8 == 0) ? (b % 8) * (n / 8) + b / 8 : b;
 }
 
-template <int BM>
-__global__ __launch_bounds__(64 * GemmTile<BM>::Shape::WAVES) __attribute__((amdgpu_waves_per_eu(BM == 128 ? 2 : 4)))
+template <int BM, int ROWS>
+__global__ __launch_bounds__((64 * GemmTile<BM, ROWS>::Shape::WAVES)) __attribute__((amdgpu_waves_per_eu(BM == 128 ? 2 : 4)))
 void gemm_linear_kernel(LinearArgs a) {
-  __shared__ __attribute__((aligned(16))) typename GemmTile<BM>::Tiles L;
-  constexpr int ROWS = GemmTile<BM>::Shape::ROWS;
+  __shared__ __attribute__((aligned(16))) typename GemmTile<BM, ROWS>::Tiles L;
   const int ntiles = (int)((((int64_t)a.N + ROWS - 1) / ROWS) * (((int64_t)a.M + BM - 1) / BM));
-  gemm_range<BM, false>(a, gemm_xcd_block(), ntiles, gridDim.x, threadIdx.x & 63, gemm_wave_id(), L, 0);
+  gemm_range<BM, ROWS, false>(a, gemm_xcd_block(), ntiles, gridDim.x, threadIdx.x & 63, gemm_wave_id(), L, 0);
 }
 
-template <int BM, bool SPLIT>
-__global__ __launch_bounds__(64 * GemmTile<BM>::Shape::WAVES) __attribute__((amdgpu_waves_per_eu(BM == 128 ? 2 : 4)))
+template <int BM, int ROWS, bool SPLIT>
+__global__ __launch_bounds__((64 * GemmTile<BM, ROWS>::Shape::WAVES)) __attribute__((amdgpu_waves_per_eu(BM == 128 ? 2 : 4)))
 void gemm_stack_kernel(const StackHeader* __restrict__ h,
                                   StackSync* __restrict__ sy) {
   // one LDS object: with two, the compiler tags every LDS access with its
   // object's alias scope and then makes the first LDS read after a tile DMA
   // wait for that DMA (the tag says "may alias"), which drained the rings
   struct Lds {
-    typename GemmTile<BM>::Tiles tiles;
+    typename GemmTile<BM, ROWS>::Tiles tiles;
     PrologueLds prol;
   };
   __shared__ __attribute__((aligned(16))) Lds lds;
@@ -605,56 +612,82 @@ void gemm_stack_kernel(const StackHeader* __restrict__ h,
   for (int s = seg_start[worker]; s < s1; ++s) {
     const Segment sg = seg[s];
     const LinearArgs a = lin[sg.lin];
-    gemm_range<BM, SPLIT>(a, sg.row_begin, sg.row_end, 1, lane, w, L, SPLIT ? sg.flags : 0);
+    gemm_range<BM, ROWS, SPLIT>(a, sg.row_begin, sg.row_end, 1, lane, w, L, SPLIT ? sg.flags : 0);
   }
 }
 
+// kind 0: 128 rows x 64 tokens; 1: 256 x 128; 2: 512 x 128
 template <typename F>
-static hipError_t with_gemm_stack_kernel(int bm, bool split, F&& f) {
-  if (split) return bm == 128 ? f(gemm_stack_kernel<128, true>) : f(gemm_stack_kernel<64, true>);
-  return bm == 128 ? f(gemm_stack_kernel<128, false>) : f(gemm_stack_kernel<64, false>);
+static hipError_t with_gemm_stack_kernel(int kind, bool split, F&& f) {
+  if (split) {
+    if (kind == 2) return f(gemm_stack_kernel<128, 512, true>);
+    if (kind == 1) return f(gemm_stack_kernel<128, 256, true>);
+    return f(gemm_stack_kernel<64, 128, true>);
+  }
+  if (kind == 2) return f(gemm_stack_kernel<128, 512, false>);
+  if (kind == 1) return f(gemm_stack_kernel<128, 256, false>);
+  return f(gemm_stack_kernel<64, 128, false>);
 }
+
+template <typename F>
+static hipError_t with_gemm_linear_kernel(int kind, F&& f) {
+  if (kind == 2) return f(gemm_linear_kernel<128, 512>);
+  if (kind == 1) return f(gemm_linear_kernel<128, 256>);
+  return f(gemm_linear_kernel<64, 128>);
+}
+
+// A stack (or one linear) with fewer than this many 512-row tiles per CU
+// takes 256-row tiles: with the larger ones its last tiles leave most of
+// the chip idle (one 8B layer at M = 512: 166 -> 116 us; four layers, 1,216
+// tiles: 447 -> 417 us the other way).
+constexpr int64_t kBigTilesPerCu = 3;
 
 }  // namespace
 
 int gemm_tile_tokens(int32_t M) { return M > 64 ? 128 : 64; }
 
-int gemm_unit_rows(int bm) { return bm == 128 ? LineShape::ROWS : GemmShape<64>::ROWS; }
-
-static int gemm_block(int bm) { return 64 * (bm == 128 ? LineShape::WAVES : GemmShape<64>::WAVES); }
-
-hipError_t launch_gemm_linear(const LinearArgs& a, hipStream_t s) {
-  const int bm = gemm_tile_tokens(a.M);
-  const int rows = gemm_unit_rows(bm);
-  const int64_t tiles = (((int64_t)a.N + rows - 1) / rows) * (((int64_t)a.M + bm - 1) / bm);
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(tiles, 65535));
-  const dim3 grid((unsigned)blocks), block(gemm_block(bm));
-  if (bm == 128)
-    hipLaunchKernelGGL(gemm_linear_kernel<128>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(gemm_linear_kernel<64>, grid, block, 0, s, a);
-  return hipGetLastError();
+int gemm_kind(int32_t M, int64_t tiles512, int cus) {
+  if (gemm_tile_tokens(M) == 64) return 0;
+  return tiles512 >= kBigTilesPerCu * (int64_t)cus ? 2 : 1;
 }
 
-hipError_t launch_gemm_stack(int bm, const void* ws, const LaunchShape& shp, hipStream_t s) {
+int gemm_kind_rows(int kind) { return kind == 2 ? 512 : kind == 1 ? 256 : GemmShape<64>::ROWS; }
+
+int gemm_kind_tokens(int kind) { return kind == 0 ? 64 : 128; }
+
+static int gemm_block(int kind) { return 64 * (kind == 0 ? GemmShape<64>::WAVES : LineShape<512>::WAVES); }
+
+hipError_t launch_gemm_linear(const LinearArgs& a, int cus, hipStream_t s) {
+  const int64_t ntok = ((int64_t)a.M + 127) / 128;
+  const int kind = gemm_kind(a.M, (((int64_t)a.N + 511) / 512) * ntok, cus);
+  const int rows = gemm_kind_rows(kind), bm = gemm_kind_tokens(kind);
+  const int64_t tiles = (((int64_t)a.N + rows - 1) / rows) * (((int64_t)a.M + bm - 1) / bm);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(tiles, 65535));
+  return with_gemm_linear_kernel(kind, [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(gemm_block(kind)), 0, s, a);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_gemm_stack(int kind, const void* ws, const LaunchShape& shp, hipStream_t s) {
   const StackHeader* h = static_cast<const StackHeader*>(ws);
   const bool split = shp.splits > 0;
   if (split) {
     const hipError_t e = launch_split_clear(ws, shp, s);
     if (e != hipSuccess) return e;
   }
-  const hipError_t e = with_gemm_stack_kernel(bm, split, [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(shp.grid), dim3(gemm_block(bm)), 0, s, h, stack_sync(ws));
+  const hipError_t e = with_gemm_stack_kernel(kind, split, [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(shp.grid), dim3(gemm_block(kind)), 0, s, h, stack_sync(ws));
     return hipGetLastError();
   });
   if (e != hipSuccess || !split) return e;
   return launch_split_finish(ws, shp, s);
 }
 
-int gemm_stack_blocks_per_cu(int bm) {
+int gemm_stack_blocks_per_cu(int kind) {
   int n = 0;
-  const hipError_t e = with_gemm_stack_kernel(bm, false, [&](auto kern) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, gemm_block(bm), 0);
+  const hipError_t e = with_gemm_stack_kernel(kind, false, [&](auto kern) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, gemm_block(kind), 0);
   });
   if (e != hipSuccess || n < 1) n = 1;
   return n;

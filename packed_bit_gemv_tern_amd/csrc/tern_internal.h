@@ -170,8 +170,9 @@ hipError_t launch_validate(const uint8_t* packed, int64_t N, int64_t K, int32_t*
 
 // VALU path for one linear, M in {1, 2, 4} token registers (M <= 4).
 hipError_t launch_valu_linear(const LinearArgs& a, hipStream_t s);
-// MFMA path for one linear, any M.
-hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s);
+// MFMA path for one linear, any M (cus: compute units of the device, for
+// the prefill GEMM's choice of tile).
+hipError_t launch_mfma_linear(const LinearArgs& a, int cus, hipStream_t s);
 
 // Rows handled per work unit (schedule granularity) of each path.
 int valu_unit_rows(int32_t variant, int32_t M);
@@ -203,6 +204,9 @@ bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy);
 // the prefill GEMM's variant for M tokens (any M >= 1, any K), and whether
 // `variant` is the lockstep kernel (a workgroup takes whole rows over all K)
 int32_t mfma_gemm_variant(int32_t M);
+// the prefill GEMM variant for a stack of tiles512 512 x 128 tiles (variant
+// unchanged if it is not the prefill GEMM's)
+int32_t mfma_gemm_refine(int32_t variant, int32_t M, int64_t tiles512, int cus);
 bool mfma_is_lockstep(int32_t variant);
 // the activation-window kernel: is `variant` it, and its window width in K
 bool mfma_is_window(int32_t variant);
@@ -216,13 +220,17 @@ bool mfma_can_split(int32_t variant);
 hipError_t launch_split_clear(const void* ws, const LaunchShape& shp, hipStream_t s);
 hipError_t launch_split_finish(const void* ws, const LaunchShape& shp, hipStream_t s);
 
-// Prefill GEMM (M > 16; tern_gemm.hip): tiles of gemm_unit_rows(bm) rows x
-// bm = gemm_tile_tokens(M) tokens, one workgroup per tile.
+// Prefill GEMM (M > 16; tern_gemm.hip): one workgroup per tile of
+// gemm_kind_rows(kind) rows x gemm_kind_tokens(kind) tokens.  Kind 0: 128 x
+// 64 (M <= 64); 1: 256 x 128; 2: 512 x 128, for work of at least a few of
+// its tiles per CU (tiles512: the work's tile count at 512 x 128).
 int gemm_tile_tokens(int32_t M);
-int gemm_unit_rows(int bm);
-hipError_t launch_gemm_linear(const LinearArgs& a, hipStream_t s);
-hipError_t launch_gemm_stack(int bm, const void* ws, const LaunchShape& shp, hipStream_t s);
-int gemm_stack_blocks_per_cu(int bm);
+int gemm_kind(int32_t M, int64_t tiles512, int cus);
+int gemm_kind_rows(int kind);
+int gemm_kind_tokens(int kind);
+hipError_t launch_gemm_linear(const LinearArgs& a, int cus, hipStream_t s);
+hipError_t launch_gemm_stack(int kind, const void* ws, const LaunchShape& shp, hipStream_t s);
+int gemm_stack_blocks_per_cu(int kind);
 // token tiles of the prefill GEMM per row unit (its schedule counts tiles);
 // 0 for every other kernel (its schedule counts rows)
 int32_t mfma_token_tiles(int32_t variant, int32_t M);

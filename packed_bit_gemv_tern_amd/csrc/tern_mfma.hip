@@ -1051,15 +1051,21 @@ __global__ __launch_bounds__(kSplitBlock) void split_finish_kernel(const StackHe
 
 // Kernel selector of the MFMA path: bit 1 = ragged K compiled in, bit 2 =
 // 9 <= M <= 16 (16 activation rows) for the lockstep workgroup kernel;
-// 8 = the activation-window kernel (M <= 8, no ragged K); 9 and 10 = the
-// prefill GEMM (M > 16) with 64- and 128-token tiles.
+// 8 = the activation-window kernel (M <= 8, no ragged K); 9, 14 and 10 = the
+// prefill GEMM (M > 16) with tiles of 128 x 64, 256 x 128 and 512 x 128.
 constexpr int32_t kWinVariant = 8;
 constexpr int32_t kGemm64Variant = 9;
 constexpr int32_t kGemm128Variant = 10;
+constexpr int32_t kGemm128sVariant = 14;
 constexpr int32_t kWin16Variant = 11;  // the window kernel for 9 <= M <= 16
 // the window kernels compiled for stacks with block scales
 constexpr int32_t kWinBlkVariant = 12;
 constexpr int32_t kWin16BlkVariant = 13;
+
+static bool is_gemm(int32_t v) { return v == kGemm64Variant || v == kGemm128Variant || v == kGemm128sVariant; }
+
+// tile kind of a prefill GEMM variant (gemm_kind_rows)
+static int gemm_kind_of(int32_t v) { return v == kGemm128Variant ? 2 : v == kGemm128sVariant ? 1 : 0; }
 
 bool mfma_win_offsets_fit(int64_t N, int64_t ld, int64_t M, int64_t ldy) {
   // weight row offsets and output byte offsets are 32-bit in that kernel
@@ -1074,7 +1080,7 @@ bool mfma_is_window(int32_t variant) {
 // (the 16-token window kernel never splits: stacks small enough to want it
 // take the prefill GEMM at 9..16 tokens)
 bool mfma_can_split(int32_t variant) {
-  return variant == kWinVariant || variant == kGemm64Variant || variant == kGemm128Variant;
+  return variant == kWinVariant || is_gemm(variant);
 }
 
 hipError_t launch_split_clear(const void* ws, const LaunchShape& shp, hipStream_t s) {
@@ -1097,6 +1103,11 @@ int32_t mfma_gemm_variant(int32_t M) {
   return gemm_tile_tokens(M) == 128 ? kGemm128Variant : kGemm64Variant;
 }
 
+int32_t mfma_gemm_refine(int32_t variant, int32_t M, int64_t tiles512, int cus) {
+  if (variant != kGemm128Variant && variant != kGemm128sVariant) return variant;
+  return gemm_kind(M, tiles512, cus) == 2 ? kGemm128Variant : kGemm128sVariant;
+}
+
 bool mfma_is_lockstep(int32_t variant) { return variant >= 0 && variant < kWinVariant; }
 
 int32_t mfma_stack_variant(int32_t M, bool ragged, bool big, bool blocked) {
@@ -1107,8 +1118,8 @@ int32_t mfma_stack_variant(int32_t M, bool ragged, bool big, bool blocked) {
 }
 
 int32_t mfma_token_tiles(int32_t variant, int32_t M) {
-  if (variant != kGemm64Variant && variant != kGemm128Variant) return 0;
-  const int bm = variant == kGemm128Variant ? 128 : 64;
+  if (!is_gemm(variant)) return 0;
+  const int bm = gemm_kind_tokens(gemm_kind_of(variant));
   return (int32_t)(((int64_t)M + bm - 1) / bm);
 }
 
@@ -1117,8 +1128,7 @@ bool mfma_per_workgroup(int32_t) { return true; }
 int mfma_unit_rows(int32_t variant) {
   if (variant == kWinVariant || variant == kWinBlkVariant) return kWinRows;
   if (variant == kWin16Variant || variant == kWin16BlkVariant) return WinGeo<16>::ROWS;
-  if (variant == kGemm64Variant || variant == kGemm128Variant)
-    return gemm_unit_rows(variant == kGemm128Variant ? 128 : 64);
+  if (is_gemm(variant)) return gemm_kind_rows(gemm_kind_of(variant));
   return kWgRows;
 }
 
@@ -1155,9 +1165,9 @@ static hipError_t with_mfma_stack_kernel(int32_t variant, F&& f) {
   }
 }
 
-hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
+hipError_t launch_mfma_linear(const LinearArgs& a, int cus, hipStream_t s) {
   int32_t v = mfma_stack_variant(a.M, (a.K & 63) != 0, !mfma_win_offsets_fit(a.N, a.ld, a.M, a.ldy), false);
-  if (v == kGemm64Variant || v == kGemm128Variant) return launch_gemm_linear(a, s);
+  if (is_gemm(v)) return launch_gemm_linear(a, cus, s);
   if (v == kWin16Variant) v = 4;  // one linear at 9..16 tokens: the lockstep kernel
   const int64_t units = (a.N + mfma_unit_rows(v) - 1) / mfma_unit_rows(v);
   int64_t blocks = units;
@@ -1176,8 +1186,7 @@ hipError_t launch_mfma_linear(const LinearArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape& shp, hipStream_t s) {
-  if (variant == kGemm64Variant || variant == kGemm128Variant)
-    return launch_gemm_stack(variant == kGemm128Variant ? 128 : 64, ws, shp, s);
+  if (is_gemm(variant)) return launch_gemm_stack(gemm_kind_of(variant), ws, shp, s);
   const StackHeader* h = static_cast<const StackHeader*>(ws);
   const dim3 grid(shp.grid), block(variant == kWinVariant || variant == kWinBlkVariant       ? kWinBlock
                                     : variant == kWin16Variant || variant == kWin16BlkVariant ? WinGeo<16>::BLOCK
@@ -1202,8 +1211,7 @@ hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape&
 }
 
 int mfma_stack_blocks_per_cu(int32_t variant) {
-  if (variant == kGemm64Variant || variant == kGemm128Variant)
-    return gemm_stack_blocks_per_cu(variant == kGemm128Variant ? 128 : 64);
+  if (is_gemm(variant)) return gemm_stack_blocks_per_cu(gemm_kind_of(variant));
   int n = 0;
   const int block = variant == kWinVariant || variant == kWinBlkVariant       ? kWinBlock
                     : variant == kWin16Variant || variant == kWin16BlkVariant ? WinGeo<16>::BLOCK

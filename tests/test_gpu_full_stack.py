@@ -105,16 +105,8 @@ def layer8b():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.timeout(300)
-@pytest.mark.parametrize("M", [16, 64, 512])
-def test_8b_layer_prefill_sampled(layer8b, M):
-    """One 8B layer as one stack launch at prefill M (the configuration the
-    prefill sweep times): sampled rows of every linear against the oracle."""
-    b = layer8b.bind(M, with_acc=True)
-    b.run()
-    b.run()
-    torch.cuda.synchronize()
-    for i, pl in enumerate(layer8b.linears):
+def _check_sampled(st, b, M):
+    for i, pl in enumerate(st.linears):
         rows = pl.sample_rows
         q, s_act, z = b.host_act[i]
         rp, rr, bad = oracle.pack(pl.sample_w)
@@ -124,3 +116,40 @@ def test_8b_layer_prefill_sampled(layer8b, M):
         assert np.array_equal(acc, racc), (pl.name, M)
         assert np.all(np.abs(y.astype(np.float64) - ry64) <= RTOL * np.abs(ry64)), (pl.name, M)
         assert np.array_equal(y.view(np.uint32), ry32.view(np.uint32)), (pl.name, M)
+
+
+# prefill GEMM variants: 9 = 128 x 64 tiles, 14 = 256 x 128, 10 = 512 x 128
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("M,kernel", [(16, 16 + 9), (64, 16 + 9), (512, 16 + 14)])
+def test_8b_layer_prefill_sampled(layer8b, M, kernel):
+    """One 8B layer as one stack launch at prefill M (the configuration the
+    prefill sweep times): sampled rows of every linear against the oracle."""
+    b = layer8b.bind(M, with_acc=True)
+    assert b.plan.kernel == kernel, (M, b.plan.kernel)
+    b.run()
+    b.run()
+    torch.cuda.synchronize()
+    _check_sampled(layer8b, b, M)
+
+
+@pytest.fixture(scope="module")
+def layers8b4():
+    from packed_bit_gemv_tern_amd.stack import DeviceStack
+    st = DeviceStack("8b", layers=4, seed=3, threads=16, sample_rows=48)
+    yield st
+    del st
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("M", [512, 300])
+def test_8b_four_layers_prefill_sampled(layers8b4, M):
+    """Four 8B layers (28 linears) as one launch at M = 512 (the profiled
+    prefill workload) and at a ragged M = 300: enough tiles for the 512-row
+    GEMM tile; sampled rows of every linear against the oracle."""
+    b = layers8b4.bind(M, with_acc=True)
+    assert b.plan.kernel == 16 + 10 and b.plan.splits == 0, (M, b.plan.kernel, b.plan.splits)
+    b.run()
+    b.run()
+    torch.cuda.synchronize()
+    _check_sampled(layers8b4, b, M)

@@ -160,7 +160,7 @@ CASES = [
      lambda k: k == 16 + 2),
     ("gemm_m12", 12, tern.TERN_PATH_AUTO, [], lambda k: k in (16 + 9, 16 + 10)),
     ("gemm_m64", 64, tern.TERN_PATH_AUTO, [], lambda k: k == 16 + 9),
-    ("gemm_m200", 200, tern.TERN_PATH_AUTO, [], lambda k: k == 16 + 10),
+    ("gemm_m200", 200, tern.TERN_PATH_AUTO, [], lambda k: k == 16 + 14),
 ]
 
 

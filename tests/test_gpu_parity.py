@@ -199,6 +199,17 @@ def test_gemm_prefill(M):
     assert_parity(y, acc, oracle_ref(lin), "prefill M=%d" % M)
 
 
+def test_gemm_prefill_512_row_tiles():
+    # a single call with enough 512 x 128 tiles (96 x 8 = 768, three per CU)
+    # for the 512-row tile, ragged in M
+    N, K, M = 49152, 64, 1000
+    lin = make(N, K, M, seed=11)
+    up = Uploaded(lin)
+    up.run()
+    y, acc = up.results()
+    assert_parity(y, acc, oracle_ref(lin), "prefill N=%d M=%d" % (N, M))
+
+
 def test_gemm_empty_problems():
     y = torch.full((4, 8), 5.0, device=DEV)
     dummy8 = torch.zeros(64, dtype=torch.int8, device=DEV)
