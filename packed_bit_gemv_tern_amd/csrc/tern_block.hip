@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kBlkBlock) void blocked_gemv_kernel(BlkArgs a) {
         // sum c * qb of the chunk (plane k is 4^k-scaled), then of the block
         const uint32_t sc = p[0] + (p[1] >> 2) + (p[2] >> 4) + (p[3] >> 6);
         const uint32_t sb = group_sum_int(sc, g);
-        const int32_t accb = (int32_t)(sb - qbb[t] - zb * (uint32_t)c.r[u][t]);
+        const int32_t accb = (int32_t)(sb - qbb[t] - mul_zr((int32_t)zb, c.r[u][t]));
         const int ch = lane + 64 * t;
         if ((lane & (g - 1)) == 0 && ch < a.nch) prow[u * pitch + ch / g] = __fmul_rn(c.s[u][t], (float)accb);
       }

@@ -158,6 +158,13 @@ __device__ __forceinline__ uint32_t group_sum(uint32_t x) {
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // y = (s_row * acc) * s_act with two round-to-nearest products.
+// z * rowsum (or (z + 128) * rowsum) as a full-rate 24-bit multiply: the
+// 32-bit integer multiply is a quarter-rate instruction.  The product is
+// exact while both factors fit 24 signed bits, which the call preconditions
+// give: |z| <= 255, and a row or block sum of ternary weights is at most K <=
+// TERN_MAX_K < 2^23 in magnitude.
+__device__ __forceinline__ uint32_t mul_zr(int32_t z, int32_t r) { return (uint32_t)__mul24(z, r); }
+
 __device__ __forceinline__ float epilogue(float s_row, int32_t acc, float s_act) {
   return __fmul_rn(__fmul_rn(s_row, (float)acc), s_act);
 }

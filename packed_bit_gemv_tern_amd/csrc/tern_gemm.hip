@@ -308,7 +308,7 @@ __device__ __forceinline__ void gemm_tile(const LinearArgs& a, int row0, int tok
       for (int b = 0; b < S::WR; ++b) {
         const int rl = rbase + 16 * b + r;
         if (row0 + rl >= N) continue;
-        const int32_t accv = (int32_t)((uint32_t)acc[b][t][v] - (uint32_t)zz * (uint32_t)L.rowsum[rl]);
+        const int32_t accv = (int32_t)((uint32_t)acc[b][t][v] - mul_zr(zz, L.rowsum[rl]));
         const int64_t o = o0 + 16 * b;
         if (partial) {
           __hip_atomic_fetch_add((int32_t __attribute__((address_space(1)))*)(reinterpret_cast<int32_t*>(a.y) + o),
@@ -526,7 +526,7 @@ __device__ __forceinline__ void gemm_tile_lines(const LinearArgs& a, int row0, i
       for (int b = 0; b < S::WR; ++b) {
         const int rl = rl0 + 16 * b;
         if (row0 + rl >= N) continue;
-        const int32_t accv = (int32_t)((uint32_t)acc[b][t][v] - (uint32_t)zz * (uint32_t)L.rowsum[rl]);
+        const int32_t accv = (int32_t)((uint32_t)acc[b][t][v] - mul_zr(zz, L.rowsum[rl]));
         const int64_t o = o0 + 16 * b;
         if (partial) {
           __hip_atomic_fetch_add((int32_t __attribute__((address_space(1)))*)(reinterpret_cast<int32_t*>(a.y) + o),

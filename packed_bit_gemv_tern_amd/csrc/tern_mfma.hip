@@ -205,7 +205,7 @@ __device__ __forceinline__ void mfma_wg_range(const LinearArgs& a, int row_lo, i
         const int m = 4 * g + v;
         if (m < M) {
           const int32_t accv =
-              (int32_t)((uint32_t)acc[b][v] - (uint32_t)load_g(a.z + m) * (uint32_t)rs);
+              (int32_t)((uint32_t)acc[b][v] - mul_zr(load_g(a.z + m), rs));
           const int64_t o = (int64_t)m * a.ldy + row;
           store_g(a.y + o, epilogue(sr, accv, load_g(a.s_act + m)));
           if (a.acc) store_g(a.acc + o, accv);
@@ -721,7 +721,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
             for (int k = kw << lbks; k < (kw + 1) << lbks; ++k) qb += L.blk.qpiece[m][k];
             const int32_t cq = c1 + (c4 >> 2) + (c16 >> 4);
             const int32_t accb = (int32_t)((uint32_t)cq - (uint32_t)cprev[j] - (uint32_t)qb -
-                                           (uint32_t)L.z[m] * ms[32 + 16 * b + r]);
+                                           mul_zr(L.z[m], (int32_t)ms[32 + 16 * b + r]));
             cprev[j] = cq;
             bsum[j] = add_product_rn(bsum[j], __uint_as_float(ms[16 * b + r]), (float)accb);
             bint[j] += accb;
@@ -819,14 +819,14 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int m = 4 * (g & 1) + v;
-            const int32_t accv = (int32_t)((uint32_t)cq[v] - (uint32_t)L.qsum[m] - (uint32_t)L.z[m] * (uint32_t)rsel);
+            const int32_t accv = (int32_t)((uint32_t)cq[v] - (uint32_t)L.qsum[m] - mul_zr(L.z[m], rsel));
             vals[v] = epilogue(ssel, accv, L.s_act[m]);
           }
         } else {
 #pragma unroll
           for (int j = 0; j < NV; ++j) {
             const int b = j >> 2, m = (4 * g + (j & 3)) & (T - 1);
-            const int32_t accv = (int32_t)((uint32_t)cq[j] - (uint32_t)L.qsum[m] - (uint32_t)L.z[m] * (uint32_t)rs[b]);
+            const int32_t accv = (int32_t)((uint32_t)cq[j] - (uint32_t)L.qsum[m] - mul_zr(L.z[m], rs[b]));
             vals[j] = epilogue(sr[b], accv, L.s_act[m]);
           }
         }
@@ -872,7 +872,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
           if (m < M) {
             const int32_t cq = acc1[b][v] + (acc4[b][v] >> 2) + (acc16[b][v] >> 4);  // sum(c*q)
             const int32_t accv = (int32_t)((uint32_t)cq - (uint32_t)L.qsum[m] -
-                                           (uint32_t)zt[v] * (uint32_t)rs[b]);
+                                           mul_zr(zt[v], rs[b]));
             // byte offset of (m, row) in y and acc: below 2^32 (checked by the host)
             const uint32_t off = ((uint32_t)m * (uint32_t)a.ldy + (uint32_t)row) * 4u;
             if (partial) {

@@ -315,7 +315,7 @@ __device__ __forceinline__ void valu_range_blk(const LinearArgs& a, int row_lo, 
         uint32_t p[4] = {0, 0, 0, 0};
         dot_chunk(c.w[u][t], qc[t], p);
         const uint32_t sbk = group_sum_lg(combine_exact(p), lg);
-        const int32_t accb = (int32_t)(sbk - qbb[t] - zb * (uint32_t)c.rs[u][t]);
+        const int32_t accb = (int32_t)(sbk - qbb[t] - mul_zr((int32_t)zb, c.rs[u][t]));
         const int ch = r + LPR * t;
         if (first && ch < nch) {
           const int o = (u * RPW + sub) * pitch + (ch >> lg);
