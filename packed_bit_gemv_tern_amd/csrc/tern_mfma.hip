@@ -270,15 +270,24 @@ struct WinGeo {
 };
 constexpr int kWinTile = 16 * kWinR * kStepBytes;
 
-// Block-wise scales (BLK): the block scale and row sum of a wave's 32 rows
-// for one block, by 4-byte DMA (lanes 0..31 the scales, 32..63 the row sums
-// of rows 16 (l / 16 % 2) + l % 16), in a ring of kBlkSlots per wave; and
-// each staged token's activation sum per 512-column piece of the window.
-constexpr int kBlkSlots = 4;
+// Block-wise scales (BLK): the block scales and row sums of a wave's 32 rows
+// for a group of up to kBlkGroup consecutive blocks of one window, by four
+// 4-byte DMA instructions (scales of rows 0..15, of rows 16..31, then the
+// row sums likewise; lane l: row l / 4, block l % 4 of the group, so four
+// lanes read 16 contiguous bytes of a row: one instruction touches 16 cache
+// lines where one block per instruction touched 64), in a ring of kBlkSlots
+// groups per wave: slot word 128 a + 4 row + block (a = 0 scale, 1 row sum).
+// A step issues the DMA of the tile D = 2 steps ahead before it finishes its
+// own block, so with one-step groups three are live at once;
+// and each staged token's activation sums over the window's 512-column
+// pieces (an exclusive prefix: qpre[m][k] sums pieces 0 .. k - 1).
+constexpr int kBlkGroup = 4;
+constexpr int kBlkDma = 4;  // DMA instructions per group
+constexpr int kBlkSlots = 3;
 template <int T, bool BLK>
 struct WinBlk {
-  uint32_t meta[WinGeo<T>::WAVES][kBlkSlots][64];
-  int32_t qpiece[T][8];
+  uint32_t meta[WinGeo<T>::WAVES][kBlkSlots][kBlkDma * 64];
+  int32_t qpre[T][9];
 };
 template <int T>
 struct WinBlk<T, false> {};
@@ -404,6 +413,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   constexpr int NLD = 16 * R / 8;  // 1 KB wave loads per K-step
   constexpr int ROWS = WinGeo<T>::ROWS, BLOCK = WinGeo<T>::BLOCK, WAVES = WinGeo<T>::WAVES;
   constexpr int D = WinGeo<T>::DEPTH;
+  static_assert(!BLK || kBlkSlots >= D + 1, "block metadata groups live at once");
   constexpr int NV = T / 2;  // held values per unit and lane
   static_assert(D >= 1 && D <= 3, "tile depth");
   static_assert(!BLK || D == 2, "block metadata counts assume two tiles in flight");
@@ -446,22 +456,29 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   // numbered in the order the wave consumes them, across units); with block
   // scales the block's scales and row sums go first when ks starts a block
   // (one DMA instruction, counted by the waits below)
-  // (block scales: lanes 0..31 bring the scales, 32..63 the row sums of the
-  // wave's rows; mo = the lane's row times nb, below 2^31: checked by the host)
-  const char* mptr = BLK && blk ? (lane < 32 ? reinterpret_cast<const char*>(a.s_b)
-                                             : reinterpret_cast<const char*>(a.rowsum_b))
-                                : nullptr;
-  auto unit_meta = [&](int unit) -> uint32_t {
-    if (!(BLK && blk)) return 0;
-    const int brow = min(row_lo + unit * ROWS + 16 * R * w + 16 * ((lane >> 4) & 1) + (lane & 15), row_hi - 1);
-    return (uint32_t)brow * (uint32_t)nb;
+  // (block scales: the lane's rows l / 4 and 16 + l / 4 of the wave, times
+  // nb (below 2^31: checked by the host); groups of gsz = min(4, blocks per
+  // window) blocks, aligned within the window, so a group never spans two
+  // passes of the window-major walk)
+  const int gmask = BLK && blk ? min(kBlkGroup, (kWinK / 512) >> lbks) - 1 : 0;
+  auto unit_meta = [&](int unit) -> uint2 {
+    if (!(BLK && blk)) return uint2{0u, 0u};
+    const int b0 = row_lo + unit * ROWS + 16 * R * w + (lane >> 2);
+    return uint2{(uint32_t)min(b0, row_hi - 1) * (uint32_t)nb, (uint32_t)min(b0 + 16, row_hi - 1) * (uint32_t)nb};
   };
-  auto issue = [&](const uint32_t (&src)[NLD], uint32_t mo, int ks, int t) {
+  auto issue = [&](const uint32_t (&src)[NLD], uint2 mo, int ks, int t) {
     if constexpr (BLK) {
-      if (blk && (ks & bmask) == 0) {
-        const void* msrc = mptr + 4 * (uint64_t)(mo + (uint32_t)(ks >> lbks));
-        __builtin_amdgcn_global_load_lds(msrc, (lds_ptr)&L.blk.meta[w][mb_issue][0], 4, 0, 0);
-        mb_issue = (mb_issue + 1) & (kBlkSlots - 1);
+      const int bk = ks >> lbks;
+      if (blk && (ks & bmask) == 0 && (bk & gmask) == 0) {
+        const uint32_t bi = (uint32_t)min(bk + (lane & 3), nb - 1);
+        uint32_t* dst = &L.blk.meta[w][mb_issue][0];
+#pragma unroll
+        for (int i = 0; i < kBlkDma; ++i) {
+          const char* base = i < 2 ? reinterpret_cast<const char*>(a.s_b) : reinterpret_cast<const char*>(a.rowsum_b);
+          const void* msrc = base + 4 * (uint64_t)(((i & 1) ? mo.y : mo.x) + bi);
+          __builtin_amdgcn_global_load_lds(msrc, (lds_ptr)(dst + 64 * i), 4, 0, 0);
+        }
+        mb_issue = mb_issue + 1 == kBlkSlots ? 0 : mb_issue + 1;
       }
     }
     uint8_t* tile = L.w[w][t % D];
@@ -493,7 +510,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
   // unit's (a window's, window-major) K-steps, so a lookahead reaches at
   // most into the next unit
   const int depth = min(D, nks);
-  uint32_t mo = 0;
+  uint2 mo{0u, 0u};
   if (ufirst < row_hi) {
     unit_src(unit0, src);
     mo = unit_meta(unit0);
@@ -535,7 +552,7 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
     const bool has_next = nu >= 0;
     const int nkb = wmajor ? 8 * np : 0;
     uint32_t nsrc[NLD];
-    uint32_t nmo = 0;
+    uint2 nmo{0u, 0u};
     if (has_next) unit_src(nu, nsrc), nmo = unit_meta(nu);
     int32_t rs[R];
     float sr[R];
@@ -612,7 +629,10 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
           // windows' (windows are staged in order); wave w owns tokens w,
           // w + WAVES, ... so no two waves write one entry
           for (int tq = w; tq < T; tq += WAVES) {
-            uint32_t part = 0;
+            uint32_t part = 0, run = 0;
+            if constexpr (BLK) {
+              if (lane == 0) L.blk.qpre[tq][0] = 0;
+            }
 #pragma unroll
             for (int i = 0; i < kWinK / 1024; ++i) {
               const u32x4 v = *reinterpret_cast<const u32x4*>(&L.q[tq][16 * lane + 1024 * i]);
@@ -621,9 +641,16 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
               for (int k = 0; k < 4; ++k) pi = (uint32_t)__builtin_amdgcn_sdot4((int)v[k], 0x01010101, (int)pi, false);
               part += pi;
               if constexpr (BLK) {
-                // the window's 512-column piece 2i + (lane >= 32): a half-wave sum
+                // the window's 512-column pieces 2i and 2i + 1 (half-wave
+                // sums), kept as an exclusive prefix: qpre[k] = the sum of
+                // pieces 0 .. k - 1
                 const uint32_t ph = group_sum<32>(pi);
-                if ((lane & 31) == 0) L.blk.qpiece[tq][2 * i + (lane >> 5)] = (int32_t)ph;
+                const uint32_t p0 = __builtin_amdgcn_readlane(ph, 0), p1 = __builtin_amdgcn_readlane(ph, 32);
+                if (lane == 0) {
+                  L.blk.qpre[tq][2 * i + 1] = (int32_t)(run + p0);
+                  L.blk.qpre[tq][2 * i + 2] = (int32_t)(run + p0 + p1);
+                }
+                run += p0 + p1;
               }
             }
             const int32_t tot = (int32_t)group_sum<64>(part);
@@ -648,13 +675,14 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
       // and other loads and stores in between only add to the count)
       {
         const int after = has_next ? depth - 1 : min(depth - 1, ke - 1 - ks);
-        // (the tile after this one carries its block's metadata DMA first
-        // when it starts a block)
-        const bool meta_after = BLK && blk && after == 1 && ((ks + 1 < ke ? ks + 1 : nkb) & bmask) == 0;
+        // (the tile after this one carries a block group's metadata DMA
+        // first when it starts a group)
+        const int kn = ks + 1 < ke ? ks + 1 : nkb;
+        const bool meta_after = BLK && blk && after == 1 && (kn & bmask) == 0 && ((kn >> lbks) & gmask) == 0;
         if (after >= 2)
           wait_vm<2 * NLD>();
         else if (meta_after)
-          wait_vm<NLD + 1>();
+          wait_vm<NLD + kBlkDma>();
         else if (after == 1)
           wait_vm<NLD>();
         else
@@ -707,7 +735,8 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
           // then one rounding for s_b * acc_b and one for the running sum.
           // Its metadata landed with the tile of its first step.
           const uint32_t* ms = L.blk.meta[w][mb_use];
-          mb_use = (mb_use + 1) & (kBlkSlots - 1);
+          const int bi = (ks >> lbks) & gmask;  // block within its group
+          if (bi == gmask || ks + 1 == nks) mb_use = mb_use + 1 == kBlkSlots ? 0 : mb_use + 1;
           const int kw = (ks & 7) >> lbks;  // block within the window (blocks never span windows)
 #pragma unroll
           for (int j = 0; j < NV; ++j) {
@@ -717,13 +746,12 @@ __device__ __forceinline__ void mfma_win_range(const LinearArgs& a, int row_lo, 
             const int32_t c1 = b ? acc1[1][v] : acc1[0][v];
             const int32_t c4 = b ? acc4[1][v] : acc4[0][v];
             const int32_t c16 = b ? acc16[1][v] : acc16[0][v];
-            int32_t qb = 0;
-            for (int k = kw << lbks; k < (kw + 1) << lbks; ++k) qb += L.blk.qpiece[m][k];
+            const int32_t qb = L.blk.qpre[m][(kw + 1) << lbks] - L.blk.qpre[m][kw << lbks];
             const int32_t cq = c1 + (c4 >> 2) + (c16 >> 4);
             const int32_t accb = (int32_t)((uint32_t)cq - (uint32_t)cprev[j] - (uint32_t)qb -
-                                           mul_zr(L.z[m], (int32_t)ms[32 + 16 * b + r]));
+                                           mul_zr(L.z[m], (int32_t)ms[128 + 4 * (16 * b + r) + bi]));
             cprev[j] = cq;
-            bsum[j] = add_product_rn(bsum[j], __uint_as_float(ms[16 * b + r]), (float)accb);
+            bsum[j] = add_product_rn(bsum[j], __uint_as_float(ms[4 * (16 * b + r) + bi]), (float)accb);
             bint[j] += accb;
           }
         }

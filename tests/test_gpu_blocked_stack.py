@@ -99,12 +99,14 @@ def test_blocked_stack_mixed_with_per_row_linears():
     del keep
 
 
-@pytest.mark.parametrize("B", [512, 1024, 4096])
+@pytest.mark.parametrize("B", [512, 1024, 2048, 4096])
 @pytest.mark.parametrize("M", [2, 5, 8, 12, 16])
 def test_blocked_stack_mfma(M, B):
     # the activation-window kernels (8 and 16 tokens): blocks of whole
     # 512-column steps; y-only linears of several windows walk window-major
-    specs = [(300, 4096), (77, 12288), (129, 1536), (64, 2048), (40, 8192), (33, 16384), (1000, 12288)]
+    # (K = 512 and 4,608: units whose last block group is one K-step)
+    specs = [(300, 4096), (77, 12288), (129, 1536), (64, 2048), (40, 8192), (33, 16384), (1000, 12288),
+             (45, 512), (38, 4608)]
     items = [BlockedLinear(200 + i, N, K, B, M, with_acc=(i % 3 == 1)) for i, (N, K) in enumerate(specs)]
     plan = _stack(items, M)
     assert plan.kernel in (16 + 12, 16 + 13)  # the block-scaled window kernels
@@ -117,7 +119,7 @@ def test_blocked_stack_mfma(M, B):
 def test_blocked_stack_mfma_window_major_groups(M):
     # a few multi-window units per workgroup, y only: window-major groups
     # carry the running block sums between passes in the held slots
-    specs = [(65536, 8192, 512), (24576, 12288, 1024), (8192, 16384, 4096)]
+    specs = [(65536, 8192, 512), (24576, 12288, 1024), (8192, 8192, 2048), (8192, 16384, 4096)]
     items = [BlockedLinear(300 + i, N, K, B, M, with_acc=False) for i, (N, K, B) in enumerate(specs)]
     plan = _stack(items, M)
     assert plan.kernel == 16 + 12
