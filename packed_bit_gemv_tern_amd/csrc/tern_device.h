@@ -10,6 +10,7 @@ namespace tern {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Pointers reach the kernels through descriptors in memory, so the compiler
 // cannot see that they are global; say so, to get global_load instead of

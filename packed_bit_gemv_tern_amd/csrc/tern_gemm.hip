@@ -85,7 +85,11 @@ struct GemmShape {
 // of RING stages.  Staged one K-step at a time, every row's 16 bytes and
 // every token's 64 were an L2 request of their own (640 per step for four 8B
 // layers at M = 512), and the requests in flight per CU, not bytes or MFMAs,
-// set the pace.
+// set the pace.  Their MFMAs take the decoded weights as A and the
+// activations as B, so that a lane's four results are four adjacent rows of
+// one token (16 contiguous bytes of y) rather than four tokens of one row:
+// the epilogue stores 16 bytes per instruction instead of 4 (four 8B layers
+// at M = 512: 415.6 -> 389.3 us).
 template <int ROWS_>
 struct LineShape {
   static constexpr int ROWS = ROWS_, BM = 128, WAVES = 8;
@@ -361,23 +365,11 @@ __device__ __forceinline__ void gemm_tile_lines(const LinearArgs& a, int row0, i
   const int wr = w % S::RGROUPS, wt = w / S::RGROUPS;
   const int rbase = wr * 16 * S::WR, tbase = wt * 16 * S::WT;
 
-  // DMA sources: the token / row index of each instruction's lane (clamped)
-  // and its swizzled piece; the 64-bit addresses are formed at each issue
-  // (held across the loop, twelve more registers made the kernel spill)
-  int atok[S::APW], apc[S::APW];
-#pragma unroll
-  for (int i = 0; i < S::APW; ++i) {
-    const int t = 8 * (w * S::APW + i) + (lane >> 3);
-    atok[i] = min(tok0 + t, M - 1);
-    apc[i] = 16 * ((lane & 7) ^ line_fa(t));
-  }
-  int wrow[S::WPW], wpc[S::WPW];
-#pragma unroll
-  for (int i = 0; i < S::WPW; ++i) {
-    const int rho = 16 * (w * S::WPW + i) + (lane >> 2);
-    wrow[i] = min(row0 + rho, N - 1);
-    wpc[i] = (lane & 3) ^ line_fw(rho);
-  }
+  // DMA sources: each issue derives its lanes' row / token index and swizzled
+  // piece from the lane number afresh (an opaque copy, so that the compiler
+  // cannot hoist them and hold twelve registers through the loop: the kernel
+  // then spilled them and reloaded them at the issues, whose wait for the
+  // reload also waited for every DMA in flight)
   const int qmax = a.ldq - 16;
 
   auto issue_meta = [&]() {
@@ -400,22 +392,26 @@ __device__ __forceinline__ void gemm_tile_lines(const LinearArgs& a, int row0, i
   };
   auto issue_w = [&](int J) {
     uint8_t* dst = L.w[J % S::RING];
+    int l = lane;
+    asm volatile("" : "+v"(l));
 #pragma unroll
     for (int i = 0; i < S::WPW; ++i) {
-      int row = wrow[i];
-      asm volatile("" : "+v"(row));  // keep the address computation here
-      const int ch = min(S::WS * J + wpc[i], nks - 1);
+      const int rho = 16 * (w * S::WPW + i) + (l >> 2);
+      const int row = min(row0 + rho, N - 1);
+      const int ch = min(S::WS * J + ((l & 3) ^ line_fw(rho)), nks - 1);
       __builtin_amdgcn_global_load_lds((const void*)(a.packed + (int64_t)row * a.ld + 16 * ch),
                                        (lds_ptr_t)(dst + 1024 * (w * S::WPW + i)), 16, 0, 0);
     }
   };
   auto issue_a = [&](int j) {
     uint8_t* dst = L.q[j % S::RING];
+    int l = lane;
+    asm volatile("" : "+v"(l));
 #pragma unroll
     for (int i = 0; i < S::APW; ++i) {
-      int tok = atok[i];
-      asm volatile("" : "+v"(tok));
-      const int off = min(64 * S::AS * j + apc[i], qmax);
+      const int t = 8 * (w * S::APW + i) + (l >> 3);
+      const int tok = min(tok0 + t, M - 1);
+      const int off = min(64 * S::AS * j + 16 * ((l & 7) ^ line_fa(t)), qmax);
       __builtin_amdgcn_global_load_lds((const void*)(a.q + (int64_t)tok * a.ldq + off),
                                        (lds_ptr_t)(dst + 1024 * (w * S::APW + i)), 16, 0, 0);
     }
@@ -452,7 +448,7 @@ __device__ __forceinline__ void gemm_tile_lines(const LinearArgs& a, int row0, i
       const i32x4 wb = gemm_decode(wd[b]);
 #pragma unroll
       for (int t = 0; t < S::WT; ++t)
-        acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[t], wb, acc[b][t], 0, 0, 0);
+        acc[b][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wb, qa[t], acc[b][t], 0, 0, 0);
     }
     // issue order: the LDS reads, the first row block's decode, then each
     // MFMA followed by a share of the next row block's decode, so that the
@@ -504,36 +500,57 @@ __device__ __forceinline__ void gemm_tile_lines(const LinearArgs& a, int row0, i
   for (int j = 0; j + 1 < nas; ++j) stage(j, std::false_type{});
   stage(nas - 1, std::true_type{});
 
-  // epilogue: lane holds tokens tok0 + tbase + 16t + 4g + v of row row0 +
-  // rbase + 16b + r; token by token, as in gemm_tile.  (The lane's row and
-  // token offsets are taken here, where the compiler cannot lift the
+  // epilogue: lane (r, g) holds rows row0 + rbase + 16b + 4g + v (v = 0..3)
+  // of token tok0 + tbase + 16t + r, i.e. 16 contiguous bytes of y's token
+  // row: one 16-byte store per (b, t) where y's rows allow it.  (The lane's
+  // row and token offsets are taken here, where the compiler cannot lift the
   // addresses derived from them above the loop and hold them through it.)
   const bool partial = SPLIT && (flags & kSegPartial) != 0;
   const bool zpoint = !partial || (flags & kSegZeroPoint) != 0;
-  int rl0 = rbase + r, ml0 = tbase + 4 * g;
+  const bool vec = (a.ldy & 3) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.acc) & 15) == 0;
+  int rl0 = rbase + 4 * g, ml0 = tbase + r;
   asm volatile("" : "+v"(rl0), "+v"(ml0));
+  int32_t zz[S::WT];
+  float sa[S::WT];
 #pragma unroll
   for (int t = 0; t < S::WT; ++t) {
+    zz[t] = zpoint ? L.z[ml0 + 16 * t] : 0;
+    sa[t] = L.s_act[ml0 + 16 * t];
+  }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int ml = ml0 + 16 * t + v;
-      const int m = tok0 + ml;
+  for (int b = 0; b < S::WR; ++b) {
+    const int row = row0 + rl0 + 16 * b;  // the first of the lane's four
+    const i32x4 rsum = *reinterpret_cast<const i32x4*>(&L.rowsum[rl0 + 16 * b]);
+    const f32x4 srow = *reinterpret_cast<const f32x4*>(&L.s_row[rl0 + 16 * b]);
+#pragma unroll
+    for (int t = 0; t < S::WT; ++t) {
+      const int m = tok0 + ml0 + 16 * t;
       if (m >= M) continue;
-      const int32_t zz = zpoint ? L.z[ml] : 0;
-      const float sa = L.s_act[ml];
-      const int64_t o0 = (int64_t)m * a.ldy + row0 + rl0;
+      i32x4 av;
+      f32x4 yv;
 #pragma unroll
-      for (int b = 0; b < S::WR; ++b) {
-        const int rl = rl0 + 16 * b;
-        if (row0 + rl >= N) continue;
-        const int32_t accv = (int32_t)((uint32_t)acc[b][t][v] - mul_zr(zz, L.rowsum[rl]));
-        const int64_t o = o0 + 16 * b;
-        if (partial) {
-          __hip_atomic_fetch_add((int32_t __attribute__((address_space(1)))*)(reinterpret_cast<int32_t*>(a.y) + o),
-                                 accv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-          store_g(a.y + o, epilogue(L.s_row[rl], accv, sa));
-          if (a.acc) store_g(a.acc + o, accv);
+      for (int v = 0; v < 4; ++v) {
+        av[v] = (int32_t)((uint32_t)acc[b][t][v] - mul_zr(zz[t], rsum[v]));
+        yv[v] = epilogue(srow[v], av[v], sa[t]);
+      }
+      const int64_t o = (int64_t)m * a.ldy + row;
+      if (partial) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (row + v < N)
+            __hip_atomic_fetch_add(
+                (int32_t __attribute__((address_space(1)))*)(reinterpret_cast<int32_t*>(a.y) + o + v), av[v],
+                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else if (vec && row + 3 < N) {
+        store_g(reinterpret_cast<f32x4*>(a.y + o), yv);
+        if (a.acc) store_g(reinterpret_cast<i32x4*>(a.acc + o), av);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if (row + v >= N) continue;
+          store_g(a.y + o + v, yv[v]);
+          if (a.acc) store_g(a.acc + o + v, av[v]);
         }
       }
     }
