@@ -115,6 +115,13 @@ constexpr int kValuOversubscribe = 16;
 // lose 30 %, and at about 1x (four layers at M = 64, one at M = 512) the
 // partial sums' atomics cost more than the shorter tail saves.
 constexpr double kSplitRatio = 3.0;
+// The 9..16-token stacks go to the prefill GEMM when their longest unit
+// outlasts this many even shares of a workgroup.  One 8B layer (the down
+// projection's unit is ~4.2 shares) runs faster on the window kernel: 39.4 ->
+// 30.3 us at M = 9, 40.1 -> 30.9 us at M = 16 (at 3 shares it went to the
+// GEMM); two and four layers (2.1 and 1.05 shares) measured the same either
+// way; single linears and small stacks (tens of shares) keep the GEMM.
+constexpr double kGemmRouteRatio = 6.0;
 constexpr int64_t kValuWaveBytes = 24 << 10;
 // Tokens up to which the MFMA path takes block-scaled linears (the
 // activation-window kernels).
@@ -546,11 +553,10 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
     return std::min(mfma_stack_blocks_per_cu(v), kMaxWavesPerCu / kWavesPerBlock);
   };
   // The kernels at 9..16 tokens keep a workgroup on one unit of rows for
-  // the linear's whole K.  When the longest unit outlasts
-  // kSplitRatio even shares of a workgroup (a stack of a few layers), the
-  // prefill GEMM, whose tiles end sooner and which may split long K, takes
-  // the stack instead; deeper stacks keep their kernel, which streams them
-  // faster.
+  // the linear's whole K.  When the longest unit outlasts kGemmRouteRatio
+  // even shares of a workgroup (a single linear, a small stack), the prefill
+  // GEMM, whose tiles end sooner and which may split long K, takes the stack
+  // instead; deeper stacks keep their kernel, which streams them faster.
   if (p == TERN_PATH_MFMA && M > 8 && !any_blocked &&
       (mfma_is_lockstep(kernel - SK_MFMA) || mfma_is_window(kernel - SK_MFMA))) {
     const int32_t v = kernel - SK_MFMA;
@@ -564,7 +570,7 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
       tot += (double)d.N * ld + 256.0 * (double)((d.N + unit - 1) / unit);
       gm = std::max(gm, (double)std::min<int64_t>(unit, d.N) * ld + 256.0);
     }
-    if (gm > kSplitRatio * tot / workers_v) kernel = (int32_t)SK_MFMA + mfma_gemm_variant((int32_t)M);
+    if (gm > kGemmRouteRatio * tot / workers_v) kernel = (int32_t)SK_MFMA + mfma_gemm_variant((int32_t)M);
   }
   // the prefill GEMM's row tile: 512 rows for stacks of a few such tiles per
   // CU or more, else 256

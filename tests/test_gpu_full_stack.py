@@ -118,9 +118,10 @@ def _check_sampled(st, b, M):
         assert np.array_equal(y.view(np.uint32), ry32.view(np.uint32)), (pl.name, M)
 
 
-# prefill GEMM variants: 9 = 128 x 64 tiles, 14 = 256 x 128, 10 = 512 x 128
+# M = 16: the 16-token window kernel (11); prefill GEMM variants: 9 = 128 x
+# 64 tiles, 14 = 256 x 128, 10 = 512 x 128
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("M,kernel", [(16, 16 + 9), (64, 16 + 9), (512, 16 + 14)])
+@pytest.mark.parametrize("M,kernel", [(16, 16 + 11), (64, 16 + 9), (512, 16 + 14)])
 def test_8b_layer_prefill_sampled(layer8b, M, kernel):
     """One 8B layer as one stack launch at prefill M (the configuration the
     prefill sweep times): sampled rows of every linear against the oracle."""

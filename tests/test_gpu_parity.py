@@ -250,11 +250,12 @@ def test_stack_8b_one_layer(M):
     ws = torch.empty(tern.tern_linear_stack_workspace_bytes(len(ups), M), dtype=torch.uint8,
                      device=DEV)
     plan = tern.tern_linear_stack_prepare([u.desc() for u in ups], M, ws)
-    # one layer at M >= 8 is small enough that the K = 12,288 down projection
+    # one layer at M = 8 is small enough that the K = 12,288 down projection
     # is split per window (partial sums through the output buffer); at 12
-    # and 16 tokens the layer takes the prefill GEMM (the lockstep kernel
-    # never splits)
-    assert plan.splits == (0 if M == 1 else 1)
+    # and 16 tokens the layer takes the 16-token window kernel, which never
+    # splits
+    assert plan.kernel == (16 + 11 if M > 8 else plan.kernel)
+    assert plan.splits == (1 if M == 8 else 0)
     tern.tern_linear_stack(plan)
     tern.tern_linear_stack(plan)  # a second launch over the same plan
     for lin, up in zip(lins, ups):
