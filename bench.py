@@ -93,6 +93,8 @@ def kernel_name(plan) -> str:
         return "valu_stack_kernel<%d, 0u>" % {4: 2, 5: 4, 6: 8}[k]
     if 8 <= k < 12:
         return "valu_stack_blk_kernel<%s>" % _VALU_SETS[k - 8]
+    if 12 <= k < 16:
+        return "valu_stack_tok_kernel<%s>" % _VALU_SETS[k - 12]
     v = k - 16
     if v == 8:
         return "mfma_win_stack_kernel<%s>" % ("true" if getattr(plan, "splits", 0) else "false")
@@ -600,9 +602,10 @@ def suite(args):
     # --- block-wise scales inside the stack launch: the full 8B-shaped stack
     # with one fp32 scale and int32 row sum per block of B columns (8 bytes
     # of metadata per row and block counted in the bytes)
+    # (at M = 8 blocks of 128 columns run token by token on the vector ALU)
     for B in (128, 512):
         stb = DeviceStack("8b", seed=6, threads=16, block=B)
-        for M in ((1, 8) if B == 512 else (1,)):
+        for M in (1, 8):
             b = stb.bind(M)
             us = _event_times(lambda i: b.run(), 20)
             emit({"suite": "stack8b_blocked", "workload": "full 8B-shaped stack (252 linears), block scales "

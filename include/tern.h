@@ -179,7 +179,7 @@ typedef struct {
   int32_t* acc; /* may be NULL */
   /* Block-wise scales along K (see "Block-wise scales" below): block = 0
    * keeps one scale per row (s_row, rowsum).  block = B > 0 (a power of two
-   * in [64, 4096]; a multiple of 512 on the MFMA path, M >= 2) gives row i
+   * in [64, 4096]; a multiple of 512 on the MFMA path) gives row i
    * the scale s_block[i * nb + b] and row sum rowsum_block[i * nb + b] of
    * each block b of B columns (nb = ceil(K / B); from tern_block_rowsum);
    * s_row and rowsum are then not read and may be NULL.  acc, when given,
@@ -250,9 +250,14 @@ int64_t tern_linear_stack_workspace_bytes(int64_t L, int64_t M);
  * the kernel and written when its work ends: as always, y is complete once
  * the launch has completed on the stream, and no other work may read or
  * write it in between.
- * A block-scaled linear (block > 0) needs K a multiple of 64; at M = 1 on the
- * VALU path K <= 16,384, on the MFMA path B a multiple of 512: otherwise
- * TERN_ERR_UNSUPPORTED.  plan->bytes counts 8 bytes of block metadata per
+ * A block-scaled linear (block > 0) needs K a multiple of 64; on the VALU
+ * path (M <= TERN_VALU_MAX_M) K <= 16,384, on the MFMA path (M <= 16) B a
+ * multiple of 512: otherwise TERN_ERR_UNSUPPORTED.  On the automatic path a
+ * stack of 2..TERN_VALU_MAX_M tokens holding a linear whose B is not a
+ * multiple of 512 takes the VALU path, which runs every linear of it token
+ * by token through the one-token kernels (each token's y the bits of the
+ * one-token result; the rows are re-read from the L2, at M times the vector
+ * ALU work of one token).  plan->bytes counts 8 bytes of block metadata per
  * row and block in place of the 8 per row.
  */
 int tern_linear_stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,

@@ -440,8 +440,15 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
   if (!plan || L < 0 || M < 0) return TERN_ERR_INVALID_ARG;
   if (L > kI32Max || M > kI32Max) return TERN_ERR_RANGE;
   if (L > 0 && !descs) return TERN_ERR_INVALID_ARG;
-  const int p = resolve_path(path, M < 1 ? 1 : M);
+  int p = resolve_path(path, M < 1 ? 1 : M);
   if (p < 0) return TERN_ERR_UNSUPPORTED;
+  // block sizes the activation-window kernels cannot take (below 512
+  // columns, or not a multiple of it) send a stack of 2..8 tokens on the
+  // automatic path to the vector ALU, which runs it token by token
+  if (path == TERN_PATH_AUTO && M > 1 && M <= TERN_VALU_MAX_M) {
+    for (int64_t i = 0; i < L; ++i)
+      if (descs[i].block != 0 && descs[i].block % mfma_step_k() != 0) p = TERN_PATH_VALU;
+  }
   // every descriptor is checked before anything is written
   int64_t bytes = 0;
   bool any_blocked = false;
@@ -510,7 +517,7 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
     if (blk) {
       any_blocked = true;
       if (d.K % 64 != 0) return TERN_ERR_UNSUPPORTED;
-      if (p == TERN_PATH_VALU && (M > 1 || valu_blocked_variant(d.K, d.block) < 0)) return TERN_ERR_UNSUPPORTED;
+      if (p == TERN_PATH_VALU && valu_blocked_variant(d.K, d.block) < 0) return TERN_ERR_UNSUPPORTED;
       if (p == TERN_PATH_MFMA && (M > kMfmaBlockedMaxM || d.block % mfma_step_k() != 0))
         return TERN_ERR_UNSUPPORTED;
       if (d.N * nb > kI32Max) return TERN_ERR_RANGE;
@@ -627,7 +634,9 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
   const int64_t wk_k = mfma_window_k();
   auto add_units = [&](int32_t li, int32_t flags) {
     const LinearArgs& a = lin[(size_t)li];
-    const int unit = p == TERN_PATH_VALU ? (a.s_b ? valu_blocked_unit_rows(a.variant) : valu_unit_rows(a.variant, (int32_t)M))
+    // (the token-by-token kernel takes one-token units)
+    const int32_t mu = any_blocked ? 1 : (int32_t)M;
+    const int unit = p == TERN_PATH_VALU ? (a.s_b ? valu_blocked_unit_rows(a.variant) : valu_unit_rows(a.variant, mu))
                                          : mfma_unit_rows(kernel - SK_MFMA);
     // bytes of a row the unit reads: packed weights (and block metadata)
     const double ld = 16.0 * a.nch + (a.s_b ? 8.0 * a.nb : 0.0);

@@ -128,13 +128,15 @@ constexpr int32_t kStackMagic = 0x7e54a11;
 // SK_VALU_M1 .. SK_VALU_M1 + 3 are the M = 1 kernel compiled for growing
 // variant sets (8B shapes, 0.6B shapes, every register variant, all).
 // SK_VALU_M1_BLK .. + 3: the same sets for stacks holding block-scaled
-// linears.
+// linears; SK_VALU_TOK_BLK .. + 3: such stacks at 2..8 tokens, run token by
+// token through the M = 1 paths.
 enum StackKernel : int32_t {
   SK_VALU_M1 = 0,
   SK_VALU_M2 = 4,
   SK_VALU_M4 = 5,
   SK_VALU_M8 = 6,
   SK_VALU_M1_BLK = 8,
+  SK_VALU_TOK_BLK = 12,
   SK_MFMA = 16  // SK_MFMA + mfma_stack_variant(M, ragged)
 };
 

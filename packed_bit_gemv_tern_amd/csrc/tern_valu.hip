@@ -644,6 +644,51 @@ __global__ __launch_bounds__(kBlock) void valu_stack_blk_kernel(const StackHeade
   }
 }
 
+// Stacks of 2..8 tokens holding block-scaled linears: every segment is run
+// token by token through the M = 1 paths above (block-scaled linears the
+// block path, the others the per-row one), token m reading q row m, s_act[m]
+// and z[m] and writing y (and acc) row m.  A segment's rows are re-read for
+// each token from the L2 (a segment is a few hundred KB at most), and each
+// token's y has the bits of the one-token evaluation, the blocks summed in
+// order.  It takes block sizes the activation-window kernels cannot (below
+// 512 columns), at the M = 1 path's vector-ALU cost per token.
+template <uint32_t VSET>
+__global__ __launch_bounds__(kBlock) void valu_stack_tok_kernel(const StackHeader* __restrict__ h,
+                                  StackSync* __restrict__ sy) {
+  __shared__ __attribute__((aligned(16))) float prods[kWavesPerBlock][kBlkLdsWave / 4];
+  __shared__ PrologueLds prol;
+  const uint32_t launch1 = stack_prologue(h, sy, prol);
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id_uniform();
+  const int worker = xcd_logical_block() * kWavesPerBlock + w;
+  if (worker >= h->workers) return;
+  const LinearArgs* lin = reinterpret_cast<const LinearArgs*>(
+      reinterpret_cast<const char*>(h) + h->off_lin);
+  const int32_t* seg_start = reinterpret_cast<const int32_t*>(
+      reinterpret_cast<const char*>(h) + h->off_seg_start);
+  const Segment* seg = reinterpret_cast<const Segment*>(
+      reinterpret_cast<const char*>(h) + h->off_seg);
+  const int s1 = seg_start[worker + 1];
+  wait_segment_inputs(h, sy, lin, seg, seg_start[worker], s1, launch1);
+  for (int s = seg_start[worker]; s < s1; ++s) {
+    const Segment sg = seg[s];
+    const LinearArgs a = lin[sg.lin];
+    for (int m = 0; m < a.M; ++m) {
+      LinearArgs t = a;
+      t.M = 1;
+      t.q = a.q + (int64_t)m * a.ldq;
+      t.s_act = a.s_act + m;
+      t.z = a.z + m;
+      t.y = a.y + (int64_t)m * a.ldy;
+      if (a.acc) t.acc = a.acc + (int64_t)m * a.ldy;
+      if (t.s_b)
+        valu_m1_segment_blk<VSET>(t, sg.row_begin, sg.row_end, lane, prods[w]);
+      else
+        valu_m1_segment<VSET>(t, sg.row_begin, sg.row_end, lane);
+    }
+  }
+}
+
 // ------------------------------------------------------------- launchers --
 
 // The register variant of a block-scaled linear: the per-row one when its
@@ -751,8 +796,8 @@ hipError_t launch_valu_linear(const LinearArgs& a, hipStream_t s) {
 
 
 int32_t valu_stack_kernel_for(int32_t M, uint32_t used_variants, bool blocked) {
-  if (M == 1) {
-    const int32_t k0 = blocked ? SK_VALU_M1_BLK : SK_VALU_M1;
+  if (M == 1 || blocked) {
+    const int32_t k0 = blocked ? (M == 1 ? SK_VALU_M1_BLK : SK_VALU_TOK_BLK) : SK_VALU_M1;
     for (int i = 0; i < 4; ++i)
       if ((used_variants & ~kSets[i]) == 0) return k0 + i;
     return k0 + 3;
@@ -776,6 +821,10 @@ static hipError_t with_valu_stack_kernel(int32_t kernel, F&& f) {
     case SK_VALU_M1_BLK + 1: return f(valu_stack_blk_kernel<kSets[1]>);
     case SK_VALU_M1_BLK + 2: return f(valu_stack_blk_kernel<kSets[2]>);
     case SK_VALU_M1_BLK + 3: return f(valu_stack_blk_kernel<kSets[3]>);
+    case SK_VALU_TOK_BLK + 0: return f(valu_stack_tok_kernel<kSets[0]>);
+    case SK_VALU_TOK_BLK + 1: return f(valu_stack_tok_kernel<kSets[1]>);
+    case SK_VALU_TOK_BLK + 2: return f(valu_stack_tok_kernel<kSets[2]>);
+    case SK_VALU_TOK_BLK + 3: return f(valu_stack_tok_kernel<kSets[3]>);
     default: return hipErrorInvalidValue;
   }
 }

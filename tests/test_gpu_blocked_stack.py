@@ -127,6 +127,50 @@ def test_blocked_stack_mfma_window_major_groups(M):
         it.check("window-major M=%d B=%d K=%d" % (M, it.B, it.K))
 
 
+@pytest.mark.parametrize("B", [64, 128, 256])
+@pytest.mark.parametrize("M", [2, 3, 5, 8])
+def test_blocked_stack_small_blocks_token_by_token(M, B):
+    # blocks below 512 columns at 2..8 tokens: the automatic path runs the
+    # stack token by token through the one-token kernels
+    specs = [(300, 4096), (77, 12288), (129, 1024), (64, 2048), (33, 3072), (50, 512), (40, 8192), (17, 16384)]
+    items = [BlockedLinear(400 + i, N, K, B, M, with_acc=(i % 2 == 0)) for i, (N, K) in enumerate(specs)]
+    plan = _stack(items, M)
+    assert 12 <= plan.kernel < 16  # the token-by-token kernels
+    for it in items:
+        it.check("tokens M=%d B=%d K=%d N=%d" % (M, B, it.K, it.N))
+
+
+@pytest.mark.parametrize("M", [2, 6])
+def test_blocked_stack_token_by_token_with_per_row_linears(M):
+    # per-row linears (one of ragged K) beside block-scaled ones, token by token
+    items = [BlockedLinear(17, 500, 4096, 128, M, True), BlockedLinear(18, 200, 12288, 512, M, False)]
+    rows = []
+    for i, (N, K) in enumerate([(300, 4096), (90, 100), (64, 12288)]):
+        lin = synth.make_linear(19 + i, 0, 2, N, K, 0.626, M)
+        packed, rowsum, _ = gpu_pack(lin.w)
+        q = to_dev(pad_cols(lin.q))
+        y = torch.full((M, N + 1), float("nan"), dtype=torch.float32, device=DEV)
+        acc = torch.empty((M, N + 1), dtype=torch.int32, device=DEV) if i != 1 else None
+        bufs = (packed, rowsum, q, to_dev(lin.s_row), to_dev(lin.s_act), to_dev(lin.z), y, acc)
+        rows.append((lin, bufs, tern.make_desc(packed, bufs[3], rowsum, N, K, q, q.shape[1], bufs[4], bufs[5],
+                                               y, N + 1, acc)))
+    descs = [items[0].desc(), rows[0][2], rows[1][2], items[1].desc(), rows[2][2]]
+    ws = torch.empty(tern.tern_linear_stack_workspace_bytes(len(descs), M), dtype=torch.uint8, device=DEV)
+    plan = tern.tern_linear_stack_prepare(descs, M, ws)
+    assert 12 <= plan.kernel < 16
+    tern.tern_linear_stack(plan)
+    for it in items:
+        it.check("mixed tokens M=%d" % M)
+    for lin, bufs, _ in rows:
+        rp, rr, _ = oracle.pack(lin.w)
+        racc, ry32, _ = oracle.linear(rp, lin.s_row, rr, lin.K, lin.q, lin.s_act, lin.z)
+        y = bufs[6].cpu().numpy()
+        assert np.all(np.isnan(y[:, lin.N:]))
+        assert np.array_equal(y[:, :lin.N].view(np.uint32), ry32.view(np.uint32)), (M, lin.N, lin.K)
+        if bufs[7] is not None:
+            assert np.array_equal(bufs[7].cpu().numpy()[:, :lin.N], racc), (M, lin.N, lin.K)
+
+
 def test_blocked_stack_rejections():
     # block sizes the stack cannot take come back as errors before any launch
     M = 8
@@ -135,7 +179,15 @@ def test_blocked_stack_rejections():
     d = it.desc()
     d.block = 128  # the MFMA path takes whole 512-column steps
     with pytest.raises(tern.TernError) as e:
-        tern.tern_linear_stack_prepare([d], M, ws)
+        tern.tern_linear_stack_prepare([d], M, ws, tern.TERN_PATH_MFMA)
+    assert e.value.status == tern.TERN_ERR_UNSUPPORTED
+    # ... and the vector ALU at most TERN_VALU_MAX_M tokens
+    it12 = BlockedLinear(4, 64, 4096, 512, 12, False)
+    ws12 = torch.empty(tern.tern_linear_stack_workspace_bytes(1, 12), dtype=torch.uint8, device=DEV)
+    d12 = it12.desc()
+    d12.block = 128
+    with pytest.raises(tern.TernError) as e:
+        tern.tern_linear_stack_prepare([d12], 12, ws12)
     assert e.value.status == tern.TERN_ERR_UNSUPPORTED
     d.block = 96
     with pytest.raises(tern.TernError) as e:
