@@ -84,6 +84,49 @@ def load_traffic(kernel: str):
 _VALU_SETS = {0: "80u", 1: "14u", 2: "255u", 3: "511u"}
 
 
+def _counter_means(path: str):
+    """Mean counter value per kernel name over its dispatches (rocprofv3 csv)."""
+    import csv
+    sums, counts = {}, {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            k = row["Kernel_Name"]
+            sums[k] = sums.get(k, 0.0) + float(row["Counter_Value"])
+            counts[k] = counts.get(k, 0) + 1
+    return {k: (sums[k] / counts[k], counts[k]) for k in sums}
+
+
+def write_traffic(d: str):
+    """profiles/traffic.json from FETCH_SIZE / WRITE_SIZE runs of the m1 and
+    m8 passes and of a 1 GiB device copy (the calibration: the copy reads and
+    writes 1 GiB, so scale = 2^20 KiB / its counter reading)."""
+    def means(c, w):
+        return _counter_means(os.path.join(d, "pmc_%s_%s" % (c, w), "run_counter_collection.csv"))
+    scale = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cp = [v for k, v in means(c, "copy").items() if "copyBuffer" in k]
+        kib = max(v[0] for v in cp)  # the 1 GiB copies (other copies are small)
+        scale[c] = float(1 << 20) / kib
+    algo = {"m1": 1754580960, "m8": 1803108096}  # bytes of the 8B stack pass at M = 1 / 8
+    out = {"source_hash": kernel_source_hash(), "fetch_scale": scale["FETCH_SIZE"],
+           "write_scale": scale["WRITE_SIZE"], "kernels": {}}
+    for w, M in (("m1", 1), ("m8", 8)):
+        f = {k: v for k, v in means("FETCH_SIZE", w).items() if "stack_kernel" in k}
+        wr = {k: v for k, v in means("WRITE_SIZE", w).items() if "stack_kernel" in k}
+        (k, (fk, _)), = f.items()
+        wk = wr[k][0]
+        # the profiler's name without return type, namespaces and arguments,
+        # as kernel_name() gives it (the defaulted template argument dropped)
+        name = k.split("(")[0].replace("void ", "").replace("tern::", "").replace("(anonymous namespace)::", "")
+        name = {"mfma_win_stack_kernel<false, false>": "mfma_win_stack_kernel<false>"}.get(name, name)
+        hbm = fk * 1024 * scale["FETCH_SIZE"] + wk * 1024 * scale["WRITE_SIZE"]
+        out["kernels"][name] = {"M": M, "fetch_kib": fk, "write_kib": wk, "hbm_bytes_per_launch": int(round(hbm)),
+                                "algorithmic_bytes": algo[w], "ratio": round(hbm / algo[w], 4)}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def kernel_name(plan) -> str:
     """Name of the HIP kernel a prepared stack launches (as the profiler shows it)."""
     k = plan.kernel
@@ -669,7 +712,14 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times "
                          "(reference for the HBM byte counters) and exit")
+    ap.add_argument("--write-traffic", default=None, metavar="DIR",
+                    help="no GPU: read the rocprofv3 counter runs under DIR (pmc_<C>_<m1|m8|copy>/"
+                         "run_counter_collection.csv for C = FETCH_SIZE, WRITE_SIZE) and write "
+                         "profiles/traffic.json for the current sources")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; the stack is the one-GPU share "
