@@ -387,11 +387,12 @@ int tern_head_gemv(const int8_t* W, const float* s_row, const int32_t* rowsum, i
   if (!aligned(y, 4) || !aligned(s_row, 4) || !aligned(rowsum, 4) || !aligned(s_act, 4) ||
       !aligned(z, 4) || (acc && !aligned(acc, 4)))
     return TERN_ERR_ALIGNMENT;
-  // a workgroup per ~4 of each CU's slots, with a whole number of units
+  // head_wg_per_cu() workgroups per CU, each with a whole number of units
   const int cus = device_cus();
   if (cus <= 0) return hip_fail(hipErrorNoDevice);
   const int64_t unit = head_rows_per_unit(M);
-  const int64_t per = (N + 4 * (int64_t)cus - 1) / (4 * (int64_t)cus);
+  const int64_t wgc = (int64_t)head_wg_per_cu() * cus;
+  const int64_t per = (N + wgc - 1) / wgc;
   const int64_t rows = (per + unit - 1) / unit * unit;
   if (head_lds_bytes(M, K, rows) > 65536) return TERN_ERR_RANGE;
   const hipError_t e = launch_head(W, s_row, rowsum, N, K, ldw, M, q, M > 1 ? ldq : K, s_act, z, y,

@@ -31,10 +31,14 @@ namespace {
 constexpr int kHeadBlock = 256;
 constexpr int kHeadWaves = kHeadBlock / 64;
 
-// rows per unit for MT tokens: U * MT values go through one 64-lane reduction
+// rows per unit for MT tokens: U * MT values go through one 64-lane reduction.
+// Eight rows (eight 16-byte weight loads per lane and step) at every MT:
+// with four at M > 1 the full 151,936 x 4,096 head took 105.8 us at M = 8
+// against 102.1 with eight (M = 2 and 4 the same either way), the launches
+// sized as below.
 template <int MT>
 struct HeadU {
-  static constexpr int U = MT == 1 ? 8 : 4;
+  static constexpr int U = 8;
 };
 
 struct HeadArgs {
@@ -209,6 +213,13 @@ int head_tokens(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 int64_t head_lds_bytes(int64_t M, int64_t K, int64_t rows) {
   return (int64_t)head_tokens(M) * (16 * ((K + 15) / 16)) + 8 * rows;
 }
+
+// Workgroups per CU the host sizes a launch for (each takes N / (that * CUs)
+// rows).  Every workgroup stages its tokens' activations in LDS first, and
+// fewer, longer workgroups ran faster: the full head at M = 1 / 8 took
+// 96.6 / 105.8 us with four per CU (and four rows per unit at M = 8),
+// 92.5 / 102.1 with two; one per CU was slower again (97.8 / 123.5).
+int head_wg_per_cu() { return 2; }
 
 int head_rows_per_unit(int64_t M) {
   switch (head_tokens(M)) {

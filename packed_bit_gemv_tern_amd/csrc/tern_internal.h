@@ -240,6 +240,7 @@ hipError_t launch_mfma_stack(int32_t variant, const void* ws, const LaunchShape&
                              hipStream_t s);
 // int8 output head (tern_head.hip): M <= 8 tokens, workgroups of contiguous rows
 int head_tokens(int64_t M);
+int head_wg_per_cu();
 int head_rows_per_unit(int64_t M);  // rows a workgroup takes per pass of its waves
 int64_t head_lds_bytes(int64_t M, int64_t K, int64_t rows);
 hipError_t launch_head(const int8_t* W, const float* s_row, const int32_t* rowsum, int64_t N, int64_t K,
