@@ -107,7 +107,12 @@ def write_traffic(d: str):
         cp = [v for k, v in means(c, "copy").items() if "copyBuffer" in k]
         kib = max(v[0] for v in cp)  # the 1 GiB copies (other copies are small)
         scale[c] = float(1 << 20) / kib
-    algo = {"m1": 1754580960, "m8": 1803108096}  # bytes of the 8B stack pass at M = 1 / 8
+    from packed_bit_gemv_tern_amd import synth, tern
+
+    def algo_bytes(M):  # the stack planner's count for one pass (plan.bytes)
+        return sum(N * tern.tern_row_bytes(K) + 8 * N + M * K + 8 * M + 4 * M * N
+                   for (_, _, _, N, K, _) in synth.stack_specs("8b"))
+    algo = {"m1": algo_bytes(1), "m8": algo_bytes(8)}
     out = {"source_hash": kernel_source_hash(), "fetch_scale": scale["FETCH_SIZE"],
            "write_scale": scale["WRITE_SIZE"], "kernels": {}}
     for w, M in (("m1", 1), ("m8", 8)):
