@@ -96,6 +96,10 @@ def _declare(lib):
         _p(ctypes.c_float), i64, i64, i64, _p(ctypes.c_int8), i64, _p(ctypes.c_float), _p(i32)]
     lib.oracle_block_rowsum.restype = None
     lib.oracle_block_rowsum.argtypes = [_p(ctypes.c_int8), i64, i64, i64, i64, _p(i32)]
+    lib.oracle_exp32.restype = None
+    lib.oracle_exp32.argtypes = [_p(ctypes.c_float), i64, _p(ctypes.c_float)]
+    lib.oracle_swiglu.restype = None
+    lib.oracle_swiglu.argtypes = [_p(ctypes.c_float), _p(ctypes.c_float), i64, i64, i64, _p(ctypes.c_float)]
     lib.oracle_linear_blocked.restype = ctypes.c_int
     lib.oracle_linear_blocked.argtypes = [
         _p(ctypes.c_uint8), _p(ctypes.c_float), _p(i32), i64, i64, i64, i64,
@@ -277,6 +281,29 @@ def quantize_act(x, lib=None):
     lib.oracle_quantize_act(_ptr(x, ctypes.c_float), M, K, K, _ptr(q, ctypes.c_int8), K,
                             _ptr(s_act, ctypes.c_float), _ptr(z, ctypes.c_int32))
     return q, s_act, z
+
+
+def exp32(x, lib=None):
+    """The fp32 exp of the SwiGLU evaluation (Cody-Waite reduction, Taylor to
+    r^7): float32 array of the same shape."""
+    lib = lib or load()
+    x = _c(np.asarray(x), np.float32)
+    out = np.empty_like(x)
+    lib.oracle_exp32(_ptr(x, ctypes.c_float), x.size, _ptr(out, ctypes.c_float))
+    return out
+
+
+def swiglu(g, u, lib=None):
+    """h = silu(g) * u in the fixed fp32 steps of oracle_swiglu (model card
+    "Neutrino-1 8B", "Architecture": gated SwiGLU feed-forward); (M, K)."""
+    lib = lib or load()
+    g = _c(np.atleast_2d(g), np.float32)
+    u = _c(np.atleast_2d(u), np.float32)
+    assert g.shape == u.shape
+    M, K = g.shape
+    h = np.empty((M, K), np.float32)
+    lib.oracle_swiglu(_ptr(g, ctypes.c_float), _ptr(u, ctypes.c_float), M, K, K, _ptr(h, ctypes.c_float))
+    return h
 
 
 def block_rowsum(w, B, lib=None):

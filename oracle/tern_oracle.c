@@ -570,3 +570,72 @@ void oracle_quantize_weights(const float* W, int64_t N, int64_t K, int64_t ldw, 
     }
   }
 }
+
+/*
+ * The gated feed-forward activation.  The model card ("Neutrino-1 8B",
+ * "Architecture") gives each layer a gated SwiGLU feed-forward of three
+ * linears; the pages do not write the gate out, so this takes the plainest
+ * reading, the SiLU-gated product of the gate and up projections' outputs:
+ *
+ *     h_j = silu(g_j) * u_j,      silu(x) = x / (1 + e^(-x))
+ *
+ * h is the down projection's input, quantised per token like any other
+ * activation.  A correctly rounded exp is not available on both sides, so
+ * the fp32 evaluation is fixed step by step (round to nearest even, no
+ * fused multiply-add) and the GPU follows the same steps:
+ *
+ *   e = exp32(min(max(-g, -87), 100))     (e^-87 is still a normal float, and
+ *                                          below it 1 + e rounds to 1 anyway;
+ *                                          past 88.7 exp32 overflows to +inf
+ *                                          and s below is -0)
+ *   s = g / (1 + e)                       (one correctly rounded division)
+ *   h = s * u
+ *
+ * exp32(x): Cody and Waite's argument reduction x = k ln2 + r with
+ *   k = rint(x * log2(e)),  r = (x - k * L1) - k * L2,
+ * L1 = 0.693145751953125 (ln 2 to 15 significant bits, so k * L1 is exact
+ * for |k| <= 256) and L2 = ln 2 - L1 rounded to fp32, then the
+ * Taylor series of e^r through r^7 by Horner's rule with coefficients
+ * 1/n! rounded to fp32, scaled by 2^k.  |r| <= ln 2 / 2 makes the truncation
+ * below 6e-9 relative; oracle_exp32_ulp tests bound the whole error.
+ */
+static float exp32(float x) {
+  const double ln2 = 0.69314718055994530942;
+  const float kLog2e = (float)(1.0 / ln2);
+  const float kL1 = 0.693145751953125f;
+  const float kL2 = (float)(ln2 - 0.693145751953125);
+  const float k = rintf(x * kLog2e);
+  const float r = (x - k * kL1) - k * kL2;
+  /* 1/n! for n = 7 .. 2, then 1, 1 */
+  const float c7 = (float)(1.0 / 5040.0), c6 = (float)(1.0 / 720.0), c5 = (float)(1.0 / 120.0);
+  const float c4 = (float)(1.0 / 24.0), c3 = (float)(1.0 / 6.0), c2 = 0.5f;
+  float p = c7;
+  p = p * r + c6;
+  p = p * r + c5;
+  p = p * r + c4;
+  p = p * r + c3;
+  p = p * r + c2;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  return ldexpf(p, (int)k);
+}
+
+void oracle_exp32(const float* x, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = exp32(x[i]);
+}
+
+/* h = silu(g) * u, element by element (M x K with row strides ldg = ldu). */
+void oracle_swiglu(const float* g, const float* u, int64_t M, int64_t K, int64_t ld, float* h) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t j = 0; j < K; ++j) {
+      const float gv = g[m * ld + j];
+      float t = -gv;
+      if (t < -87.0f) t = -87.0f;
+      if (t > 100.0f) t = 100.0f;
+      const float e = exp32(t);
+      const float s = gv / (1.0f + e);
+      h[m * K + j] = s * u[m * ld + j];
+    }
+  }
+}
