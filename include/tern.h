@@ -196,9 +196,25 @@ typedef struct {
    * must name the same x, ldx, K, ldq, s_act and z (and every linear
    * naming such a q reads the quantised values, with or without x);
    * otherwise TERN_ERR_INVALID_ARG.  q, s_act and z are outputs of the
-   * launch, complete when it is; x must not overlap them. */
+   * launch, complete when it is; x (and x_up) must not overlap them. */
   const float* x;
   int64_t ldx;
+  /* With x_up (NULL: the input is x itself) the input the launch quantises
+   * is the gated feed-forward activation of the model card's SwiGLU layers
+   * ("Neutrino-1 8B", "Architecture"), h = silu(x) * x_up element by element
+   * (x the gate projection's output, x_up the up projection's, both M x K
+   * with row stride ldx, 4-byte aligned), in these fp32 steps (round to
+   * nearest even, no fused multiply-add):
+   *     t = min(max(-x_j, -87), 100)
+   *     e = exp32(t): k = rint(t * fp32(1/ln 2)), r = (t - k * 0.693145751953125)
+   *                   - k * fp32(ln 2 - 0.693145751953125), then the Taylor
+   *                   series of e^r through r^7 (coefficients 1/n! rounded to
+   *                   fp32) by Horner's rule, times 2^k (+inf past 88.7)
+   *     h_j = (x_j / (1 + e)) * x_up_j   (one correctly rounded division)
+   * so a down projection reads its input straight from the gate and up
+   * outputs of an earlier launch, with the gate and the quantisation done in
+   * its own launch.  Linears naming the same q must name the same x_up. */
+  const float* x_up;
 } tern_linear_desc;
 
 /* Host-side handle filled by tern_linear_stack_prepare (plain data; copy it

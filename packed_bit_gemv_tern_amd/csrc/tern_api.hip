@@ -460,14 +460,17 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
   std::map<const void*, int32_t> job_of_q;
   for (int64_t i = 0; i < L; ++i) {
     const tern_linear_desc& d = descs[i];
-    if (!d.x) continue;
+    if (!d.x) {
+      if (d.x_up) return TERN_ERR_INVALID_ARG;  // the gate without its input
+      continue;
+    }
     // (checked here as well as below: a linear with no rows still has its
     // input quantised)
     if (d.K < 1 || d.ldx < d.K || !d.q || !d.s_act || !d.z) return TERN_ERR_INVALID_ARG;
     if (d.K > TERN_MAX_K || d.ldx > kI32Max || d.ldq > kI32Max) return TERN_ERR_RANGE;
     if (M > 1 && d.ldq < d.K) return TERN_ERR_INVALID_ARG;
-    if (!aligned(d.x, 4) || !aligned(d.q, 16) || !aligned(d.s_act, 4) || !aligned(d.z, 4) ||
-        (M > 1 && d.ldq % 16 != 0))
+    if (!aligned(d.x, 4) || !aligned(d.x_up, 4) || !aligned(d.q, 16) || !aligned(d.s_act, 4) ||
+        !aligned(d.z, 4) || (M > 1 && d.ldq % 16 != 0))
       return TERN_ERR_ALIGNMENT;
     const int64_t ldq = M > 1 ? d.ldq : d.K;
     auto it = job_of_q.find(d.q);
@@ -475,6 +478,7 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
       QuantJob j;
       memset(&j, 0, sizeof(j));
       j.x = d.x;
+      j.x_up = d.x_up;
       j.q = const_cast<int8_t*>(d.q);
       j.s_act = const_cast<float*>(d.s_act);
       j.z = const_cast<int32_t*>(d.z);
@@ -486,7 +490,8 @@ int stack_prepare(const tern_linear_desc* descs, int64_t L, int64_t M, int path,
       continue;
     }
     const QuantJob& j = jobs[(size_t)it->second];
-    if (j.x != d.x || j.ldx != d.ldx || j.K != d.K || j.ldq != ldq || j.s_act != d.s_act || j.z != d.z)
+    if (j.x != d.x || j.x_up != d.x_up || j.ldx != d.ldx || j.K != d.K || j.ldq != ldq ||
+        j.s_act != d.s_act || j.z != d.z)
       return TERN_ERR_INVALID_ARG;
   }
   if (!jobs.empty()) {

@@ -97,7 +97,8 @@ struct alignas(16) QuantJob {
   int32_t* z;
   int64_t ldx, ldq;
   int32_t K;
-  int32_t pad[3];
+  int32_t pad;
+  const float* x_up;  // non-null: quantise silu(x) * x_up (the SwiGLU gate)
 };
 static_assert(sizeof(QuantJob) == 64, "QuantJob layout");
 

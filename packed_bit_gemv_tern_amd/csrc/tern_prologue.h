@@ -34,6 +34,35 @@ __device__ __forceinline__ float wave_max_f(float v) {
   return v;
 }
 
+// The SwiGLU gate of the model card's feed-forward layers, silu(g) * u,
+// in fixed fp32 steps (round to nearest even, no fused multiply-add: the
+// build keeps every product and sum as written) so that the result is a
+// function of g and u alone:
+//   t = clamp(-g, -87, 100); e = e^t by Cody and Waite's reduction
+//   t = k ln2 + r (k = rint(t / ln 2), ln 2 split in a 15-bit head, whose
+//   product with k is exact, and an fp32 tail) and the Taylor series of e^r
+//   through r^7 by Horner's rule, scaled by 2^k (+inf past 88.7);
+//   silu = g / (1 + e), correctly rounded; h = silu * u.
+__device__ __forceinline__ float swiglu32(float g, float u) {
+  constexpr double kLn2 = 0.69314718055994530942;
+  constexpr float kInvLn2 = (float)(1.0 / kLn2);
+  constexpr float kHead = 0.693145751953125f;
+  constexpr float kTail = (float)(kLn2 - 0.693145751953125);
+  const float t = fminf(fmaxf(-g, -87.0f), 100.0f);
+  const float k = __builtin_rintf(__fmul_rn(t, kInvLn2));
+  const float r = __fsub_rn(__fsub_rn(t, __fmul_rn(k, kHead)), __fmul_rn(k, kTail));
+  float p = (float)(1.0 / 5040.0);
+  p = __fadd_rn(__fmul_rn(p, r), (float)(1.0 / 720.0));
+  p = __fadd_rn(__fmul_rn(p, r), (float)(1.0 / 120.0));
+  p = __fadd_rn(__fmul_rn(p, r), (float)(1.0 / 24.0));
+  p = __fadd_rn(__fmul_rn(p, r), (float)(1.0 / 6.0));
+  p = __fadd_rn(__fmul_rn(p, r), 0.5f);
+  p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+  p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+  const float e = __builtin_ldexpf(p, (int)k);
+  return __fmul_rn(__fdiv_rn(g, __fadd_rn(1.0f, e)), u);
+}
+
 // LDS a stack kernel lends the prologue: the claim just made (two slots,
 // alternating) and the waves' partial minima and maxima.
 struct PrologueLds {
@@ -44,15 +73,17 @@ struct PrologueLds {
 // One token row of K floats quantised by the whole workgroup: a min/max
 // pass, then the codes (thread t takes columns 4t + 4Ti .. +3, T threads,
 // stored as one dword where the four lie inside K; q is 4-byte aligned).
-__device__ __forceinline__ void quantize_row_wg(const float* x, int K, int8_t* q, float* s_out,
-                                                int32_t* z_out, PrologueLds& pl) {
+// With x_up the row's values are swiglu32(x_j, x_up_j), formed in each pass.
+__device__ __forceinline__ void quantize_row_wg(const float* x, const float* x_up, int K, int8_t* q,
+                                                float* s_out, int32_t* z_out, PrologueLds& pl) {
   const int t = threadIdx.x, nt = blockDim.x, waves = blockDim.x >> 6;
+  auto val = [&](int j) { return x_up ? swiglu32(load_g(x + j), load_g(x_up + j)) : load_g(x + j); };
   float lo = 0.0f, hi = 0.0f;
   for (int j0 = 4 * t; j0 < K; j0 += 4 * nt) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (j0 + u < K) {
-        const float v = load_g(x + j0 + u);
+        const float v = val(j0 + u);
         lo = fminf(lo, v);
         hi = fmaxf(hi, v);
       }
@@ -70,10 +101,10 @@ __device__ __forceinline__ void quantize_row_wg(const float* x, int K, int8_t* q
     if (j0 + 3 < K) {
       uint32_t word = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) word |= ((uint32_t)act_code(load_g(x + j0 + u), s, zm) & 0xffu) << (8 * u);
+      for (int u = 0; u < 4; ++u) word |= ((uint32_t)act_code(val(j0 + u), s, zm) & 0xffu) << (8 * u);
       store_g(reinterpret_cast<uint32_t*>(q + j0), word);
     } else {
-      for (int u = 0; j0 + u < K; ++u) store_g(q + j0 + u, (int8_t)act_code(load_g(x + j0 + u), s, zm));
+      for (int u = 0; j0 + u < K; ++u) store_g(q + j0 + u, (int8_t)act_code(val(j0 + u), s, zm));
     }
   }
   if (t == 0) {
@@ -119,7 +150,8 @@ __device__ __forceinline__ uint32_t stack_prologue(const StackHeader* h, StackSy
     if (item >= nitems) return launch1;
     const int job = (int)(item / M), m = (int)(item % M);
     const QuantJob jb = jobs[job];
-    quantize_row_wg(jb.x + (int64_t)m * jb.ldx, jb.K, jb.q + (int64_t)m * jb.ldq, jb.s_act + m, jb.z + m, pl);
+    quantize_row_wg(jb.x + (int64_t)m * jb.ldx, jb.x_up ? jb.x_up + (int64_t)m * jb.ldx : nullptr, jb.K,
+                    jb.q + (int64_t)m * jb.ldq, jb.s_act + m, jb.z + m, pl);
     // every wave's codes are visible device-wide before the row's flag
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();

@@ -60,7 +60,7 @@ class tern_linear_desc(ctypes.Structure):
         ("s_act", ctypes.c_void_p), ("z", ctypes.c_void_p),
         ("y", ctypes.c_void_p), ("ldy", ctypes.c_int64), ("acc", ctypes.c_void_p),
         ("block", ctypes.c_int64), ("s_block", ctypes.c_void_p), ("rowsum_block", ctypes.c_void_p),
-        ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64),
+        ("x", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("x_up", ctypes.c_void_p),
     ]
 
 
@@ -236,14 +236,16 @@ def tern_linear_stack_workspace_bytes(L: int, M: int) -> int:
 
 
 def make_desc(packed, s_row, rowsum, N, K, q, ldq, s_act, z, y, ldy, acc=None, block=0, s_block=None,
-              rowsum_block=None, x=None, ldx=0) -> tern_linear_desc:
+              rowsum_block=None, x=None, ldx=0, x_up=None) -> tern_linear_desc:
     """One linear of a stack.  With block > 0 (block-wise scales along K),
     s_block / rowsum_block are N x ceil(K / block) and s_row / rowsum may be
     None.  With x (fp32, M x K, row stride ldx) the launch quantises x into
-    q, s_act and z itself."""
+    q, s_act and z itself; with x_up as well, it quantises silu(x) * x_up
+    (the gated feed-forward activation; x the gate projection's output)."""
     d = tern_linear_desc()
     d.x = None if x is None else x.data_ptr()
     d.ldx = int(ldx)
+    d.x_up = None if x_up is None else x_up.data_ptr()
     d.packed = packed.data_ptr()
     d.s_row = None if s_row is None else s_row.data_ptr()
     d.rowsum = None if rowsum is None else rowsum.data_ptr()

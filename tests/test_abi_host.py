@@ -168,6 +168,12 @@ def test_stack_fused_input_errors(lib):
     # one q buffer, two different inputs or scales
     assert prep(_desc(x=X, ldx=64), _desc(x=X + 1024, ldx=64)) == tern.TERN_ERR_INVALID_ARG
     assert prep(_desc(x=X, ldx=64), _desc(x=X, ldx=80)) == tern.TERN_ERR_INVALID_ARG
+    # the SwiGLU gate's second input: never without x, 4-byte aligned, one per q buffer
+    assert prep(_desc(x_up=X)) == tern.TERN_ERR_INVALID_ARG
+    assert prep(_desc(x=X, ldx=64, x_up=X + 4096 + 2)) == tern.TERN_ERR_ALIGNMENT
+    assert prep(_desc(x=X, ldx=64, x_up=X + 4096), _desc(x=X, ldx=64)) == tern.TERN_ERR_INVALID_ARG
+    assert prep(_desc(x=X, ldx=64, x_up=X + 4096), _desc(x=X, ldx=64, x_up=X + 8192)) \
+        == tern.TERN_ERR_INVALID_ARG
     assert prep(_desc(x=X, ldx=64), _desc(s_act=A16 + 64)) == tern.TERN_ERR_INVALID_ARG
     assert prep(_desc(x=X, ldx=64), _desc(K=128, ldq=128)) == tern.TERN_ERR_INVALID_ARG
     assert lib.tern_linear_stack_status(None, S) == tern.TERN_ERR_INVALID_ARG
