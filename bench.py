@@ -19,7 +19,9 @@ kernels run on; ``cpu_baseline`` is the CPU oracle on a bounded sample.
 each: the single 256 x 512 GEMV; one 8B layer at M = 1 per linear and per
 layer (eight rotating copies, 390 MB, more than the 256 MB Infinity Cache);
 the 0.6B stack as seven M = 1 passes per step (three rotating copies, and
-warm); the prefill sweep M = 1 .. 512 on one 8B layer (eight copies) and
+warm); the prefill sweep M = 1 .. 512 on one 8B layer (eight copies), that
+layer's gated feed-forward as two launches (gate and up, then down reading
+silu(g) * u through its fused quantiser) at M = 1 and 8, and
 M = 16, 64, 512 on four layers; the int8 output head (151,936 x 4,096) at
 M = 1 and 8; block-wise scales on the 8B's stacked gate projections; the
 same gate projections in 2-bit and in 1.6-bit rows; the weight quantiser;
@@ -396,6 +398,49 @@ def suite(args):
                                  "sample": "32 rows of each of the 7 linears at M = 512"}
         emit(rec)
         del bm
+
+    # --- one 8B layer's gated feed-forward chained over two launches, eight
+    # rotating copies: launch 1 quantises the fp32 hidden state and runs gate
+    # and up; launch 2 quantises silu(g) * u (from launch 1's outputs) inside
+    # its own prologue and runs down
+    for M in (1, 8):
+        chain = []
+        for st in copies:
+            gate, up, down = st.linears[4], st.linears[5], st.linears[6]
+            H, F = gate.K, gate.N
+            x = torch.from_numpy(synth.make_hidden(0, 0, 4, H, M)).to(dev)
+            b = {"x": x}
+            for key, n in (("q1", H), ("q2", F)):
+                b[key] = torch.zeros((M, n), dtype=torch.int8, device=dev)
+            for key in ("s1", "s2"):
+                b[key] = torch.empty(M, dtype=torch.float32, device=dev)
+            for key in ("z1", "z2"):
+                b[key] = torch.empty(M, dtype=torch.int32, device=dev)
+            b["g"] = torch.empty((M, F), dtype=torch.float32, device=dev)
+            b["u"] = torch.empty((M, F), dtype=torch.float32, device=dev)
+            b["y"] = torch.empty((M, H), dtype=torch.float32, device=dev)
+            d1 = [tern.make_desc(pl.packed, pl.s_row, pl.rowsum, pl.N, pl.K, b["q1"], H, b["s1"], b["z1"], yy, F,
+                                 x=x, ldx=H) for pl, yy in ((gate, b["g"]), (up, b["u"]))]
+            d2 = [tern.make_desc(down.packed, down.s_row, down.rowsum, down.N, down.K, b["q2"], F, b["s2"],
+                                 b["z2"], b["y"], H, x=b["g"], ldx=F, x_up=b["u"])]
+            b["ws1"] = torch.empty(tern.tern_linear_stack_workspace_bytes(2, M), dtype=torch.uint8, device=dev)
+            b["ws2"] = torch.empty(tern.tern_linear_stack_workspace_bytes(1, M), dtype=torch.uint8, device=dev)
+            b["p1"] = tern.tern_linear_stack_prepare(d1, M, b["ws1"])
+            b["p2"] = tern.tern_linear_stack_prepare(d2, M, b["ws2"])
+            chain.append(b)
+
+        def ffn(i):
+            tern.tern_linear_stack(chain[i % 8]["p1"])
+            tern.tern_linear_stack(chain[i % 8]["p2"])
+        us = _event_times(ffn, 40)
+        nb = int(chain[0]["p1"].bytes + chain[0]["p2"].bytes)
+        emit({"suite": "ffn_chain", "workload": "one 8B layer's gated feed-forward (gate, up 12,288 x 4,096; "
+              "down 4,096 x 12,288), M = %d: two launches, the fp32 hidden state and silu(g) * u quantised "
+              "inside them, 8 rotating copies" % M, "M": M,
+              "kernels": [kernel_name(chain[0]["p1"]), kernel_name(chain[0]["p2"])],
+              "note": "bytes: packed weights, metadata, int8 activations and outputs of the three linears "
+                      "(the fp32 inputs the launches quantise are not counted)", **_stats(us, nb)})
+        del chain
     del copies
 
     # --- prefill over four 8B layers (28 linears, 195 MB): enough tiles to
