@@ -118,3 +118,57 @@ def test_swiglu_input_8b_down_shape(M):
     _check_quant(q, s, z, K, rq, rs, rz, "M=%d" % M)
     racc, ry32, _ = down.oracle(rq, rs, rz)
     _check_lin(down, racc, ry32, "M=%d" % M)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("M", [1, 8])
+def test_ffn_chain_graph_replays_static_workspace(M):
+    # the two launches captured in a HIP graph, the down launch prepared in the
+    # library's static workspace: every replay, with new hidden states and
+    # eager launches of the same plans in between, matches the oracle chain
+    H, F = 1024, 3072
+    gate, up, down = Lin(9, 4, F, H, M, 0.7), Lin(9, 5, F, H, M, 0.62), Lin(9, 6, H, F, M, 0.7)
+    ldq1, ldq2 = _pad16(H), _pad16(F)
+    xd = torch.empty((M, H), dtype=torch.float32, device=DEV)
+    q1 = torch.zeros((M, ldq1), dtype=torch.int8, device=DEV)
+    s1 = torch.empty(M, dtype=torch.float32, device=DEV)
+    z1 = torch.empty(M, dtype=torch.int32, device=DEV)
+    q2 = torch.zeros((M, ldq2), dtype=torch.int8, device=DEV)
+    s2 = torch.empty(M, dtype=torch.float32, device=DEV)
+    z2 = torch.empty(M, dtype=torch.int32, device=DEV)
+    d1 = [gate.desc(q1, ldq1, s1, z1, x=xd, ldx=H), up.desc(q1, ldq1, s1, z1, x=xd, ldx=H)]
+    ws1 = torch.empty(tern.tern_linear_stack_workspace_bytes(2, M), dtype=torch.uint8, device=DEV)
+    p1 = tern.tern_linear_stack_prepare(d1, M, ws1)
+    p2 = tern.tern_linear_stack_prepare_static([down.desc(q2, ldq2, s2, z2, x=gate.y, ldx=F, x_up=up.y)], M)
+
+    def check(x, ctx):
+        rq1, rs1, rz1 = oracle.quantize_act(x)
+        _, yg, _ = gate.oracle(rq1, rs1, rz1)
+        _, yu, _ = up.oracle(rq1, rs1, rz1)
+        rq2, rs2, rz2 = oracle.quantize_act(oracle.swiglu(yg, yu))
+        _check_quant(q2, s2, z2, F, rq2, rs2, rz2, ctx)
+        ad, yd, _ = down.oracle(rq2, rs2, rz2)
+        _check_lin(down, ad, yd, ctx)
+
+    rng = np.random.default_rng(M + 300)
+    xs = [(rng.normal(0, 1 + i, (M, H)) * (1 + 20 * (rng.random((M, H)) < 0.004))).astype(np.float32)
+          for i in range(3)]
+    xd.copy_(torch.from_numpy(xs[0]))
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        tern.tern_linear_stack(p1)
+        tern.tern_linear_stack(p2)
+    torch.cuda.synchronize()
+    for rep, x in enumerate(xs):
+        for eager in (False, True):
+            xd.copy_(torch.from_numpy(x))
+            down.y.fill_(float("nan"))
+            torch.cuda.synchronize()
+            if eager:
+                tern.tern_linear_stack(p1)
+                tern.tern_linear_stack(p2)
+            else:
+                graph.replay()
+            torch.cuda.synchronize()
+            check(x, "M=%d input %d %s" % (M, rep, "eager" if eager else "replay"))
